@@ -1,0 +1,254 @@
+"""Decode throughput of cached GQA attention with append on one MI355X.
+
+Workload (the headline case): continuous-batch decode over 32 full-cache
+layers, B = 64 rows, Hq 32 / Hkv 8, head_dim 128, bf16, max_len 8192; initial
+row lengths ~ U[1, 8128]; each step every row decodes one token except 6
+idle rows (n_new = 0, redrawn per step).  The history is filled through the
+real protocol in 64-token chunks before timing (untimed); q/k/v are
+synthetic N(0, 1) tensors already resident in HBM.
+
+One step = for each of the 32 layers kvc_append + kvc_attend, then one
+kvc_advance.  Warmup steps run first; the timed steps are bracketed by
+torch.cuda.synchronize().  Decode kernel durations come from HIP events the
+library records on the launch stream around each decode launch.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
+GPU.  ``--cpu-baseline-seconds 0`` skips the oracle timing.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import kv_cached_gqa_append_amd as K  # noqa: E402
+import workloads as wl  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_kernel_bytes(lens, n_new, work):
+    """Algorithmic bytes one decode launch (one layer) must move: the visible
+    K and V rows of every decoding row read once per KV head, plus its
+    queries read.  lens: lengths before the step."""
+    s = work.dtype_bytes
+    hkv, D, hq = work.n_kv_head[0], work.head_dim, work.n_q_head
+    act = n_new == 1
+    kv = int(((lens[act] + 1) * hkv * D * s * 2).sum())
+    qb = int(act.sum()) * hq * D * s
+    return kv + qb
+
+
+def step_bytes(lens, n_new, work):
+    """Algorithmic bytes of one whole step (all layers): attention reads, the
+    new rows (k, v read and written), queries read, outputs written."""
+    s = work.dtype_bytes
+    hkv, D, hq = work.n_kv_head[0], work.head_dim, work.n_q_head
+    act = n_new == 1
+    per_layer = decode_kernel_bytes(lens, n_new, work)
+    per_layer += int(act.sum()) * (hkv * D * s * 2 * 2 + hq * D * s)
+    return per_layer * work.n_layer
+
+
+def fill_history(cache, work, target, dev):
+    """Bring every row to target[b] tokens through append/attend/advance."""
+    B, D = work.batch, work.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "fill"))
+    C = 64
+    q = torch.randn(B, C, work.n_q_head, D, generator=g, device=dev).to(work.torch_dtype)
+    k = torch.randn(B, C, work.n_kv_head[0], D, generator=g, device=dev).to(work.torch_dtype)
+    v = torch.randn(B, C, work.n_kv_head[0], D, generator=g, device=dev).to(work.torch_dtype)
+    out = torch.empty_like(q)
+    plan = wl.fill_plan(target, C)
+    t0 = time.perf_counter()
+    for si, (n, Cs) in enumerate(plan):
+        for l in range(work.n_layer):
+            cache.append(l, k[:, :Cs].contiguous(), v[:, :Cs].contiguous(), n)
+            cache.attend(l, q[:, :Cs].contiguous(), out[:, :Cs].contiguous())
+        cache.advance()
+        if si % 16 == 0:
+            torch.cuda.synchronize()
+            log(f"[bench] fill step {si + 1}/{len(plan)} ({time.perf_counter() - t0:.1f}s)")
+    torch.cuda.synchronize()
+    log(f"[bench] history filled: {len(plan)} chunk steps in {time.perf_counter() - t0:.1f}s")
+
+
+def cpu_baseline(work, lens_all, seconds):
+    """Time the oracle on a bounded sample of the same workload."""
+    import oracle
+    n_rows = 4
+    rows = np.arange(n_rows)
+    lens = np.asarray(lens_all)[rows]
+    ref = oracle.OracleCache(n_rows, work.n_q_head, [work.n_kv_head[0]], work.head_dim,
+                             work.max_len, [0], work.rope_base)
+    Cmax = int(lens.max())
+    g = np.random.default_rng(wl.seed_of(work.name, "cpu_baseline"))
+    hk = work.n_kv_head[0]
+    k = g.standard_normal((n_rows, Cmax, hk, work.head_dim))
+    v = g.standard_normal((n_rows, Cmax, hk, work.head_dim))
+    q = np.zeros((n_rows, Cmax, work.n_q_head, work.head_dim))
+    ref.step(lens, [(q, k, v)], compute=False)
+    del k, v, q
+    done_tokens, done_bytes = 0, 0
+    t0 = time.perf_counter()
+    step = 0
+    while time.perf_counter() - t0 < seconds:
+        q1 = g.standard_normal((n_rows, 1, work.n_q_head, work.head_dim))
+        k1 = g.standard_normal((n_rows, 1, hk, work.head_dim))
+        v1 = g.standard_normal((n_rows, 1, hk, work.head_dim))
+        n = np.ones(n_rows, dtype=np.int64)
+        if (ref.lens + n > work.max_len).any():
+            break
+        lens_before = ref.lens.copy()
+        ref.step(n, [(q1, k1, v1)])
+        done_tokens += n_rows
+        done_bytes += decode_kernel_bytes(lens_before, n, work)
+        step += 1
+    dt = time.perf_counter() - t0
+    per_row_layer = dt / max(done_tokens, 1)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {
+        "value": 1.0 / (per_row_layer * work.n_layer),
+        "unit": "tokens/s",
+        "cores": cores,
+        "torch_threads": torch.get_num_threads(),
+        "kind": "oracle",
+        "gbs_equiv": done_bytes / dt / 1e9,
+        "sample": (f"oracle (float64, no cache) on {n_rows} rows with the workload's first "
+                   f"{n_rows} initial lengths {lens.tolist()}, one layer, {step} decode steps "
+                   f"({dt:.1f}s); tokens/s scaled to {work.n_layer} layers"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=56)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--layers", type=int, default=0, help="override layer count (debug only)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
+              "(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    work = wl.DECODE_B64
+    if args.layers:
+        work = work.replace(n_layer=args.layers, n_kv_head=work.n_kv_head[:args.layers],
+                            window=work.window[:args.layers])
+    total_steps = args.steps + args.warmup
+    lens0 = wl.initial_lens_decode_b64(work.batch)
+    if lens0.max() + total_steps > work.max_len:
+        lens0 = np.minimum(lens0, work.max_len - total_steps)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = K.config_from_workload(work)
+    log(f"[bench] buffer {K.kvc_nbytes(cfg, K.KVC_NB_ALLOC) / 2**30:.2f} GiB "
+        f"(KV {K.kvc_nbytes(cfg, K.KVC_NB_KV) / 2**30:.2f} GiB)")
+    cache = K.Cache(cfg, dev)
+    fill_history(cache, work, lens0, dev)
+
+    # decode inputs, resident in HBM
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "decode"))
+    B, D = work.batch, work.head_dim
+    qs = [torch.randn(B, 1, work.n_q_head, D, generator=g, device=dev).to(work.torch_dtype)
+          for _ in range(work.n_layer)]
+    ks = [torch.randn(B, 1, work.n_kv_head[0], D, generator=g, device=dev).to(work.torch_dtype)
+          for _ in range(work.n_layer)]
+    vs = [torch.randn(B, 1, work.n_kv_head[0], D, generator=g, device=dev).to(work.torch_dtype)
+          for _ in range(work.n_layer)]
+    outs = [torch.empty_like(x) for x in qs]
+    schedule = [wl.n_new_decode_b64(s, B) for s in range(total_steps)]
+
+    def run_step(n):
+        for l in range(work.n_layer):
+            cache.append(l, ks[l], vs[l], n)
+            cache.attend(l, qs[l], outs[l])
+        cache.advance()
+
+    for s in range(args.warmup):
+        run_step(schedule[s])
+    torch.cuda.synchronize()
+    lens_at = np.asarray(cache.lens(), dtype=np.int64)
+    kbytes, sbytes, tokens = 0, 0, 0
+    lens_cur = lens_at.copy()
+    for s in range(args.warmup, total_steps):
+        n = schedule[s]
+        kbytes += decode_kernel_bytes(lens_cur, n, work) * work.n_layer
+        sbytes += step_bytes(lens_cur, n, work)
+        tokens += int(n.sum())
+        lens_cur = lens_cur + n
+    K.kvc_timing_begin(cache.handle, args.steps * work.n_layer * 4 + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, total_steps):
+        run_step(schedule[s])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kt = K.kvc_timing_end(cache.handle)
+    assert cache.lens() == lens_cur.tolist()
+    dec_ms, dec_n = kt["decode"]
+    ms_step = dt * 1e3 / args.steps
+    achieved = kbytes / (dec_ms / 1e3) / 1e9 if dec_ms > 0 else 0.0
+    value = sbytes / dt / 1e9
+    kinds = {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                 "us_avg": round(v[0] * 1e3 / v[1], 2) if v[1] else None} for k, v in kt.items()}
+    log(f"[bench] {args.steps} steps in {dt:.3f}s: {ms_step:.3f} ms/step, "
+        f"{tokens / dt:.0f} tok/s, whole-step {value:.0f} GB/s, decode kernel {achieved:.0f} GB/s")
+    log(f"[bench] kernels: {json.dumps(kinds)}")
+
+    cpu = None
+    if args.cpu_baseline_seconds > 0:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(work, lens0, args.cpu_baseline_seconds)
+        log(f"[bench] cpu baseline: {cpu['value']:.3f} tok/s ({cpu['sample']})")
+
+    line = {
+        "metric": "decode cached-attn HBM GB/s (% of peak) + tokens/s, B=64 ctx<=8k bf16",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "tokens_per_s": round(tokens / dt, 1),
+        "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
+        "config": {"workload": "decode_b64", "n_layer": work.n_layer, "batch": B,
+                   "n_q_head": work.n_q_head, "n_kv_head": work.n_kv_head[0], "head_dim": D,
+                   "max_len": work.max_len, "lens_init": "U[1,8128]", "idle_rows_per_step": 6,
+                   "new_tokens_per_row": 1},
+        "roofline": {"bound": "hbm", "kernel": "k_decode<128,4>",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(dec_ms * 1e3 / dec_n, 2) if dec_n else None,
+                     "bytes_per_launch": int(kbytes / max(dec_n, 1))},
+        "kernels": kinds,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,190 @@
+/*
+ * kvc.h - cached GQA attention with append on AMD Instinct MI355X (gfx950).
+ *
+ * One handle holds the per-layer key/value cache of B rows (sequences).  Each
+ * row has its own length.  A step appends a right-padded chunk of new tokens
+ * to every layer and attends the chunk's queries against the cache:
+ *
+ *     for each layer l:  kvc_append(h, l, k, v, n_new, C, ...);
+ *                        kvc_attend(h, l, q, out, ...);
+ *     kvc_advance(h, ...);                  (once, after every layer)
+ *
+ * Sources for the operation (page titles and sections of the study pages):
+ *   - tiny_agent "generate.py": KVCache (global cache with a scratch slot,
+ *     sliding rings with a scratch slot, per-row lengths mirrored on the host),
+ *     _rope_pos (RoPE at per-row absolute positions), append (host-side
+ *     capacity check, right-padded chunks), _append_chunk (slot addressing,
+ *     grouped-query attention straight against the cache, float32 softmax).
+ *   - tinyllm "kv_cache.py": the begin/update/end step protocol; per-slot
+ *     lengths with a device copy and a host copy.
+ *   - pycraft-1 "model/kv_cache.py": preallocated pre-expansion cache of
+ *     post-RoPE keys; update() does not advance, advance() runs once after all
+ *     layers; overflow / dtype / batch guards; reset without zeroing; the
+ *     bottom-right aligned mask (build_attn_mask).
+ *   - colibri PR "inkling: ring-buffer KV cache for sliding-window layers":
+ *     "What this does" (W-key clamp), "How it works" (ring iff 0 < W < max_len;
+ *     score the chunk from its own new rows and append after scoring; keep
+ *     only the last W rows of a chunk; fail-fast bound check).
+ *   - "Lab 07 - KV cache and sampling": section 1 (bytes per token), section 2
+ *     (the offset mask: query i at pos+i sees key j iff j <= pos+i), section 3
+ *     (chunked prefill equals one prefill).
+ *
+ * Conventions for every call
+ *   - Device memory is owned by the caller.  The library never allocates
+ *     device memory and never synchronises the host with the device inside a
+ *     step.  All device pointers must be 16-byte aligned and contiguous.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *     on it; all calls of one step must be on one stream (or ordered).
+ *   - Every check happens on the host before anything is enqueued: a call
+ *     that returns an error has changed nothing.  Asynchronous device faults
+ *     surface at the caller's next synchronisation, not here.
+ *   - A handle is not thread-safe.
+ *   - Integer status codes: KVC_OK (0) or a negative KVC_E_* value.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct kvc_cache kvc_t;
+
+enum {
+  KVC_OK = 0,
+  KVC_E_ARG = -1,     /* bad argument or unsupported shape                    */
+  KVC_E_FULL = -2,    /* "KV cache full": some row would pass max_len         */
+  KVC_E_DTYPE = -3,   /* unknown dtype                                        */
+  KVC_E_STATE = -4,   /* call out of the step protocol's order                */
+  KVC_E_HIP = -5      /* the HIP runtime reported an error while enqueueing   */
+};
+
+enum { KVC_F32 = 0, KVC_BF16 = 1 };
+
+/* kvc_nbytes selectors */
+enum {
+  KVC_NB_KV = 0,      /* sum over layers of 2*B*Hkv_l*rows_l*D*bytes, the
+                         size formula of Lab 07 section 1 with ring rows
+                         (colibri PR, kv_ring_rows); no scratch rows          */
+  KVC_NB_ALLOC = 1    /* bytes of device memory kvc_create needs             */
+};
+
+typedef struct {
+  int32_t n_layer;          /* >= 1                                             */
+  int32_t batch;            /* B rows, >= 1                                     */
+  int32_t n_q_head;         /* Hq                                               */
+  int32_t head_dim;         /* D: a multiple of 8 in [8, 256]                    */
+  int32_t max_len;          /* positions per row, >= 1                          */
+  int32_t max_chunk;        /* largest C accepted by kvc_append, in [1, 1024]    */
+  int32_t dtype;            /* KVC_F32 or KVC_BF16: cache, q, k, v and out      */
+  const int32_t *n_kv_head; /* [n_layer] Hkv_l, Hq % Hkv_l == 0 (host memory)   */
+  const int32_t *window;    /* [n_layer] 0 = global layer; W > 0 = sliding
+                               layer whose queries see the W most recent keys
+                               including their own (host memory)                */
+  int32_t use_ring;         /* 1: a sliding layer with 0 < W < max_len keeps a
+                               W-row ring; 0: every layer keeps max_len rows and
+                               the window is applied as a mask only           */
+  double rope_base;         /* > 0: RoPE with theta_d = base^(-2d/D), half-split
+                               pairs (d, d+D/2); 0: q and k arrive rotated      */
+} kvc_config;
+
+/* Size in bytes for `what` (KVC_NB_KV or KVC_NB_ALLOC); 0 if cfg is invalid.
+ * Pure host computation. */
+size_t kvc_nbytes(const kvc_config *cfg, int what);
+
+/* Create a handle over caller-owned device memory `dev_buf` of `buf_bytes`
+ * (>= kvc_nbytes(cfg, KVC_NB_ALLOC)) on the current HIP device.  Copies cfg
+ * (the arrays too).  Enqueues the RoPE table upload and the zeroing of the
+ * row lengths on `stream` and waits for them (create is not part of a step).
+ * All rows start empty.  On error *out is NULL and nothing was enqueued. */
+int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes,
+               void *stream, kvc_t **out);
+
+/* Free the host handle.  The device buffer stays the caller's. */
+void kvc_destroy(kvc_t *h);
+
+/* Empty `n_rows` rows (host array of row indices): their length drops to 0.
+ * Nothing is zeroed: stale keys and values stay in memory and are never read
+ * again (pycraft-1 reset; tiny_agent KVCache.reset).  Not allowed inside a
+ * step (KVC_E_STATE). */
+int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream);
+
+/* Append layer `layer`'s new keys and values.
+ *   k, v          device, (B, C, Hkv_l, D) in the cache dtype; k is pre-RoPE
+ *                 (rotated here at position lens[b]+i) unless rope_base == 0.
+ *   n_new_host    host, [B]: real tokens of row b, 0 <= n_new[b] <= C; tokens
+ *                 i >= n_new[b] are padding (written to the scratch row).
+ *   C             chunk width, 1 <= C <= max_chunk.
+ *   slot_out_dev  device int32 (B, C) or NULL: the cache row each token lands
+ *                 in (full layer: pos or max_len for padding; ring layer:
+ *                 pos % W for the last W real tokens, else W).
+ * The first append of a step checks capacity (lens[b] + n_new[b] <= max_len
+ * for every row, else KVC_E_FULL) and latches n_new and C; every other append
+ * of the step must pass the same values (else KVC_E_STATE).  Each layer is
+ * appended once per step. */
+int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
+               const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev,
+               void *stream);
+
+/* Attend layer `layer`'s queries: q device (B, C, Hq, D) pre-RoPE (unless
+ * rope_base == 0); out device (B, C, Hq, D).  Query i of row b sits at
+ * p = lens[b] + i and sees cached key j iff j <= p and, on a sliding layer,
+ * p - j < W.  Query head h reads KV head h / (Hq / Hkv_l).  Scores are
+ * q.k / sqrt(D) in float32, softmax in float32.  Outputs of padded queries
+ * (i >= n_new[b]) and of rows with n_new[b] == 0 are exactly zero.  Must
+ * follow this layer's kvc_append in the same step (else KVC_E_STATE). */
+int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
+
+/* End the step: lens[b] += n_new[b] on the device and in the host mirror.
+ * Every layer must have been appended and attended (else KVC_E_STATE). */
+int kvc_advance(kvc_t *h, void *stream);
+
+/* Copy the host mirror of the row lengths into lens_host[B]. */
+int kvc_lens(const kvc_t *h, int32_t *lens_host);
+
+/* Where layer `layer` lives inside the device buffer (for inspection).
+ * K rows are row-major: byte offset k_offset + ((b*Hkv + g)*rows_alloc + r)*D*s.
+ * V is stored transposed in blocks of 16 rows: element (b, g, r, d) sits at
+ * v_offset + ((((b*Hkv + g)*rows_alloc/16 + r/16)*D + d)*16 + r%16)*s.
+ * rows excludes the scratch row (index `rows`); rows_alloc = rows + 1 rounded
+ * up to 32.  Staging (ring layers, max_chunk >= 2) uses the same two layouts
+ * with stage_rows_alloc rows; stage offsets are -1 when there is none. */
+typedef struct {
+  int64_t k_offset, v_offset, stage_k_offset, stage_v_offset;
+  int32_t n_kv_head, window, is_ring, rows, rows_alloc, stage_rows_alloc;
+} kvc_layer_info;
+int kvc_layer_layout(const kvc_t *h, int32_t layer, kvc_layer_info *info);
+
+/* Where the handle's own state lives inside the device buffer (inspection):
+ * the int32 row lengths [B] (device copy of the host mirror), the int32 n_new
+ * [B] of the current step, and the float (cos, sin) RoPE table
+ * [max_len][D/2][2] (-1 when rope_base == 0). */
+typedef struct {
+  int64_t total_bytes, kv_bytes, lens_offset, n_new_offset, rope_offset;
+} kvc_buffer_info_t;
+int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info);
+
+/* Kernel timing with HIP events recorded on the launch stream around every
+ * launch of one kernel kind (diagnostics; adds two event records per launch).
+ *   kvc_timing_begin: allocate a pool for `max_launches` launches and start
+ *                     recording (KVC_E_HIP if events cannot be created).
+ *   kvc_timing_end:   wait for the recorded events, write the summed kernel
+ *                     time in ms and the launch count per kind, stop.
+ * Kinds: 0 append, 1 decode attention, 2 chunk attention, 3 split combine,
+ * 4 ring commit, 5 generic attention. */
+enum { KVC_K_APPEND = 0, KVC_K_DECODE = 1, KVC_K_PREFILL = 2, KVC_K_COMBINE = 3,
+       KVC_K_COMMIT = 4, KVC_K_GENERIC = 5, KVC_K_NKINDS = 6 };
+int kvc_timing_begin(kvc_t *h, int32_t max_launches);
+int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind);
+
+/* Static text for a status code. */
+const char *kvc_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,380 @@
+"""Python binding of ``libkvc.so``: cached GQA attention with append on MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch provides device memory (the cache buffer, q/k/v/out tensors) and the
+HIP stream (``torch.cuda.current_stream()``).  The C functions keep their
+names (``kvc_nbytes``, ``kvc_create``, ``kvc_reset``, ``kvc_append``,
+``kvc_attend``, ``kvc_advance``, ``kvc_lens``, ...); ``Cache`` bundles them
+with a torch-allocated buffer.
+
+Errors: status codes become exceptions, following pycraft-1
+``KVCache.update``: a full cache raises ``CacheFullError`` (a ValueError),
+a dtype mismatch ``TypeError``, a batch/shape mismatch ``ValueError``; a
+call out of step order raises ``StepOrderError``.
+
+The library must be built first (``__graft_entry__.build()`` or
+``python -m kv_cached_gqa_append_amd.build``); there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkvc.so")
+
+KVC_OK, KVC_E_ARG, KVC_E_FULL, KVC_E_DTYPE, KVC_E_STATE, KVC_E_HIP = 0, -1, -2, -3, -4, -5
+KVC_F32, KVC_BF16 = 0, 1
+KVC_NB_KV, KVC_NB_ALLOC = 0, 1
+KERNEL_KINDS = ("append", "decode", "chunk", "combine", "commit", "generic")
+
+_DTYPES = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
+_TORCH_OF = {KVC_F32: torch.float32, KVC_BF16: torch.bfloat16}
+
+
+class KvcError(RuntimeError):
+    pass
+
+
+class CacheFullError(ValueError):
+    """Some row would pass max_len; nothing was written."""
+
+
+class StepOrderError(KvcError):
+    """A call broke the append -> attend -> advance protocol."""
+
+
+class KvcConfig(ctypes.Structure):
+    _fields_ = [
+        ("n_layer", ctypes.c_int32),
+        ("batch", ctypes.c_int32),
+        ("n_q_head", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_len", ctypes.c_int32),
+        ("max_chunk", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("n_kv_head", ctypes.POINTER(ctypes.c_int32)),
+        ("window", ctypes.POINTER(ctypes.c_int32)),
+        ("use_ring", ctypes.c_int32),
+        ("rope_base", ctypes.c_double),
+    ]
+
+
+class KvcBufferInfo(ctypes.Structure):
+    _fields_ = [
+        ("total_bytes", ctypes.c_int64),
+        ("kv_bytes", ctypes.c_int64),
+        ("lens_offset", ctypes.c_int64),
+        ("n_new_offset", ctypes.c_int64),
+        ("rope_offset", ctypes.c_int64),
+    ]
+
+
+class KvcLayerInfo(ctypes.Structure):
+    _fields_ = [
+        ("k_offset", ctypes.c_int64),
+        ("v_offset", ctypes.c_int64),
+        ("stage_k_offset", ctypes.c_int64),
+        ("stage_v_offset", ctypes.c_int64),
+        ("n_kv_head", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("is_ring", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("rows_alloc", ctypes.c_int32),
+        ("stage_rows_alloc", ctypes.c_int32),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ``libkvc.so`` (raises if it was never built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_void_p
+        L.kvc_nbytes.argtypes = [P(KvcConfig), ctypes.c_int]
+        L.kvc_nbytes.restype = ctypes.c_size_t
+        L.kvc_create.argtypes = [P(KvcConfig), VP, ctypes.c_size_t, VP, P(VP)]
+        L.kvc_create.restype = ctypes.c_int
+        L.kvc_destroy.argtypes = [VP]
+        L.kvc_destroy.restype = None
+        L.kvc_reset.argtypes = [VP, P(I32), I32, VP]
+        L.kvc_reset.restype = ctypes.c_int
+        L.kvc_append.argtypes = [VP, I32, VP, VP, P(I32), I32, VP, VP]
+        L.kvc_append.restype = ctypes.c_int
+        L.kvc_attend.argtypes = [VP, I32, VP, VP, VP]
+        L.kvc_attend.restype = ctypes.c_int
+        L.kvc_advance.argtypes = [VP, VP]
+        L.kvc_advance.restype = ctypes.c_int
+        L.kvc_lens.argtypes = [VP, P(I32)]
+        L.kvc_lens.restype = ctypes.c_int
+        L.kvc_layer_layout.argtypes = [VP, I32, P(KvcLayerInfo)]
+        L.kvc_layer_layout.restype = ctypes.c_int
+        L.kvc_buffer_info.argtypes = [VP, P(KvcBufferInfo)]
+        L.kvc_buffer_info.restype = ctypes.c_int
+        L.kvc_timing_begin.argtypes = [VP, I32]
+        L.kvc_timing_begin.restype = ctypes.c_int
+        L.kvc_timing_end.argtypes = [VP, P(ctypes.c_double), P(I32)]
+        L.kvc_timing_end.restype = ctypes.c_int
+        L.kvc_strerror.argtypes = [ctypes.c_int]
+        L.kvc_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def kvc_strerror(code: int) -> str:
+    return lib().kvc_strerror(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code == KVC_OK:
+        return
+    msg = f"{what}: {kvc_strerror(code)}"
+    if code == KVC_E_FULL:
+        raise CacheFullError(msg)
+    if code == KVC_E_DTYPE:
+        raise TypeError(msg)
+    if code == KVC_E_ARG:
+        raise ValueError(msg)
+    if code == KVC_E_STATE:
+        raise StepOrderError(msg)
+    raise KvcError(msg)
+
+
+def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
+                n_kv_head, window, use_ring=True, rope_base=10000.0) -> KvcConfig:
+    """A ``KvcConfig`` that keeps its per-layer arrays alive."""
+    if isinstance(dtype, torch.dtype):
+        dtype = _DTYPES[dtype]
+    elif isinstance(dtype, str):
+        dtype = {"f32": KVC_F32, "bf16": KVC_BF16}[dtype]
+    if isinstance(n_kv_head, int):
+        n_kv_head = [n_kv_head] * n_layer
+    if isinstance(window, int):
+        window = [window] * n_layer
+    hk = (ctypes.c_int32 * len(n_kv_head))(*[int(x) for x in n_kv_head])
+    wn = (ctypes.c_int32 * len(window))(*[int(x) for x in window])
+    cfg = KvcConfig(int(n_layer), int(batch), int(n_q_head), int(head_dim), int(max_len),
+                    int(max_chunk), int(dtype), hk, wn, int(bool(use_ring)), float(rope_base))
+    cfg._keep = (hk, wn)
+    return cfg
+
+
+def config_from_workload(w) -> KvcConfig:
+    """Config for a ``workloads.Workload``."""
+    return make_config(w.n_layer, w.batch, w.n_q_head, w.head_dim, w.max_len, w.max_chunk,
+                       w.dtype, list(w.n_kv_head), list(w.window), w.use_ring, w.rope_base)
+
+
+def kvc_nbytes(cfg: KvcConfig, what: int = KVC_NB_KV) -> int:
+    return int(lib().kvc_nbytes(ctypes.byref(cfg), int(what)))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def kvc_create(cfg: KvcConfig, buf: torch.Tensor, stream=None):
+    if not (buf.is_cuda and buf.dtype == torch.uint8 and buf.is_contiguous()):
+        raise ValueError("buffer must be a contiguous uint8 tensor on the GPU")
+    h = ctypes.c_void_p()
+    _check(lib().kvc_create(ctypes.byref(cfg), ctypes.c_void_p(buf.data_ptr()),
+                            ctypes.c_size_t(buf.numel()), _stream_handle(stream),
+                            ctypes.byref(h)), "kvc_create")
+    return h
+
+
+def kvc_destroy(h) -> None:
+    lib().kvc_destroy(h)
+
+
+def _rows_array(values):
+    vals = [int(x) for x in values]
+    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals)
+
+
+def kvc_reset(h, rows, stream=None) -> None:
+    arr, n = _rows_array(rows)
+    _check(lib().kvc_reset(h, arr, n, _stream_handle(stream)), "kvc_reset")
+
+
+def kvc_append(h, layer: int, k: torch.Tensor, v: torch.Tensor, n_new, C: int,
+               slot_out=None, stream=None) -> None:
+    arr, _ = _rows_array(n_new)
+    so = ctypes.c_void_p(slot_out.data_ptr()) if slot_out is not None else ctypes.c_void_p()
+    _check(lib().kvc_append(h, int(layer), ctypes.c_void_p(k.data_ptr()),
+                            ctypes.c_void_p(v.data_ptr()), arr, int(C), so,
+                            _stream_handle(stream)), "kvc_append")
+
+
+def kvc_attend(h, layer: int, q: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check(lib().kvc_attend(h, int(layer), ctypes.c_void_p(q.data_ptr()),
+                            ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
+           "kvc_attend")
+
+
+def kvc_advance(h, stream=None) -> None:
+    _check(lib().kvc_advance(h, _stream_handle(stream)), "kvc_advance")
+
+
+def kvc_lens(h, batch: int):
+    arr = (ctypes.c_int32 * batch)()
+    _check(lib().kvc_lens(h, arr), "kvc_lens")
+    return [int(x) for x in arr]
+
+
+def kvc_layer_layout(h, layer: int) -> KvcLayerInfo:
+    info = KvcLayerInfo()
+    _check(lib().kvc_layer_layout(h, int(layer), ctypes.byref(info)), "kvc_layer_layout")
+    return info
+
+
+def kvc_buffer_info(h) -> KvcBufferInfo:
+    info = KvcBufferInfo()
+    _check(lib().kvc_buffer_info(h, ctypes.byref(info)), "kvc_buffer_info")
+    return info
+
+
+def kvc_timing_begin(h, max_launches: int) -> None:
+    _check(lib().kvc_timing_begin(h, int(max_launches)), "kvc_timing_begin")
+
+
+def kvc_timing_end(h):
+    """{kind: (total_ms, launches)} for every kernel kind."""
+    ms = (ctypes.c_double * len(KERNEL_KINDS))()
+    cnt = (ctypes.c_int32 * len(KERNEL_KINDS))()
+    _check(lib().kvc_timing_end(h, ms, cnt), "kvc_timing_end")
+    return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(KERNEL_KINDS)}
+
+
+class Cache:
+    """A handle plus its torch-allocated device buffer.
+
+    Shapes: k, v (B, C, Hkv_l, D); q, out (B, C, Hq, D); contiguous, on the
+    buffer's device, in the config dtype.
+    """
+
+    def __init__(self, cfg: KvcConfig, device="cuda", stream=None, buffer=None):
+        self.cfg = cfg
+        self.batch = cfg.batch
+        self.n_layer = cfg.n_layer
+        self.n_q_head = cfg.n_q_head
+        self.head_dim = cfg.head_dim
+        self.max_len = cfg.max_len
+        self.max_chunk = cfg.max_chunk
+        self.dtype = _TORCH_OF[cfg.dtype]
+        self.n_kv_head = [cfg.n_kv_head[i] for i in range(cfg.n_layer)]
+        nbytes = kvc_nbytes(cfg, KVC_NB_ALLOC)
+        if nbytes == 0:
+            raise ValueError("invalid kvc config")
+        if buffer is None:
+            buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        elif buffer.numel() < nbytes:
+            raise ValueError(f"buffer holds {buffer.numel()} bytes, {nbytes} needed")
+        self.buffer = buffer
+        self.handle = kvc_create(cfg, self.buffer, stream)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            kvc_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- checks that mirror pycraft-1's guards ------------------------------------
+    def _check_tensor(self, t: torch.Tensor, heads: int, C: int, name: str):
+        if t.dtype != self.dtype:
+            raise TypeError(f"{name}: cache dtype {self.dtype} != {t.dtype}")
+        if t.device != self.buffer.device:
+            raise ValueError(f"{name} must be on {self.buffer.device}")
+        if t.dim() != 4 or t.shape[0] != self.batch:
+            raise ValueError(f"{name}: batch {t.shape[0] if t.dim() else '?'} does not match "
+                             f"cache batch {self.batch}")
+        if tuple(t.shape[1:]) != (C, heads, self.head_dim):
+            raise ValueError(f"{name}: shape {tuple(t.shape)} != {(self.batch, C, heads, self.head_dim)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def append(self, layer, k, v, n_new, slot_out=None, stream=None):
+        if len(n_new) != self.batch:
+            raise ValueError(f"n_new has {len(n_new)} entries, cache batch is {self.batch}")
+        C = int(k.shape[1])
+        hk = self.n_kv_head[layer]
+        self._check_tensor(k, hk, C, "k")
+        self._check_tensor(v, hk, C, "v")
+        if slot_out is not None and (slot_out.dtype != torch.int32 or slot_out.numel() != self.batch * C):
+            raise ValueError("slot_out must be int32 (B, C)")
+        kvc_append(self.handle, layer, k, v, n_new, C, slot_out, stream)
+
+    def attend(self, layer, q, out=None, stream=None):
+        C = int(q.shape[1])
+        self._check_tensor(q, self.n_q_head, C, "q")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            self._check_tensor(out, self.n_q_head, C, "out")
+        kvc_attend(self.handle, layer, q, out, stream)
+        return out
+
+    def advance(self, stream=None):
+        kvc_advance(self.handle, stream)
+
+    def reset(self, rows, stream=None):
+        kvc_reset(self.handle, rows, stream)
+
+    def lens(self):
+        return kvc_lens(self.handle, self.batch)
+
+    def device_lens(self):
+        """The device copy of the row lengths (int32 [B]), read back."""
+        info = kvc_buffer_info(self.handle)
+        return self.buffer[info.lens_offset: info.lens_offset + 4 * self.batch].view(torch.int32).clone()
+
+    def layer_layout(self, layer):
+        return kvc_layer_layout(self.handle, layer)
+
+    # -- inspection (tests): views of one layer's K and V -------------------------
+    def _elem(self):
+        return torch.empty((), dtype=self.dtype).element_size()
+
+    def k_view(self, layer, staging=False):
+        """(B, Hkv, rows_alloc, D) view of the stored (rotated) keys."""
+        info = self.layer_layout(layer)
+        off = info.stage_k_offset if staging else info.k_offset
+        rows = info.stage_rows_alloc if staging else info.rows_alloc
+        n = self.batch * info.n_kv_head * rows * self.head_dim
+        s = self._elem()
+        return self.buffer[off: off + n * s].view(self.dtype).view(
+            self.batch, info.n_kv_head, rows, self.head_dim)
+
+    def v_view(self, layer, staging=False):
+        """(B, Hkv, rows_alloc, D) copy of the stored values (un-blocked)."""
+        info = self.layer_layout(layer)
+        off = info.stage_v_offset if staging else info.v_offset
+        rows = info.stage_rows_alloc if staging else info.rows_alloc
+        n = self.batch * info.n_kv_head * rows * self.head_dim
+        s = self._elem()
+        raw = self.buffer[off: off + n * s].view(self.dtype).view(
+            self.batch, info.n_kv_head, rows // 16, self.head_dim, 16)
+        return raw.permute(0, 1, 2, 4, 3).reshape(self.batch, info.n_kv_head, rows, self.head_dim)
+
+    def v_raw(self, layer):
+        """The blocked storage itself, (B, Hkv, rows_alloc/16, D, 16), as a view."""
+        info = self.layer_layout(layer)
+        n = self.batch * info.n_kv_head * info.rows_alloc * self.head_dim
+        s = self._elem()
+        return self.buffer[info.v_offset: info.v_offset + n * s].view(self.dtype).view(
+            self.batch, info.n_kv_head, info.rows_alloc // 16, self.head_dim, 16)

@@ -1,0 +1,451 @@
+// The C ABI: handle, step state machine, host-side planning and launches.
+//
+// Protocol (pycraft-1 "model/kv_cache.py": update() writes without advancing,
+// advance() once after every layer; tinyllm "kv_cache.py": begin/update/end
+// step): per step, every layer is appended and then attended, and one
+// kvc_advance ends the step.  The capacity check runs on the host before
+// anything is enqueued (tiny_agent "generate.py" append; colibri PR "How it
+// works", the fail-fast bound check).  Row lengths live on the device and in
+// a host mirror, so planning never reads device memory (tiny_agent module
+// docstring: no host syncs inside a step).
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kvc_internal.h"
+
+using kvc::Layout;
+using kvc::LayerLayout;
+
+struct kvc_cache {
+  kvc_config cfg{};
+  std::vector<int32_t> n_kv_head, window;
+  Layout lay;
+  char *base = nullptr;
+  size_t bytes = 0;
+  int device = 0;
+  std::vector<int32_t> lens_host;
+  // step state
+  bool in_step = false;
+  std::vector<int32_t> n_new;
+  int32_t C = 0;
+  std::vector<uint8_t> appended, attended;
+  // kernel timing
+  bool timing = false;
+  std::vector<hipEvent_t> ev;      // 2 per launch
+  std::vector<int> ev_kind;
+  int32_t ev_used = 0;
+};
+
+namespace {
+
+// Smallest split sizes (keys) before the split count per row is capped.
+constexpr int32_t kDecodeSplitMin = 256;
+constexpr int32_t kChunkSplitMin = 1024;
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
+
+bool use_device(const kvc_t *h) {
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return false;
+  if (cur == h->device) return true;
+  return hipSetDevice(h->device) == hipSuccess;
+}
+
+kvc::StepArgs step_args(const kvc_t *h) {
+  kvc::StepArgs st{};
+  st.lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
+  st.n_new = reinterpret_cast<const int32_t *>(h->base + h->lay.nnew_off);
+  st.rope = h->lay.rope_off >= 0 ? reinterpret_cast<const float *>(h->base + h->lay.rope_off)
+                                  : nullptr;
+  st.B = h->cfg.batch;
+  st.C = h->C;
+  st.Hq = h->cfg.n_q_head;
+  st.D = h->cfg.head_dim;
+  st.max_len = h->cfg.max_len;
+  return st;
+}
+
+kvc::LayerArgs layer_args(const kvc_t *h, int layer) {
+  const LayerLayout &L = h->lay.layers[layer];
+  kvc::LayerArgs la{};
+  la.k = h->base + L.k_off;
+  la.v = h->base + L.v_off;
+  la.sk = L.sk_off >= 0 ? h->base + L.sk_off : nullptr;
+  la.sv = L.sv_off >= 0 ? h->base + L.sv_off : nullptr;
+  la.hkv = L.hkv;
+  la.rep = h->cfg.n_q_head / L.hkv;
+  la.window = L.window;
+  la.ring = L.ring;
+  la.rows = L.rows;
+  la.rows_alloc = L.rows_alloc;
+  la.stage_rows_alloc = L.stage_rows_alloc;
+  return la;
+}
+
+// Timing helpers: events around one launch of `kind`.
+int timing_mark(kvc_t *h, int kind, void *stream) {
+  if (!h->timing) return -1;
+  if (2 * (h->ev_used + 1) > (int32_t)h->ev.size()) return -1;
+  const int i = h->ev_used++;
+  h->ev_kind[i] = kind;
+  (void)hipEventRecord(h->ev[2 * i], (hipStream_t)stream);
+  return i;
+}
+void timing_close(kvc_t *h, int i, void *stream) {
+  if (i >= 0) (void)hipEventRecord(h->ev[2 * i + 1], (hipStream_t)stream);
+}
+
+// Key span of a one-token query at p on this layer, in storage rows.
+// Global layer: rows [lo, p] (lo = p - W + 1 when a window clamps).
+// Ring layer: the visible positions occupy slots [0, min(p + 1, W)).
+void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi) {
+  int64_t lo;
+  if (la.ring) {
+    lo = 0;
+    *hi = std::min<int64_t>(p + 1, la.window);
+  } else {
+    lo = la.window > 0 ? std::max<int64_t>(0, p - la.window + 1) : 0;
+    *hi = p + 1;
+  }
+  *base = lo / kvc::kVBlock * kvc::kVBlock;
+}
+
+// Key span of a chunk of n tokens starting at L on a non-ring layer.
+void chunk_span(const kvc::LayerArgs &la, int64_t L, int64_t n, int64_t *base, int64_t *hi) {
+  const int64_t lo = la.window > 0 ? std::max<int64_t>(0, L - la.window + 1) : 0;
+  *hi = L + n;
+  *base = lo / kvc::kRowAlign * kvc::kRowAlign;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvc_strerror(int code) {
+  switch (code) {
+    case KVC_OK: return "ok";
+    case KVC_E_ARG: return "invalid argument or unsupported shape";
+    case KVC_E_FULL: return "KV cache full";
+    case KVC_E_DTYPE: return "unknown dtype";
+    case KVC_E_STATE: return "call out of step order";
+    case KVC_E_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t kvc_nbytes(const kvc_config *cfg, int what) {
+  Layout lay;
+  if (kvc::compute_layout(cfg, &lay) != KVC_OK) return 0;
+  if (what == KVC_NB_KV) return (size_t)lay.kv_bytes;
+  if (what == KVC_NB_ALLOC) return (size_t)lay.total;
+  return 0;
+}
+
+int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *stream,
+               kvc_t **out) {
+  if (!out) return KVC_E_ARG;
+  *out = nullptr;
+  Layout lay;
+  int rc = kvc::compute_layout(cfg, &lay);
+  if (rc != KVC_OK) return rc;
+  if (!dev_buf || buf_bytes < (size_t)lay.total) return KVC_E_ARG;
+  if (reinterpret_cast<uintptr_t>(dev_buf) % 256) return KVC_E_ARG;
+
+  kvc_t *h = new (std::nothrow) kvc_t();
+  if (!h) return KVC_E_ARG;
+  h->cfg = *cfg;
+  h->n_kv_head.assign(cfg->n_kv_head, cfg->n_kv_head + cfg->n_layer);
+  h->window.assign(cfg->window, cfg->window + cfg->n_layer);
+  h->cfg.n_kv_head = h->n_kv_head.data();
+  h->cfg.window = h->window.data();
+  h->lay = std::move(lay);
+  h->base = static_cast<char *>(dev_buf);
+  h->bytes = buf_bytes;
+  h->lens_host.assign(cfg->batch, 0);
+  h->n_new.assign(cfg->batch, 0);
+  h->appended.assign(cfg->n_layer, 0);
+  h->attended.assign(cfg->n_layer, 0);
+  if (hipGetDevice(&h->device) != hipSuccess) {
+    delete h;
+    return KVC_E_HIP;
+  }
+  hipStream_t s = (hipStream_t)stream;
+  // RoPE table: angle p * base^(-2d/D) in double, cos/sin rounded once to fp32.
+  if (h->lay.rope_off >= 0) {
+    const int D = cfg->head_dim, half = D / 2;
+    std::vector<float> tab((size_t)cfg->max_len * half * 2);
+    for (int d = 0; d < half; ++d) {
+      const double theta = std::pow(cfg->rope_base, -2.0 * d / D);
+      for (int64_t p = 0; p < cfg->max_len; ++p) {
+        const double a = (double)p * theta;
+        tab[((size_t)p * half + d) * 2 + 0] = (float)std::cos(a);
+        tab[((size_t)p * half + d) * 2 + 1] = (float)std::sin(a);
+      }
+    }
+    if (hipMemcpyAsync(h->base + h->lay.rope_off, tab.data(), tab.size() * sizeof(float),
+                       hipMemcpyHostToDevice, s) != hipSuccess) {
+      delete h;
+      return KVC_E_HIP;
+    }
+    if (hipStreamSynchronize(s) != hipSuccess) {
+      delete h;
+      return KVC_E_HIP;
+    }
+  }
+  if (hipMemsetAsync(h->base + h->lay.lens_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
+      hipMemsetAsync(h->base + h->lay.nnew_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess) {
+    delete h;
+    return KVC_E_HIP;
+  }
+  if (const char *e = std::getenv("KVC_LOG")) {
+    if (e[0] == '1')
+      std::fprintf(stderr, "[kvc] %d layers, B %d, KV %.1f MiB (formula), buffer %.1f MiB\n",
+                   cfg->n_layer, cfg->batch, h->lay.kv_bytes / 1048576.0,
+                   h->lay.total / 1048576.0);
+  }
+  *out = h;
+  return KVC_OK;
+}
+
+void kvc_destroy(kvc_t *h) {
+  if (!h) return;
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+}
+
+int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream) {
+  if (!h || n_rows < 0 || (n_rows > 0 && !rows_host)) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (rows_host[i] < 0 || rows_host[i] >= h->cfg.batch) return KVC_E_ARG;
+  if (n_rows == 0) return KVC_OK;
+  if (!use_device(h)) return KVC_E_HIP;
+  int32_t *lens = reinterpret_cast<int32_t *>(h->base + h->lay.lens_off);
+  int err = kvc::launch_reset_rows(lens, rows_host, n_rows, stream);
+  if (err) return KVC_E_HIP;
+  for (int32_t i = 0; i < n_rows; ++i) h->lens_host[rows_host[i]] = 0;
+  return KVC_OK;
+}
+
+int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
+               const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *stream) {
+  if (!h || !k || !v || !n_new_host) return KVC_E_ARG;
+  if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
+  if (C < 1 || C > h->cfg.max_chunk) return KVC_E_ARG;
+  const int32_t B = h->cfg.batch;
+  if (!h->in_step) {
+    for (int32_t b = 0; b < B; ++b)
+      if (n_new_host[b] < 0 || n_new_host[b] > C) return KVC_E_ARG;
+    for (int32_t b = 0; b < B; ++b)
+      if ((int64_t)h->lens_host[b] + n_new_host[b] > h->cfg.max_len) return KVC_E_FULL;
+  } else {
+    if (C != h->C) return KVC_E_STATE;
+    for (int32_t b = 0; b < B; ++b)
+      if (n_new_host[b] != h->n_new[b]) return KVC_E_STATE;
+    if (h->appended[layer]) return KVC_E_STATE;
+  }
+  if (!use_device(h)) return KVC_E_HIP;
+  if (!h->in_step) {
+    int32_t *nn = reinterpret_cast<int32_t *>(h->base + h->lay.nnew_off);
+    if (kvc::launch_set_rows(nn, n_new_host, B, stream)) return KVC_E_HIP;
+    std::copy(n_new_host, n_new_host + B, h->n_new.begin());
+    h->C = C;
+    h->in_step = true;
+    std::fill(h->appended.begin(), h->appended.end(), 0);
+    std::fill(h->attended.begin(), h->attended.end(), 0);
+  }
+  const kvc::StepArgs st = step_args(h);
+  const kvc::LayerArgs la = layer_args(h, layer);
+  const int t = timing_mark(h, KVC_K_APPEND, stream);
+  int err = kvc::launch_append(h->cfg.dtype, st, la, k, v, slot_out_dev, stream);
+  timing_close(h, t, stream);
+  if (err) return KVC_E_HIP;
+  h->appended[layer] = 1;
+  return KVC_OK;
+}
+
+int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) {
+  if (!h || !q || !out) return KVC_E_ARG;
+  if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
+  if (!h->in_step || !h->appended[layer] || h->attended[layer]) return KVC_E_STATE;
+  if (!use_device(h)) return KVC_E_HIP;
+  const kvc::StepArgs st = step_args(h);
+  const kvc::LayerArgs la = layer_args(h, layer);
+  const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
+  bool staged = false;
+  for (int32_t b = 0; b < B; ++b) staged |= (h->n_new[b] >= 2);
+  staged = staged && la.ring && la.sk;
+
+  const bool fast = h->cfg.dtype == KVC_BF16 && kvc::fast_decode_supported(D, la.rep) &&
+                    kvc::fast_prefill_supported(D, la.rep);
+  int err = 0;
+  if (!fast) {
+    const int t = timing_mark(h, KVC_K_GENERIC, stream);
+    err = kvc::launch_generic(h->cfg.dtype, st, la, q, out, stream);
+    timing_close(h, t, stream);
+    if (err) return KVC_E_HIP;
+  } else {
+    // Plan: decode rows (one token) and chunk rows (two or more tokens).
+    int64_t max_dec = 0, max_chunk_span = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t L = h->lens_host[b], n = h->n_new[b];
+      int64_t base, hi;
+      if (n == 1) {
+        decode_span(la, L, &base, &hi);
+        max_dec = std::max(max_dec, hi - base);
+      } else if (n >= 2 && !la.ring) {
+        chunk_span(la, L, n, &base, &hi);
+        max_chunk_span = std::max(max_chunk_span, hi - base);
+      }
+    }
+    kvc::PartialArgs pa{};
+    pa.dml = reinterpret_cast<float *>(h->base + h->lay.dml_off);
+    pa.dout = reinterpret_cast<float *>(h->base + h->lay.dout_off);
+    pa.pml = h->lay.pml_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pml_off) : nullptr;
+    pa.pout = h->lay.pout_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pout_off) : nullptr;
+    pa.max_chunk = h->cfg.max_chunk;
+    pa.dec_split_keys = (int32_t)std::max<int64_t>(
+        kDecodeSplitMin, round_up(ceil_div(max_dec, kvc::kDecodeSplitCap), kvc::kVBlock));
+    pa.pre_split_keys = (int32_t)std::max<int64_t>(
+        kChunkSplitMin, round_up(ceil_div(max_chunk_span, kvc::kChunkSplitCap), kvc::kRowAlign));
+    int64_t dec_items = 0, pre_items = 0;
+    for (int32_t b = 0; b < B; ++b) {
+      const int64_t L = h->lens_host[b], n = h->n_new[b];
+      int64_t base, hi;
+      if (n == 1) {
+        decode_span(la, L, &base, &hi);
+        dec_items += ceil_div(hi - base, pa.dec_split_keys);
+      } else if (n >= 2) {
+        const int64_t nqt = ceil_div(n * la.rep, kvc::kChunkQTile);
+        int64_t nks = 1;
+        if (!la.ring) {
+          chunk_span(la, L, n, &base, &hi);
+          nks = ceil_div(hi - base, pa.pre_split_keys);
+        }
+        pre_items += nqt * nks;
+      }
+    }
+    if (dec_items > 0) {
+      const int t = timing_mark(h, KVC_K_DECODE, stream);
+      err = kvc::launch_decode(st, la, pa, q, (int32_t)dec_items, stream);
+      timing_close(h, t, stream);
+      if (err) return KVC_E_HIP;
+    }
+    if (pre_items > 0) {
+      const int t = timing_mark(h, KVC_K_PREFILL, stream);
+      err = kvc::launch_prefill(st, la, pa, q, (int32_t)pre_items, stream);
+      timing_close(h, t, stream);
+      if (err) return KVC_E_HIP;
+    }
+    const int t = timing_mark(h, KVC_K_COMBINE, stream);
+    err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, stream);
+    timing_close(h, t, stream);
+    if (err) return KVC_E_HIP;
+  }
+  if (staged) {
+    const int t = timing_mark(h, KVC_K_COMMIT, stream);
+    err = kvc::launch_commit(h->cfg.dtype, st, la, stream);
+    timing_close(h, t, stream);
+    if (err) return KVC_E_HIP;
+  }
+  h->attended[layer] = 1;
+  return KVC_OK;
+}
+
+int kvc_advance(kvc_t *h, void *stream) {
+  if (!h) return KVC_E_ARG;
+  if (!h->in_step) return KVC_E_STATE;
+  for (int32_t l = 0; l < h->cfg.n_layer; ++l)
+    if (!h->appended[l] || !h->attended[l]) return KVC_E_STATE;
+  if (!use_device(h)) return KVC_E_HIP;
+  int32_t *lens = reinterpret_cast<int32_t *>(h->base + h->lay.lens_off);
+  const int32_t *nn = reinterpret_cast<const int32_t *>(h->base + h->lay.nnew_off);
+  if (kvc::launch_advance(lens, nn, h->cfg.batch, stream)) return KVC_E_HIP;
+  for (int32_t b = 0; b < h->cfg.batch; ++b) h->lens_host[b] += h->n_new[b];
+  h->in_step = false;
+  return KVC_OK;
+}
+
+int kvc_lens(const kvc_t *h, int32_t *lens_host) {
+  if (!h || !lens_host) return KVC_E_ARG;
+  std::copy(h->lens_host.begin(), h->lens_host.end(), lens_host);
+  return KVC_OK;
+}
+
+int kvc_layer_layout(const kvc_t *h, int32_t layer, kvc_layer_info *info) {
+  if (!h || !info || layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
+  const LayerLayout &L = h->lay.layers[layer];
+  info->k_offset = L.k_off;
+  info->v_offset = L.v_off;
+  info->stage_k_offset = L.sk_off;
+  info->stage_v_offset = L.sv_off;
+  info->n_kv_head = L.hkv;
+  info->window = L.window;
+  info->is_ring = L.ring;
+  info->rows = L.rows;
+  info->rows_alloc = L.rows_alloc;
+  info->stage_rows_alloc = L.stage_rows_alloc;
+  return KVC_OK;
+}
+
+int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info) {
+  if (!h || !info) return KVC_E_ARG;
+  info->total_bytes = h->lay.total;
+  info->kv_bytes = h->lay.kv_bytes;
+  info->lens_offset = h->lay.lens_off;
+  info->n_new_offset = h->lay.nnew_off;
+  info->rope_offset = h->lay.rope_off;
+  return KVC_OK;
+}
+
+int kvc_timing_begin(kvc_t *h, int32_t max_launches) {
+  if (!h || max_launches < 1) return KVC_E_ARG;
+  if ((int32_t)h->ev.size() < 2 * max_launches) {
+    while ((int32_t)h->ev.size() < 2 * max_launches) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return KVC_E_HIP;
+      h->ev.push_back(e);
+    }
+  }
+  h->ev_kind.assign(max_launches, 0);
+  h->ev_used = 0;
+  h->timing = true;
+  return KVC_OK;
+}
+
+int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind) {
+  if (!h || !ms_per_kind || !launches_per_kind) return KVC_E_ARG;
+  if (!h->timing) return KVC_E_STATE;
+  for (int k = 0; k < KVC_K_NKINDS; ++k) {
+    ms_per_kind[k] = 0.0;
+    launches_per_kind[k] = 0;
+  }
+  int rc = KVC_OK;
+  for (int32_t i = 0; i < h->ev_used; ++i) {
+    if (hipEventSynchronize(h->ev[2 * i + 1]) != hipSuccess) {
+      rc = KVC_E_HIP;
+      break;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, h->ev[2 * i], h->ev[2 * i + 1]) != hipSuccess) {
+      rc = KVC_E_HIP;
+      break;
+    }
+    ms_per_kind[h->ev_kind[i]] += ms;
+    launches_per_kind[h->ev_kind[i]] += 1;
+  }
+  h->timing = false;
+  h->ev_used = 0;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,95 @@
+// Internal declarations shared by the host library (kvc_api.cpp, layout.cpp)
+// and the kernels (kernels.hip).  Plain structs passed to kernels by value.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+// Rows per V block: V is stored as [block][d][16 rows] so that a lane can read
+// several consecutive keys of one head-dimension element with one load (the
+// contraction dimension of P.V is the key axis).
+constexpr int kVBlock = 16;
+// Row counts are padded to a multiple of the chunk-attention key tile so that
+// whole tiles can be loaded without bounds checks.
+constexpr int kRowAlign = 32;
+// Caps on split-K partial slots per query row.
+constexpr int kDecodeSplitCap = 64;
+constexpr int kChunkSplitCap = 16;
+// Query rows per chunk-attention workgroup (4 waves x 16 rows).
+constexpr int kChunkQTile = 64;
+
+struct LayerLayout {
+  int64_t k_off = 0, v_off = 0;           // byte offsets in the device buffer
+  int64_t sk_off = -1, sv_off = -1;       // staging (ring layers, max_chunk >= 2)
+  int32_t hkv = 0, window = 0, ring = 0;  // ring: 0 < W < max_len and use_ring
+  int32_t rows = 0;                       // W (ring) or max_len; scratch = rows
+  int32_t rows_alloc = 0;                 // rows + 1 rounded up to kRowAlign
+  int32_t stage_rows_alloc = 0;           // max_chunk rounded up to kRowAlign
+};
+
+struct Layout {
+  std::vector<LayerLayout> layers;
+  int64_t rope_off = -1;      // float2 (cos, sin) [max_len][D/2], fp32
+  int64_t lens_off = 0;       // int32 [B]
+  int64_t nnew_off = 0;       // int32 [B]
+  int64_t dml_off = 0;        // float2 (m, l) [B][Hq][kDecodeSplitCap]
+  int64_t dout_off = 0;       // float [B][Hq][kDecodeSplitCap][D]
+  int64_t pml_off = -1;       // float2 [B][max_chunk][Hq][kChunkSplitCap]
+  int64_t pout_off = -1;      // float [B][max_chunk][Hq][kChunkSplitCap][D]
+  int64_t total = 0;
+  int64_t kv_bytes = 0;       // the pages' size formula, no scratch rows
+};
+
+// Validates cfg and fills *lay.  Returns KVC_OK or a negative status.
+int compute_layout(const kvc_config *cfg, Layout *lay);
+int dtype_bytes(int dtype);
+
+// ---------------------------------------------------------------------------
+// Kernel-side argument blocks
+// ---------------------------------------------------------------------------
+struct LayerArgs {
+  char *k, *v;          // this layer's K and V region
+  char *sk, *sv;        // staging K and V (nullptr when the layer has none)
+  int32_t hkv, rep, window, ring, rows, rows_alloc, stage_rows_alloc;
+};
+
+struct StepArgs {
+  const int32_t *lens;    // device [B]
+  const int32_t *n_new;   // device [B]
+  const float *rope;      // device float2 table or nullptr (no rotation)
+  int32_t B, C, Hq, D, max_len;
+};
+
+struct PartialArgs {
+  float *dml, *dout;      // decode partials
+  float *pml, *pout;      // chunk partials
+  int32_t max_chunk;
+  int32_t dec_split_keys; // keys per decode split (multiple of 16)
+  int32_t pre_split_keys; // keys per chunk split (multiple of 32)
+};
+
+// Launchers (kernels.hip).  Return hipError_t as int (0 = success).
+int launch_set_rows(int32_t *dst, const int32_t *vals, int32_t n, void *stream);
+int launch_reset_rows(int32_t *lens, const int32_t *rows, int32_t n, void *stream);
+int launch_advance(int32_t *lens, const int32_t *n_new, int32_t B, void *stream);
+int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void *k,
+                  const void *v, int32_t *slot_out, void *stream);
+int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, void *stream);
+int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                  const void *q, int32_t n_items, void *stream);
+int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                   const void *q, int32_t n_items, void *stream);
+int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                   void *out, void *stream);
+int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const void *q,
+                   void *out, void *stream);
+bool fast_decode_supported(int D, int rep);
+bool fast_prefill_supported(int D, int rep);
+
+}  // namespace kvc

@@ -53,13 +53,16 @@ def softmax_attend(q, K, V, scale=None) -> np.ndarray:
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     out = np.empty((Hq, D), dtype=np.float64)
-    for h in range(Hq):
-        g = h // rep
-        Kg = np.ascontiguousarray(K[:, g, :])        # (n, D)
-        s = (Kg * q[h][None, :]).sum(axis=1) * scale  # (n,)
-        p = np.exp(s - s.max())
-        p = p / p.sum()
-        out[h] = (p[:, None] * V[:, g, :]).sum(axis=0)
+    for g in range(Hkv):
+        Kg = np.ascontiguousarray(K[:, g, :])                     # (n, D)
+        Vg = V[:, g, :]
+        qg = q[g * rep:(g + 1) * rep]                             # (rep, D)
+        # s[j, r] = sum_d K[j, d] q[r, d]: each key's sum over D on its own
+        s = (Kg[:, None, :] * qg[None, :, :]).sum(axis=2) * scale  # (n, rep)
+        for r in range(rep):
+            p = np.exp(s[:, r] - s[:, r].max())
+            p = p / p.sum()
+            out[g * rep + r] = (p[:, None] * Vg).sum(axis=0)
     return out
 
 

@@ -125,11 +125,13 @@ class OracleCache:
             raise CacheFull("KV cache full")
         return n_new
 
-    def layer_step(self, layer: int, n_new, q, k, v) -> np.ndarray:
+    def layer_step(self, layer: int, n_new, q, k, v, compute: bool = True) -> np.ndarray:
         """Append layer ``layer``'s new tokens, then attend.  Does not advance.
 
         q: (B, C, Hq, D); k, v: (B, C, Hkv, D) raw (pre-RoPE) values.
         Returns (B, C, Hq, D) float64 with zeros at padded / idle positions.
+        ``compute=False`` only appends (history for steps nobody checks) and
+        returns None.
         """
         n_new = np.asarray(n_new, dtype=np.int64)
         q = np.asarray(q, dtype=np.float64)
@@ -143,22 +145,25 @@ class OracleCache:
                 continue
             self.hist_k[layer][b] = np.concatenate((self.hist_k[layer][b], k[b, :n]), axis=0)
             self.hist_v[layer][b] = np.concatenate((self.hist_v[layer][b], v[b, :n]), axis=0)
+            if not compute:
+                continue
             T = int(self.lens[b]) + n
             krot = _rope.rotate(self.hist_k[layer][b], np.arange(T), self.rope_base)
             qrot = _rope.rotate(q[b, :n], self._query_positions(b, n), self.rope_base)
             blocked = self._blocked(layer, b, n)
             out[b, :n] = _attn.attend_rows(qrot, krot, self.hist_v[layer][b], blocked)
-        return out
+        return out if compute else None
 
     def advance(self, n_new) -> None:
         self.lens = self.lens + np.asarray(n_new, dtype=np.int64)
 
-    def step(self, n_new, layers) -> list:
+    def step(self, n_new, layers, compute: bool = True) -> list:
         """One step over every layer: ``layers[l] = (q, k, v)``.  Returns outputs."""
         n_new = self.check_capacity(n_new)
         if len(layers) != self.n_layer:
             raise ValueError("one (q, k, v) per layer")
-        outs = [self.layer_step(l, n_new, *layers[l]) for l in range(self.n_layer)]
+        outs = [self.layer_step(l, n_new, *layers[l], compute=compute)
+                for l in range(self.n_layer)]
         self.advance(n_new)
         return outs
 

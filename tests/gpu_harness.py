@@ -1,0 +1,136 @@
+"""Helpers for the GPU parity tests: run the same seeded steps through the
+HIP library (via the Python binding) and through the CPU oracle, and compare.
+
+Bars (stated once, used everywhere):
+  * lengths, positions and slot indices: bit-exact;
+  * float32 outputs: max abs error <= 1e-5;
+  * bfloat16 outputs: max abs error <= 2e-2 and ||got - ref|| / ||ref|| <= 1e-2
+    per (layer, step) tensor;
+  * padded queries and idle rows: exactly 0.
+"""
+
+import sys
+
+import numpy as np
+import torch
+
+import kv_cached_gqa_append_amd as K
+import oracle
+import workloads as wl
+
+F32_MAX_ABS = 1e-5
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 1e-2
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().double().cpu().numpy()
+
+
+def check_outputs(got, ref, n_new, dtype, what):
+    """got, ref: (B, C, Hq, D) float64 arrays."""
+    C = got.shape[1]
+    pad = np.arange(C)[None, :] >= np.asarray(n_new)[:, None]
+    assert np.all(got[pad] == 0.0), f"{what}: padded/idle outputs are not exactly zero"
+    d = np.abs(got - ref)
+    mx = float(d.max()) if d.size else 0.0
+    if dtype == "f32":
+        assert mx <= F32_MAX_ABS, f"{what}: max abs {mx:.3e} > {F32_MAX_ABS}"
+        return mx, 0.0
+    nrm = float(np.linalg.norm(ref))
+    rel = float(np.linalg.norm(got - ref)) / nrm if nrm > 0 else 0.0
+    assert mx <= BF16_MAX_ABS, f"{what}: max abs {mx:.3e} > {BF16_MAX_ABS}"
+    assert rel <= BF16_REL_L2, f"{what}: rel l2 {rel:.3e} > {BF16_REL_L2}"
+    return mx, rel
+
+
+class Pair:
+    """A GPU cache and an oracle driven by the same seeded inputs."""
+
+    def __init__(self, work: wl.Workload, device="cuda", poison=False, tag=""):
+        self.work = work
+        self.tag = tag
+        self.device = torch.device(device)
+        cfg = K.config_from_workload(work)
+        buf = None
+        if poison:
+            # 0xFF bytes are NaN in both bf16 and fp32: every row the path must
+            # never read stays NaN.
+            buf = torch.full((K.kvc_nbytes(cfg, K.KVC_NB_ALLOC),), 255, dtype=torch.uint8,
+                             device=self.device)
+        self.cache = K.Cache(cfg, self.device, buffer=buf)
+        self.ref = oracle.OracleCache(work.batch, work.n_q_head, work.n_kv_head, work.head_dim,
+                                      work.max_len, work.window, work.rope_base)
+        self.step_no = 0
+        self.worst = 0.0
+        self.worst_rel = 0.0
+
+    def step(self, n_new, C, check=True, check_slots=True):
+        w = self.work
+        n_new = np.asarray(n_new, dtype=np.int64)
+        lens_before = self.ref.lens.copy()
+        layers = [wl.step_qkv(w, l, self.step_no, C, self.tag) for l in range(w.n_layer)]
+        outs, slots = [], []
+        for l, (q, k, v) in enumerate(layers):
+            so = torch.full((w.batch, C), -7, dtype=torch.int32, device=self.device)
+            self.cache.append(l, k.to(self.device), v.to(self.device), n_new, slot_out=so)
+            outs.append(self.cache.attend(l, q.to(self.device)))
+            slots.append(so)
+        self.cache.advance()
+        exp = self.ref.step(n_new, [tuple(f64(t) for t in x) for x in layers], compute=check)
+        torch.cuda.synchronize()
+        if check_slots:
+            for l in range(w.n_layer):
+                want = oracle.slot_indices(lens_before, n_new, C, w.window[l], w.max_len,
+                                           w.use_ring)
+                got = slots[l].cpu().numpy()
+                assert np.array_equal(got, want), f"layer {l} step {self.step_no}: slots {got} != {want}"
+        if check:
+            for l in range(w.n_layer):
+                mx, rel = check_outputs(f64(outs[l]), exp[l], n_new, w.dtype,
+                                        f"{w.name} layer {l} step {self.step_no}")
+                self.worst = max(self.worst, mx)
+                self.worst_rel = max(self.worst_rel, rel)
+        assert self.cache.lens() == [int(x) for x in self.ref.lens]
+        assert self.cache.device_lens().tolist() == [int(x) for x in self.ref.lens]
+        self.step_no += 1
+        return outs
+
+    def reset(self, rows):
+        self.cache.reset(rows)
+        self.ref.reset(rows)
+
+    def check_cache_rows(self, layer):
+        """Stored K (rotated) and V of every live row against the oracle's raw
+        history: V bit-exact, K within one unit in the last place of
+        R(k, pos) rounded to the dtype (float32: within 1e-6)."""
+        w = self.work
+        kview = self.cache.k_view(layer).float().cpu().numpy()
+        vview = self.cache.v_view(layer).float().cpu().numpy()
+        W = w.window[layer]
+        ring = oracle.cache.is_ring(W, w.max_len, w.use_ring)
+        for b in range(w.batch):
+            L = int(self.ref.lens[b])
+            hk, hv = self.ref.history(layer, b)
+            lo = max(0, L - W) if ring else 0
+            pos = np.arange(lo, L)
+            if pos.size == 0:
+                continue
+            slot = pos % W if ring else pos
+            krot = oracle.rope.rotate(hk[lo:L], pos, w.rope_base)     # (n, Hkv, D) fp64
+            got_k = kview[b][:, slot, :].transpose(1, 0, 2)           # (n, Hkv, D)
+            got_v = vview[b][:, slot, :].transpose(1, 0, 2)
+            assert np.array_equal(got_v, hv[lo:L]), f"layer {layer} row {b}: V differs"
+            if w.dtype == "f32":
+                assert np.abs(got_k - krot).max() <= 1e-6, f"layer {layer} row {b}: K"
+            else:
+                kr = torch.from_numpy(krot).to(torch.bfloat16).float().numpy()
+                ulp = np.maximum(np.abs(kr), 1e-30)
+                ulp = 2.0 ** (np.floor(np.log2(ulp)) - 7)
+                bad = np.abs(got_k - kr) > ulp * 1.0001
+                assert not bad.any(), f"layer {layer} row {b}: K off by more than 1 ulp"

@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Every case prints its name before it touches the GPU.  Inputs are the seeded
+draws of ``workloads``; bars are stated in ``gpu_harness``.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cached_gqa_append_amd as K
+import workloads as wl
+from gpu_harness import Pair, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _fill(pair, target_lens, chunk=64):
+    for n, C in wl.fill_plan(target_lens, chunk):
+        pair.step(n, C, check=False)
+
+
+def test_small_fp32_chunks_then_decode():
+    # 17-token prompt in chunks 5,5,5,2, then 24 one-token steps; fp32 bar 1e-5.
+    say("case: small_fp32 schedule")
+    pair = Pair(wl.SMALL_FP32)
+    for n, C in wl.schedule_small_fp32():
+        pair.step(n, C)
+    pair.check_cache_rows(0)
+    say(f"  worst abs {pair.worst:.2e}")
+
+
+def test_small_fp32_ring_layer_generic_path():
+    say("case: fp32 ring layer (W=6) with chunks wider than the window")
+    work = wl.Workload("fp32_ring", 2, 3, 8, (2, 4), 32, 40, (6, 0), "f32", 16)
+    pair = Pair(work, poison=True)
+    for n, C in [([9, 3, 0], 9), ([1, 1, 1], 1), ([16, 2, 5], 16), ([1, 0, 1], 1), ([3, 7, 1], 7)]:
+        pair.step(n, C)
+    pair.check_cache_rows(0)
+    pair.check_cache_rows(1)
+
+
+def test_ring_bf16_wraps_then_reset_and_long_chunk():
+    # 8 layers (7 rings of W=8, one global), 12-token prompts + 24 decode
+    # steps (the ring wraps 4+ times), then a reset and one 36-token chunk.
+    say("case: ring_bf16 phase 1 (poisoned buffer)")
+    work = wl.RING_BF16
+    pair = Pair(work, poison=True)
+    phase1, phase2 = wl.schedule_ring_bf16(work.batch)
+    for n, C in phase1:
+        pair.step(n, C)
+    for l in range(work.n_layer):
+        pair.check_cache_rows(l)
+    say("case: ring_bf16 reset + 36-token chunk over a NaN-filled cache")
+    pair.reset(list(range(work.batch)))
+    for l in range(work.n_layer):
+        pair.cache.k_view(l).fill_(float("nan"))
+        pair.cache.v_raw(l).fill_(float("nan"))
+    for n, C in phase2:
+        pair.step(n, C)
+    for l in range(work.n_layer):
+        pair.check_cache_rows(l)
+    say(f"  worst abs {pair.worst:.2e} rel {pair.worst_rel:.2e}")
+
+
+def test_ring_and_full_layouts_agree():
+    say("case: ring layout vs full layout with window mask")
+    work = wl.RING_BF16
+    phase1, _ = wl.schedule_ring_bf16(work.batch)
+    a = Pair(work, tag="g7")
+    b = Pair(work.replace(use_ring=False), tag="g7")
+    for n, C in phase1[:10]:
+        oa = a.step(n, C)
+        ob = b.step(n, C)
+        for x, y in zip(oa, ob):
+            assert float((x.float() - y.float()).abs().max()) <= 2e-2
+
+
+def test_mixed_batch_decode_and_chunks_with_splits():
+    # Rows at very different lengths; decode rows (n=1), chunk rows (n>=2),
+    # idle rows and right padding in the same call; a global layer and a
+    # W=200 ring layer; lengths long enough for several key splits.
+    say("case: mixed decode/chunk batch, D128 rep4")
+    work = wl.Workload("mixed_small", 2, 5, 32, (8, 8), 128, 1700, (0, 200), "bf16", 64)
+    pair = Pair(work, poison=True)
+    _fill(pair, [0, 300, 1100, 1400, 37])
+    for n in ([64, 1, 17, 1, 0], [1, 64, 1, 2, 64], [0, 5, 64, 1, 1], [33, 1, 1, 64, 2]):
+        pair.step(n, 64)
+    say(f"  worst abs {pair.worst:.2e} rel {pair.worst_rel:.2e}")
+
+
+def test_rep8_ring_and_global_prefill_then_decode():
+    say("case: rep 8 (Hq64/Hkv8), W=64 ring + global, 64-token chunks then decode")
+    work = wl.Workload("rep8_small", 2, 2, 64, (8, 8), 128, 512, (64, 0), "bf16", 64)
+    pair = Pair(work, poison=True)
+    for s in range(5):
+        pair.step([64, 64 if s < 4 else 30], 64, check=(s >= 3))
+    for _ in range(6):
+        pair.step([1, 1], 1)
+    pair.check_cache_rows(0)
+    pair.check_cache_rows(1)
+
+
+def test_decode_many_splits():
+    say("case: decode with lengths up to ~3000 (many splits), D128 rep4")
+    work = wl.Workload("decode_splits", 1, 6, 32, (8,), 128, 3200, (0,), "bf16", 64)
+    pair = Pair(work, poison=True)
+    _fill(pair, [2900, 17, 1024, 1025, 256, 3100])
+    for s in range(3):
+        pair.step(wl.n_new_decode_b64(s, batch=6, idle=1), 1)
+
+
+@pytest.mark.parametrize("D,rep", [(64, 1), (64, 2), (64, 8), (128, 1), (128, 2), (128, 16)])
+def test_head_shapes(D, rep):
+    say(f"case: head shapes D={D} rep={rep}")
+    hkv = 2
+    work = wl.Workload(f"shape_{D}_{rep}", 1, 3, hkv * rep, (hkv,), D, 400, (0,), "bf16", 40)
+    pair = Pair(work, poison=True)
+    _fill(pair, [300, 40, 5], chunk=40)
+    pair.step([40, 1, 3], 40)
+    pair.step([1, 1, 1], 1)
+
+
+def test_guards_and_step_order():
+    say("case: guards (full, dtype, batch, step order)")
+    work = wl.Workload("guards", 2, 2, 8, (2, 2), 64, 20, (0, 4), "bf16", 16)
+    pair = Pair(work)
+    pair.step([8, 3], 8)
+    c = pair.cache
+    dev = pair.device
+    q, k, v = (t.to(dev) for t in wl.step_qkv(work, 0, 99, 8))
+    # capacity: row 0 at 8 + 13 > 20
+    with pytest.raises(K.CacheFullError):
+        c.append(0, torch.zeros(2, 13, 2, 64, dtype=torch.bfloat16, device=dev),
+                 torch.zeros(2, 13, 2, 64, dtype=torch.bfloat16, device=dev), [13, 0])
+    assert c.lens() == [8, 3]
+    with pytest.raises(TypeError):
+        c.append(0, k.float(), v.float(), [1, 1])
+    with pytest.raises(ValueError):
+        c.append(0, k[:1], v[:1], [1])
+    with pytest.raises(K.StepOrderError):
+        c.attend(0, q)                                    # attend before append
+    c.append(0, k, v, [2, 2])
+    with pytest.raises(K.StepOrderError):
+        c.append(0, k, v, [2, 2])                          # same layer twice
+    with pytest.raises(K.StepOrderError):
+        c.append(1, k, v, [2, 1])                          # different n_new in a step
+    with pytest.raises(K.StepOrderError):
+        c.advance()                                        # layer 0 not attended
+    with pytest.raises(K.StepOrderError):
+        c.reset([0])                                       # reset inside a step
+    c.attend(0, q)
+    c.append(1, k, v, [2, 2])
+    with pytest.raises(K.StepOrderError):
+        c.advance()                                        # layer 1 not attended
+    c.attend(1, q)
+    c.advance()
+    assert c.lens() == [10, 5]
+    torch.cuda.synchronize()
