@@ -17,6 +17,8 @@ GPU.  ``--cpu-baseline-seconds 0`` skips the oracle timing.
 """
 
 import argparse
+import csv
+import hashlib
 import json
 import os
 import sys
@@ -33,6 +35,9 @@ import kv_cached_gqa_append_amd as K  # noqa: E402
 import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "kv_cached_gqa_append_amd", "csrc", "kernels.hip")
+COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_decode_b64_hbm.md")
+COPY_BYTES = 2 ** 30   # the --copy-probe device copy: 1 GiB read, 1 GiB written
 
 
 def log(*a):
@@ -60,6 +65,132 @@ def step_bytes(lens, n_new, work):
     per_layer = decode_kernel_bytes(lens, n_new, work)
     per_layer += int(act.sum()) * (hkv * D * s * 2 * 2 + hq * D * s)
     return per_layer * work.n_layer
+
+
+def kernels_sha():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload_for(layers):
+    work = wl.DECODE_B64
+    if layers:
+        work = work.replace(n_layer=layers, n_kv_head=work.n_kv_head[:layers],
+                            window=work.window[:layers])
+    return work
+
+
+def plan_lens(work, steps, warmup):
+    """Initial lengths (clipped so every step fits) and the n_new schedule."""
+    total = steps + warmup
+    lens0 = wl.initial_lens_decode_b64(work.batch)
+    if lens0.max() + total > work.max_len:
+        lens0 = np.minimum(lens0, work.max_len - total)
+    return lens0, [wl.n_new_decode_b64(s, work.batch) for s in range(total)]
+
+
+def timed_decode_bytes(work, steps, warmup):
+    """Algorithmic bytes of each timed decode launch, in launch order."""
+    lens0, sched = plan_lens(work, steps, warmup)
+    lens = lens0.copy()
+    for s in range(warmup):
+        lens = lens + sched[s]
+    out = []
+    for s in range(warmup, warmup + steps):
+        out += [decode_kernel_bytes(lens, sched[s], work)] * work.n_layer
+        lens = lens + sched[s]
+    return out
+
+
+def _kname(name):
+    for k in ("k_decode", "k_combine", "k_append", "k_chunk", "k_advance", "k_commit",
+              "k_set_rows", "k_generic"):
+        if k in name:
+            return k
+    return name
+
+
+def summarize_trace(trace_csv, steps, warmup, layers):
+    """Markdown table of the timed region of a rocprofv3 kernel trace of this
+    bench: the dispatches from the first timed decode on."""
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    names = [_kname(r["Kernel_Name"]) for r in rows]
+    work = workload_for(layers)
+    dec = [i for i, n in enumerate(names) if n == "k_decode"]
+    first = dec[-steps * work.n_layer] - 1          # the append before it
+    sel = rows[first:]
+    t0, t1 = int(sel[0]["Start_Timestamp"]), int(sel[-1]["End_Timestamp"])
+    by = {}
+    for r in sel:
+        by.setdefault(_kname(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3
+            for a, b in zip(sel[:-1], sel[1:])]
+    nb = timed_decode_bytes(work, steps, warmup)
+    out = [f"timed region: {len(sel)} dispatches, {(t1 - t0) / 1e6:.3f} ms, "
+           f"{(t1 - t0) / 1e3 / steps:.1f} us per step", "",
+           "| kernel | dispatches | avg us | median us | min us | max us |",
+           "|---|---|---|---|---|---|"]
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        v = np.asarray(v)
+        out.append(f"| {k} | {len(v)} | {v.mean():.2f} | {np.median(v):.2f} | {v.min():.2f} | "
+                   f"{v.max():.2f} |")
+    g = np.asarray(gaps)
+    out += ["", f"idle between dispatches: {g.sum() / 1e3:.3f} ms in total, {g.mean():.2f} us "
+            f"average", ""]
+    dv = np.asarray(by["k_decode"])
+    out.append(f"k_decode: {np.mean(nb) / 1e9:.4f} GB algorithmic per launch / "
+               f"{dv.mean():.2f} us = {np.mean(nb) / (dv.mean() * 1e3):.1f} GB/s")
+    return "\n".join(out)
+
+
+def summarize_counters(fetch_csv, write_csv, steps, warmup, layers):
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE per timed decode dispatch,
+    scaled by what the same counters read for the 1 GiB copy probe."""
+    work = workload_for(layers)
+    nb = timed_decode_bytes(work, steps, warmup)
+    vals = {}
+    for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
+        dec = [float(r["Counter_Value"]) * 1024 for r in rows if "k_decode" in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) * 1024 for r in rows
+                if "copyBuffer" in r["Kernel_Name"]]
+        if not copy:
+            raise SystemExit(f"{path}: no copy probe dispatch (run with --copy-probe)")
+        factor = COPY_BYTES / copy[-1]
+        vals[tag] = (np.asarray(dec[-len(nb):]) * factor, factor, copy[-1])
+    fetch, ff, fc = vals["FETCH_SIZE"]
+    write, wf, wc = vals["WRITE_SIZE"]
+    traffic = fetch + write
+    ratio = float(traffic.sum() / np.sum(nb))
+    out = [f"copy probe (1 GiB read + 1 GiB written): FETCH_SIZE {fc / 1024:.1f} KiB -> factor "
+           f"{ff:.3f}; WRITE_SIZE {wc / 1024:.1f} KiB -> factor {wf:.3f}", "",
+           "| timed decode dispatch | FETCH bytes (scaled) | WRITE bytes (scaled) | traffic | "
+           "algorithmic | traffic / algorithmic |", "|---|---|---|---|---|---|"]
+    for i, (a, b, c) in enumerate(zip(fetch, write, nb)):
+        out.append(f"| {i} | {a:.4e} | {b:.4e} | {a + b:.4e} | {c:.4e} | {(a + b) / c:.4f} |")
+    out += ["", f"kernels_sha256_16: {kernels_sha()}",
+            f"traffic_bytes_per_launch: {traffic.mean():.6e}",
+            f"algorithmic_bytes_per_launch: {np.mean(nb):.6e}",
+            f"traffic_ratio: {ratio:.4f}"]
+    return "\n".join(out)
+
+
+def counter_traffic(bytes_per_launch):
+    """HBM traffic per decode launch from the committed counter summary, if it
+    was taken on the current kernel source; else None."""
+    try:
+        text = open(COUNTER_SUMMARY).read()
+    except OSError:
+        return None
+    kv = dict(l.split(": ", 1) for l in text.splitlines()
+              if l.startswith(("kernels_sha256_16:", "traffic_ratio:",
+                               "traffic_bytes_per_launch:")))
+    if kv.get("kernels_sha256_16") != kernels_sha():
+        return None
+    ratio = float(kv["traffic_ratio"])
+    return {"bytes": round(ratio * bytes_per_launch), "ratio": ratio,
+            "measured_bytes_per_launch": float(kv["traffic_bytes_per_launch"])}
 
 
 def fill_history(cache, work, target, dev):
@@ -142,20 +273,31 @@ def main():
     ap.add_argument("--steps", type=int, default=56)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
-    ap.add_argument("--layers", type=int, default=0, help="override layer count (debug only)")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="fewer layers (counter runs: per-launch work is unchanged)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy, the reference for HBM counters")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="print the timed-region summary of a rocprofv3 kernel trace of this "
+                         "bench (same --steps / --warmup / --layers) and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs of this "
+                         "bench (FETCH_SIZE, WRITE_SIZE; same --steps / --warmup / --layers, "
+                         "--copy-probe) and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, args.steps, args.warmup, args.layers))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    work = wl.DECODE_B64
-    if args.layers:
-        work = work.replace(n_layer=args.layers, n_kv_head=work.n_kv_head[:args.layers],
-                            window=work.window[:args.layers])
+    work = workload_for(args.layers)
     total_steps = args.steps + args.warmup
-    lens0 = wl.initial_lens_decode_b64(work.batch)
-    if lens0.max() + total_steps > work.max_len:
-        lens0 = np.minimum(lens0, work.max_len - total_steps)
+    lens0, schedule = plan_lens(work, args.steps, args.warmup)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = K.config_from_workload(work)
@@ -175,7 +317,6 @@ def main():
     vs = [torch.randn(B, 1, work.n_kv_head[0], D, generator=g, device=dev).to(work.torch_dtype)
           for _ in range(work.n_layer)]
     outs = [torch.empty_like(x) for x in qs]
-    schedule = [wl.n_new_decode_b64(s, B) for s in range(total_steps)]
 
     def run_step(n):
         for l in range(work.n_layer):
@@ -214,12 +355,22 @@ def main():
         f"{tokens / dt:.0f} tok/s, whole-step {value:.0f} GB/s, decode kernel {achieved:.0f} GB/s")
     log(f"[bench] kernels: {json.dumps(kinds)}")
 
+    if args.copy_probe:
+        src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).random_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy probe: 1 GiB read + 1 GiB written")
+        del src, dst
+
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(work, lens0, args.cpu_baseline_seconds)
         log(f"[bench] cpu baseline: {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
+    traffic = counter_traffic(kbytes / max(dec_n, 1))
     line = {
         "metric": "decode cached-attn HBM GB/s (% of peak) + tokens/s, B=64 ctx<=8k bf16",
         "value": round(value, 1),
@@ -241,7 +392,9 @@ def main():
                    "new_tokens_per_row": 1},
         "roofline": {"bound": "hbm", "kernel": "k_decode<128,4>",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic["bytes"] if traffic else None,
+                     "traffic_ratio": traffic["ratio"] if traffic else None,
                      "avg_launch_us": round(dec_ms * 1e3 / dec_n, 2) if dec_n else None,
                      "bytes_per_launch": int(kbytes / max(dec_n, 1))},
         "kernels": kinds,

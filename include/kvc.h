@@ -167,8 +167,10 @@ typedef struct {
 } kvc_buffer_info_t;
 int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info);
 
-/* Kernel timing with HIP events recorded on the launch stream around every
- * launch of one kernel kind (diagnostics; adds two event records per launch).
+/* Kernel timing (diagnostics): every launch of a timed kind carries a pair of
+ * HIP events that the dispatch itself stamps when the kernel starts and ends
+ * (hipExtLaunchKernel), so a measurement is the kernel's own duration and no
+ * extra packets enter the stream.
  *   kvc_timing_begin: allocate a pool for `max_launches` launches and start
  *                     recording (KVC_E_HIP if events cannot be created).
  *   kvc_timing_end:   wait for the recorded events, write the summed kernel

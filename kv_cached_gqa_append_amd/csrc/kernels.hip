@@ -20,9 +20,11 @@
 //    score the chunk from its own new rows, append after scoring.
 //  - "Lab 07 - KV cache and sampling", section 2: query i at pos + i sees key
 //    j iff j <= pos + i.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <type_traits>
 
 #include "kvc_internal.h"
 
@@ -73,25 +75,6 @@ __device__ __forceinline__ float group_sum(float x) {
   if (G >= 4) x += dpp<kQuadXor2>(x);
   if (G >= 8) x += dpp<kRowHalfMirror>(x);
   if (G >= 16) x += dpp<kRowMirror>(x);
-  return x;
-}
-
-// Reduce across groups: input uniform within aligned groups of G lanes; the
-// result is the reduction over the whole wave, in every lane.
-template <int G>
-__device__ __forceinline__ float across_groups_max(float x) {
-  if (G <= 4) x = fmaxf(x, dpp<kRowHalfMirror>(x));
-  if (G <= 8) x = fmaxf(x, dpp<kRowMirror>(x));
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
-}
-template <int G>
-__device__ __forceinline__ float across_groups_sum(float x) {
-  if (G <= 4) x += dpp<kRowHalfMirror>(x);
-  if (G <= 8) x += dpp<kRowMirror>(x);
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
   return x;
 }
 
@@ -148,7 +131,7 @@ __device__ __forceinline__ void decode_span_dev(const LayerArgs &la, int64_t p, 
     *lo = la.window > 0 ? (p - la.window + 1 > 0 ? p - la.window + 1 : 0) : 0;
     *hi = p + 1;
   }
-  *base = *lo / kVBlock * kVBlock;
+  *base = *lo / kRowAlign * kRowAlign;
 }
 __device__ __forceinline__ void chunk_span_dev(const LayerArgs &la, int64_t L, int64_t n,
                                                int64_t *base, int64_t *lo, int64_t *hi) {
@@ -233,6 +216,24 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
       s = valid ? p : la.rows;
     slot_out[(int64_t)b * st.C + i] = (int32_t)s;
   }
+  // Rows past a row's end inside its current 32-row tile are read (and
+  // masked) by the decode kernel; keep their V finite: when an append enters
+  // a new tile, zero V in the rest of that tile.  The rows zeroed here are
+  // beyond every row this append writes (only the scratch row may coincide,
+  // and both writes are finite).
+  if (i == 0 && n >= 1) {
+    const int64_t W = la.window;
+    const int64_t old_top = la.ring ? (L < W ? L : W) : L;
+    const int64_t new_top = la.ring ? (L + n < W ? L + n : W) : L + n;
+    if (old_top == 0 || (new_top - 1) / kRowAlign != (old_top - 1) / kRowAlign) {
+      int64_t end = (new_top + kRowAlign - 1) / kRowAlign * kRowAlign;
+      if (end > la.rows_alloc) end = la.rows_alloc;
+      const int64_t bgz = (int64_t)b * la.hkv + g;
+      for (int d = threadIdx.x; d < st.D; d += 64)
+        for (int64_t rz = new_top; rz < end; ++rz)
+          *v_elem<T>(la.v, bgz, la.rows_alloc, rz, d, st.D) = from_f<T>(0.f);
+    }
+  }
   int64_t r;
   char *kreg, *vreg;
   int ralloc;
@@ -268,19 +269,22 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
     }
     kd[e] = from_f<T>(y1);
     kd[e + half] = from_f<T>(y2);
-    vd[e * kVBlock] = vs[e];
-    vd[(e + half) * kVBlock] = vs[e + half];
+    // A padded token's V goes to the scratch row as zeros: the row can sit
+    // inside a tile the decode kernel reads, and whatever the caller left in
+    // padded positions must not reach an output through p = 0.
+    vd[e * kVBlock] = valid ? vs[e] : from_f<T>(0.f);
+    vd[(e + half) * kVBlock] = valid ? vs[e + half] : from_f<T>(0.f);
   }
 }
 
 int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void *k,
-                  const void *v, int32_t *slot_out, void *stream) {
+                  const void *v, int32_t *slot_out, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * la.hkv;
   if (dtype == KVC_F32)
-    hipLaunchKernelGGL(k_append<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_append<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la, (const float *)k, (const float *)v, slot_out);
   else
-    hipLaunchKernelGGL(k_append<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream, st,
+    hipExtLaunchKernelGGL(k_append<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st,
                        la, (const bf16 *)k, (const bf16 *)v, slot_out);
   return (int)hipGetLastError();
 }
@@ -314,13 +318,13 @@ __global__ __launch_bounds__(64) void k_commit(StepArgs st, LayerArgs la) {
   }
 }
 
-int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, void *stream) {
+int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * la.hkv;
   if (dtype == KVC_F32)
-    hipLaunchKernelGGL(k_commit<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_commit<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la);
   else
-    hipLaunchKernelGGL(k_commit<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream, st,
+    hipExtLaunchKernelGGL(k_commit<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st,
                        la);
   return (int)hipGetLastError();
 }
@@ -439,13 +443,13 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
 }
 
 int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const void *q, void *out,
-                   void *stream) {
+                   const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * st.Hq;
   if (dtype == KVC_F32)
-    hipLaunchKernelGGL(k_generic<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_generic<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la, (const float *)q, (float *)out);
   else
-    hipLaunchKernelGGL(k_generic<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_generic<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la, (const bf16 *)q, (bf16 *)out);
   return (int)hipGetLastError();
 }
@@ -458,59 +462,241 @@ template <typename CountFn>
 __device__ __forceinline__ void find_item(int B, int64_t it, CountFn count, int *row_out,
                                           int64_t *local_out) {
   const int lane = threadIdx.x & 63;
-  int64_t rem = it;
+  int rem = (int)it;
+  int row = -1, local = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
     const int c = b < B ? count(b) : 0;
     const int incl = wave_incl_scan(c);
-    const int total = __shfl(incl, 63);
+    // every value that steers control flow is made wave-uniform explicitly
+    const int total = __builtin_amdgcn_readlane(incl, 63);
     if (rem < total) {
       const int excl = incl - c;
-      const bool mine = rem >= excl && rem < incl;
-      const uint64_t ball = __ballot(mine);
-      const int src = __ffsll((unsigned long long)ball) - 1;
-      *row_out = b0 + src;
-      *local_out = rem - __shfl(excl, src);
-      return;
+      const uint64_t ball = __ballot(rem >= excl && rem < incl);
+      const int src = (int)__builtin_amdgcn_readfirstlane(__ffsll((unsigned long long)ball) - 1);
+      row = b0 + src;
+      local = rem - __builtin_amdgcn_readlane(excl, src);
+      break;
     }
     rem -= total;
   }
-  *row_out = -1;
-  *local_out = 0;
+  *row_out = __builtin_amdgcn_readfirstlane(row);
+  *local_out = __builtin_amdgcn_readfirstlane(local);
 }
 
 // ---------------------------------------------------------------------------
 // Decode attention (rows with one new token), bf16.  One wave per
 // (row, KV head, key split).  QK: LK lanes per key, each holding D/LK
-// elements of all REP rotated queries in registers; scores reduced with DPP.
-// PV: each lane owns D/32 head-dim elements for 8 of the 16 keys of a V block
-// and accumulates with bf16 dot2 over key pairs.  Online softmax in the exp2
-// domain with one running max per query head; partials (m, l, o) per split.
+// elements of all REP rotated queries in registers (<= 32 VGPRs for the
+// common shapes); scores reduced with DPP inside a 16-lane row.  PV: each lane
+// owns D/32 head-dim elements for 8 of the 16 keys of a V block and
+// accumulates with bf16 dot2 over key pairs.  Online softmax in the exp2
+// domain with one running max per query head (cross-row reductions with the
+// gfx950 permlane swaps).  K/V tiles are double-buffered in registers.
+// Fused mode (one-token steps): the last split block of a (row, KV head)
+// merges the partials and writes the output; idle rows are zeroed.
 // ---------------------------------------------------------------------------
-template <int D, int REP>
-struct DecodeShape {
-  static constexpr int LK0 = REP * D / 128;
-  static constexpr int LK = LK0 > 4 ? LK0 : 4;   // lanes per key (QK)
-  static constexpr int KR = 64 / LK;             // keys per QK round
-  static constexpr int NR = 16 / KR;             // rounds per 16-key tile
-  static constexpr int NCH = D / 8 / LK;         // 16-byte chunks per lane
-  static constexpr int VT = D / 32;              // V head-dim rows per lane
-  static_assert(LK <= 16 && NCH >= 1, "unsupported decode shape");
-};
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Input uniform within aligned groups of G lanes; result: reduction over the
+// whole wave, in every lane.
+template <int G>
+__device__ __forceinline__ float groups_max(float x) {
+  if (G <= 4) x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  if (G <= 8) x = fmaxf(x, dpp<kRowMirror>(x));
+  return swap32_max(swap16_max(x));
+}
+template <int G>
+__device__ __forceinline__ float groups_sum(float x) {
+  if (G <= 4) x += dpp<kRowHalfMirror>(x);
+  if (G <= 8) x += dpp<kRowMirror>(x);
+  return swap32_sum(swap16_sum(x));
+}
 
 template <int D, int REP>
-__global__ __launch_bounds__(64) void k_decode(StepArgs st, LayerArgs la, PartialArgs pa,
-                                               const bf16 *__restrict__ q) {
+struct DecodeShape {
+  // lanes per key: enough that one lane's share of the REP queries fits in 32
+  // VGPRs (bf16 pairs), at least 4 and at most D/8 (one 16-byte chunk)
+  static constexpr int LKQ = REP * D / 64;
+  static constexpr int LK0 = LKQ < 4 ? 4 : (LKQ > 16 ? 16 : LKQ);
+  static constexpr int LK = LK0 > D / 8 ? D / 8 : LK0;
+  static constexpr int KR = 64 / LK;            // keys per QK round
+  static constexpr int TK = kDecodeTile;        // keys per tile (one V block)
+  static_assert(TK == kVBlock, "a decode tile is one V block");
+  static constexpr int NR = TK / KR;            // QK rounds per tile
+  static constexpr int NCH = D / 8 / LK;        // 16-byte chunks per lane per key
+  static constexpr int VT = D / 32;             // V head-dim rows per lane
+  static constexpr int HPL = REP >= LK ? REP / LK : 1;   // heads whose scores a lane owns
+  // Register tile ring and occupancy target per SIMD.  REP 16 at D 128 holds
+  // 64 accumulators and 64 query registers per lane: it runs one wave per
+  // SIMD with the full register file rather than spill.
+  static constexpr bool BIG = REP * D >= 2048;
+  static constexpr int NBUF = REP <= 4 ? 5 : (REP <= 8 ? 4 : 2);
+  static constexpr int WAVES = BIG ? 1 : 2;
+  static_assert(NCH >= 1 && NR >= 1 && D % 32 == 0, "unsupported decode shape");
+};
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw 32-bit buffer, gfx9 family
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource over [base, base + bytes) in scalar registers: no stride,
+// raw 32-bit records, so out-of-range offsets read zero.
+__device__ __forceinline__ i32x4 sgpr_rsrc(const void *base, int bytes) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xffffu));
+  r[2] = __builtin_amdgcn_readfirstlane(bytes);
+  r[3] = kRsrcWord3;
+  return r;
+}
+
+// Streaming tile loads are issued from inline assembly and their waits are
+// placed by hand.  The compiler's own wait insertion cannot follow a ring of
+// loads that stays in flight across a loop's back edge: it waits for every
+// outstanding load at the first use in the loop, which leaves one tile in
+// flight.  Each wait names the registers it covers ("+v"), so no use of a
+// tile can be scheduled before its wait; the build scans the generated
+// assembly for any other instruction touching a register between its load
+// and its wait.
+template <int OFF>
+__device__ __forceinline__ void tile_load(u32x4 &x, i32x4 rsrc, int voff, int soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "buffer immediate offsets are 12 bits");
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 ; tile load"
+               : "=v"(x)
+               : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF));
+}
+// Wait until at most N tile loads are outstanding (loads complete in order).
+template <int N>
+__device__ __forceinline__ void tile_wait(u32x4 &x) {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%1) ; tile wait %0" : "+v"(x) : "n"(N));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+constexpr int kRowRor4 = 0x124;         // lane i <- (i - 4) mod 16 within the row
+constexpr int kRowRor8 = 0x128;         // lane i <- (i - 8) mod 16 within the row
+
+// One butterfly stage over the lanes of a key (partner selected by CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp_stage(float x) { return dpp<CTRL>(x); }
+
+// Reduce-scatter of per-head partial dot products over the LK lanes of a key.
+// Stages pair lanes i/15-i (LK = 16), i/7-i (LK >= 8), then xor 2 and xor 1;
+// while a lane holds more than one head the upper lane of each pair keeps the
+// upper half of the heads.  Each lane ends with the full sums of HPL heads,
+// starting at the returned head index; with REP < LK several lanes end with
+// the same head.
+template <int LK, int REP, int HPL>
+__device__ __forceinline__ int key_reduce_scatter(const float (&a)[REP], int lane,
+                                                  float (&o)[HPL]) {
+  float v[REP];
+#pragma unroll
+  for (int h = 0; h < REP; ++h) v[h] = a[h];
+  int hbase = 0;
+  int H = REP;
+  auto stage = [&](auto ctrl_tag, bool upper) {
+    constexpr int CTRL = decltype(ctrl_tag)::value;
+    if (H > 1) {
+      const int half = H / 2;
+#pragma unroll
+      for (int i = 0; i < REP / 2; ++i) {
+        if (i < half) {
+          const float keep = upper ? v[half + i] : v[i];
+          const float send = upper ? v[i] : v[half + i];
+          v[i] = keep + dpp_stage<CTRL>(send);
+        }
+      }
+      if (upper) hbase += half;
+      H = half;
+    } else {
+      v[0] += dpp_stage<CTRL>(v[0]);
+    }
+  };
+  if constexpr (LK >= 16) stage(std::integral_constant<int, kRowMirror>{}, (lane & 15) >= 8);
+  if constexpr (LK >= 8) stage(std::integral_constant<int, kRowHalfMirror>{}, (lane & 7) >= 4);
+  stage(std::integral_constant<int, kQuadXor2>{}, (lane & 2) != 0);
+  stage(std::integral_constant<int, kQuadXor1>{}, (lane & 1) != 0);
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) o[u] = v[u];
+  return hbase;
+}
+
+// Lane (within a key's LK lanes) that owns head h after key_reduce_scatter,
+// and the slot u of that head in the lane's owned list.
+template <int LK, int REP>
+__host__ __device__ constexpr int owner_lane(int h, int *u) {
+  const int bits[4] = {LK >= 16 ? 8 : 0, LK >= 8 ? 4 : 0, 2, 1};
+  int H = REP, rel = h, ln = 0;
+  for (int s = 0; s < 4; ++s) {
+    if (bits[s] == 0) continue;
+    if (H > 1) {
+      const int half = H / 2;
+      if (rel >= half) {
+        ln |= bits[s];
+        rel -= half;
+      }
+      H = half;
+    }
+  }
+  *u = rel;
+  return ln;
+}
+
+// Max / sum over the KR key groups (lanes that own the same heads).
+template <int LK>
+__device__ __forceinline__ float keys_max(float x) {
+  if constexpr (LK <= 4) x = fmaxf(x, dpp<kRowRor4>(x));
+  if constexpr (LK <= 8) x = fmaxf(x, dpp<kRowRor8>(x));
+  return swap32_max(swap16_max(x));
+}
+template <int LK>
+__device__ __forceinline__ float keys_sum(float x) {
+  if constexpr (LK <= 4) x += dpp<kRowRor4>(x);
+  if constexpr (LK <= 8) x += dpp<kRowRor8>(x);
+  return swap32_sum(swap16_sum(x));
+}
+
+// NBUF: register tiles in the ring (NBUF - 1 in flight); WAVES: occupancy the
+// register allocator must meet.
+template <int D, int REP, int NBUF = DecodeShape<D, REP>::NBUF,
+          int WAVES = DecodeShape<D, REP>::WAVES>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
+void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q) {
   using S = DecodeShape<D, REP>;
-  constexpr int LK = S::LK, KR = S::KR, NR = S::NR, NCH = S::NCH, VT = S::VT;
-  __shared__ float qs[REP * D];
-  __shared__ __align__(16) uint16_t pls[2][REP][16];
+  constexpr int LK = S::LK, KR = S::KR, TK = S::TK, NR = S::NR, NCH = S::NCH, VT = S::VT;
+  constexpr int HPL = S::HPL;
+  __shared__ __align__(16) float qs[REP * D];               // rotated q staging
+  __shared__ __align__(16) uint16_t pls[2][REP][TK];       // p of a tile, bf16
 
   const int lane = threadIdx.x;
   const int g = blockIdx.y;
   const int SK = pa.dec_split_keys;
   int b;
-  int64_t split;
+  int64_t split64;
   find_item(
       st.B, blockIdx.x,
       [&](int r) -> int {
@@ -519,21 +705,45 @@ __global__ __launch_bounds__(64) void k_decode(StepArgs st, LayerArgs la, Partia
         decode_span_dev(la, st.lens[r], &base, &lo, &hi);
         return (int)cdiv(hi - base, SK);
       },
-      &b, &split);
+      &b, &split64);
   if (b < 0) return;
+  const int split = (int)split64;
+  const int h0 = g * REP;
   const int64_t p = st.lens[b];
-  int64_t base, lo, hi;
-  decode_span_dev(la, p, &base, &lo, &hi);
-  const int64_t t_begin = base + split * SK;
-  const int64_t t_end = t_begin + SK < hi ? t_begin + SK : hi;
+  int64_t base64, lo64, hi64;
+  decode_span_dev(la, p, &base64, &lo64, &hi64);
+  // Row indices fit in 32 bits (rows <= max_len < 2^31).
+  const int lo = (int)lo64, hi = (int)hi64;
+  // The row's 16-key tiles are shared out evenly over its splits (sizes
+  // differ by at most one tile); SK is a multiple of TK, so the split count
+  // cdiv(hi - base, SK) is also cdiv(tiles, SK / TK) and every split gets a
+  // tile.
+  const int ntile = (hi - (int)base64 + TK - 1) / TK;
+  const int nsplit = (hi - (int)base64 + SK - 1) / SK;
+  const int tb = split * ntile / nsplit, te = (split + 1) * ntile / nsplit;
+  // (uniform values; readfirstlane keeps them in scalar registers, where the
+  // tile loads take their offsets)
+  const int t_begin = __builtin_amdgcn_readfirstlane((int)base64 + tb * TK);
+  const int n_iter = __builtin_amdgcn_readfirstlane(te - tb);
   const int64_t bg = (int64_t)b * la.hkv + g;
 
-  // -- queries: load REP heads, rotate at p, keep as bf16 pairs ----------------
-  const int h0 = g * REP;
-  const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;  // token 0 of row b
-  for (int e = lane; e < REP * D; e += 64) qs[e] = (float)qsrc[e];
+  // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
+  const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
+  for (int e = lane; e < REP * D; e += 64) {
+    const int h = e / D, d = e % D;
+    float x = (float)qsrc[e];
+    if (st.rope) {
+      const int di = d < D / 2 ? d : d - D / 2;
+      const float c = st.rope[(p * (D / 2) + di) * 2 + 0];
+      const float sn = st.rope[(p * (D / 2) + di) * 2 + 1];
+      const float other = (float)qsrc[h * D + (d < D / 2 ? d + D / 2 : d - D / 2)];
+      x = d < D / 2 ? x * c - other * sn : other * sn + x * c;
+    }
+    qs[e] = x;
+  }
   __syncthreads();
-  const int kr = lane / LK, j = lane % LK;
+  const int kr = lane / LK, j = lane % LK;          // QK: key in round, chunk group
+  const int half = lane >> 5, mm = lane & 31;       // PV: key half, head-dim row
   uint32_t qp[REP][NCH][4];
 #pragma unroll
   for (int h = 0; h < REP; ++h)
@@ -541,152 +751,206 @@ __global__ __launch_bounds__(64) void k_decode(StepArgs st, LayerArgs la, Partia
     for (int t = 0; t < NCH; ++t)
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
-        float y[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int d = (j + LK * t) * 8 + 2 * e2 + u;
-          const float x = qs[h * D + d];
-          if (st.rope) {
-            const int dd = d < D / 2 ? d : d - D / 2;
-            const float c = st.rope[(p * (D / 2) + dd) * 2 + 0];
-            const float sn = st.rope[(p * (D / 2) + dd) * 2 + 1];
-            y[u] = d < D / 2 ? x * c - qs[h * D + d + D / 2] * sn
-                             : qs[h * D + d - D / 2] * sn + x * c;
-          } else {
-            y[u] = x;
-          }
-        }
-        qp[h][t][e2] = pack_bf16(y[0], y[1]);
+        const int d = (j + LK * t) * 8 + 2 * e2;
+        qp[h][t][e2] = pack_bf16(qs[h * D + d], qs[h * D + d + 1]);
       }
+
+  // -- buffer resources over this head's K and V ------------------------------
+  const int64_t region = (int64_t)la.rows_alloc * D * 2;  // bytes per (b, g)
+  const i32x4 rk = sgpr_rsrc(la.k + bg * region, (int)region);
+  const i32x4 rv = sgpr_rsrc(la.v + bg * region, (int)region);
+  const int koff = (kr * D + j * 8) * 2;
+  const int voff = (mm * kVBlock + half * 8) * 2;
+
+  struct Tile {
+    u32x4 k[NR][NCH];
+    u32x4 v[VT];
+  };
+  constexpr int LPT = NR * NCH + VT;  // loads per tile
+  auto load = [&](int it, Tile &T) {
+    const int t0 = t_begin + (it < n_iter ? it : n_iter - 1) * TK;
+    // K rows and V blocks advance by the same bytes per row
+    const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
+    static_for<0, NR>([&](auto r) {
+      static_for<0, NCH>([&](auto t) {
+        constexpr int off = decltype(r)::value * KR * D * 2 + decltype(t)::value * LK * 16;
+        tile_load<off>(T.k[decltype(r)::value][decltype(t)::value], rk, koff, so);
+      });
+    });
+    static_for<0, VT>([&](auto t) {
+      tile_load<decltype(t)::value * 32 * kVBlock * 2>(T.v[decltype(t)::value], rv, voff, so);
+    });
+  };
+  // Wait for tile T when AFTER tiles were issued after it.
+  auto wait_tile = [&](Tile &T, auto after) {
+    constexpr int N = decltype(after)::value * LPT;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < NCH; ++t) tile_wait<N>(T.k[r][t]);
+#pragma unroll
+    for (int t = 0; t < VT; ++t) tile_wait<N>(T.v[t]);
+  };
 
   const float scale = kLog2e * rsqrtf((float)D);
-  float m[REP], lsum[REP], acc[REP][VT];
+  float m[HPL], lsum[HPL], acc[REP][VT];
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    m[h] = -INFINITY;
-    lsum[h] = 0.f;
+  for (int u = 0; u < HPL; ++u) {
+    m[u] = -INFINITY;
+    lsum[u] = 0.f;
+  }
+#pragma unroll
+  for (int h = 0; h < REP; ++h)
 #pragma unroll
     for (int t = 0; t < VT; ++t) acc[h][t] = 0.f;
-  }
-  const int half = lane >> 5, mm = lane & 31;
-  const bf16 *kbase = reinterpret_cast<const bf16 *>(la.k) + (bg * la.rows_alloc) * D;
+  int hbase = 0;     // first head this lane owns (set by the reduce-scatter)
+  bool writer = true;  // one lane per (key, head) publishes p
 
-  int par = 0;
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += 16, par ^= 1) {
-    // ---- loads: K rows of this lane's keys, V block d-rows of this lane ----
-    uint4 kv[NR][NCH];
+  // One tile: QK, online softmax, P.V.  Rows of the tile outside [lo, hi)
+  // are masked in the scores; their V is finite (rows past a row's end are
+  // zeroed when the append enters a new 32-row tile), so p = 0 cancels them.
+  auto step = [&](int it, Tile &T) {
+    const int t0 = t_begin + it * TK;
+    const int par = it & 1;
+    float a[NR][REP];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const bf16 *kr_ptr = kbase + (t0 + r * KR + kr) * D;
-#pragma unroll
-      for (int t = 0; t < NCH; ++t)
-        kv[r][t] = *reinterpret_cast<const uint4 *>(kr_ptr + (j + LK * t) * 8);
-    }
-    const bf16 *vb = v_block<bf16>(la.v, bg, la.rows_alloc, t0 / kVBlock, D);
-    uint4 vv[VT];
-#pragma unroll
-    for (int t = 0; t < VT; ++t)
-      vv[t] = *reinterpret_cast<const uint4 *>(vb + (mm + 32 * t) * kVBlock + half * 8);
-
-    // ---- scores ----
-    float s[NR][REP];
-#pragma unroll
-    for (int r = 0; r < NR; ++r) {
-      const int64_t key = t0 + r * KR + kr;
-      const bool ok = key >= lo && key < hi;
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
       for (int h = 0; h < REP; ++h) {
-        float a = 0.f;
+        float x = 0.f;
 #pragma unroll
         for (int t = 0; t < NCH; ++t) {
-          a = dot2_bf16(qp[h][t][0], kv[r][t].x, a);
-          a = dot2_bf16(qp[h][t][1], kv[r][t].y, a);
-          a = dot2_bf16(qp[h][t][2], kv[r][t].z, a);
-          a = dot2_bf16(qp[h][t][3], kv[r][t].w, a);
+          x = dot2_bf16(qp[h][t][0], T.k[r][t].x, x);
+          x = dot2_bf16(qp[h][t][1], T.k[r][t].y, x);
+          x = dot2_bf16(qp[h][t][2], T.k[r][t].z, x);
+          x = dot2_bf16(qp[h][t][3], T.k[r][t].w, x);
         }
-        a = group_sum<LK>(a);
-        s[r][h] = ok ? a * scale : -INFINITY;
+        a[r][h] = x;
       }
+    float s[NR][HPL];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      key_reduce_scatter<LK, REP, HPL>(a[r], lane, s[r]);
+      const int key = t0 + r * KR + kr;
+      const bool ok = key >= lo && key < hi;
+#pragma unroll
+      for (int u = 0; u < HPL; ++u) s[r][u] = ok ? s[r][u] : -INFINITY;
     }
-    // ---- online softmax (one running max per head, uniform over the wave) ----
-    float alpha[REP];
-    bool rescale = false;
+    float alpha[HPL];
 #pragma unroll
-    for (int h = 0; h < REP; ++h) {
-      float tm = s[0][h];
+    for (int u = 0; u < HPL; ++u) {
+      float tm = s[0][u];
 #pragma unroll
-      for (int r = 1; r < NR; ++r) tm = fmaxf(tm, s[r][h]);
-      tm = across_groups_max<LK>(tm);
-      const float mn = fmaxf(m[h], tm);
-      alpha[h] = exp2f(m[h] - mn);
-      rescale |= (mn != m[h]);
-      m[h] = mn;
+      for (int r = 1; r < NR; ++r) tm = fmaxf(tm, s[r][u]);
+      tm = keys_max<LK>(tm);
+      // A tile can be entirely masked (a windowed span starting past the
+      // tile's first 16 rows); then mn stays -inf and the subtraction uses 0.
+      const float mn = fmaxf(m[u], tm * scale);
+      const float ms = mn == -INFINITY ? 0.f : mn;
+      alpha[u] = __builtin_amdgcn_exp2f(m[u] - ms);
+      m[u] = mn;
       float ps = 0.f;
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const float pe = exp2f(s[r][h] - mn);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(s[r][u], scale, -ms));
         ps += pe;
-        if (j == 0) {
-          bf16 pb = (bf16)pe;
-          pls[par][h][r * KR + kr] = __builtin_bit_cast(uint16_t, pb);
+        if (writer) {
+          const bf16 pb = (bf16)pe;
+          pls[par][hbase + u][r * KR + kr] = __builtin_bit_cast(uint16_t, pb);
         }
       }
-      lsum[h] = lsum[h] * alpha[h] + ps;
+      lsum[u] = lsum[u] * alpha[u] + ps;
     }
-    __syncthreads();
-    // ---- zero V of keys outside [lo, hi) on edge tiles (stale rows may hold
-    //      anything, and 0 * NaN would leak) ----
-    if (t0 < lo || t0 + 16 > hi) {
-      uint32_t keep[4];
+    // The workgroup is one wave and its LDS operations execute in order, so
+    // the p reads below see the writes above.  (__syncthreads would also wait
+    // for every outstanding global load, draining the tiles in flight.)
+    __builtin_amdgcn_wave_barrier();
+    bool moved = false;
 #pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int64_t k0 = t0 + half * 8 + 2 * e2;
-        keep[e2] = ((k0 >= lo && k0 < hi) ? 0x0000ffffu : 0u) |
-                   ((k0 + 1 >= lo && k0 + 1 < hi) ? 0xffff0000u : 0u);
+    for (int u = 0; u < HPL; ++u) moved |= alpha[u] != 1.f;
+    if (__ballot(moved) != 0) {
+#pragma unroll
+      for (int h = 0; h < REP; ++h) {
+        int u = 0;
+        const int src = owner_lane<LK, REP>(h, &u);  // a lane owning head h
+        const float al = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha[u]), src));
+#pragma unroll
+        for (int t = 0; t < VT; ++t) acc[h][t] *= al;
       }
-#pragma unroll
-      for (int t = 0; t < VT; ++t) {
-        vv[t].x &= keep[0];
-        vv[t].y &= keep[1];
-        vv[t].z &= keep[2];
-        vv[t].w &= keep[3];
-      }
-    }
-    // ---- P.V ----
-    if (__builtin_expect(rescale, 0)) {
-#pragma unroll
-      for (int h = 0; h < REP; ++h)
-#pragma unroll
-        for (int t = 0; t < VT; ++t) acc[h][t] *= alpha[h];
     }
 #pragma unroll
     for (int h = 0; h < REP; ++h) {
       const uint4 pp = *reinterpret_cast<const uint4 *>(&pls[par][h][half * 8]);
 #pragma unroll
       for (int t = 0; t < VT; ++t) {
-        float a = acc[h][t];
-        a = dot2_bf16(vv[t].x, pp.x, a);
-        a = dot2_bf16(vv[t].y, pp.y, a);
-        a = dot2_bf16(vv[t].z, pp.z, a);
-        a = dot2_bf16(vv[t].w, pp.w, a);
-        acc[h][t] = a;
+        float x = acc[h][t];
+        x = dot2_bf16(T.v[t].x, pp.x, x);
+        x = dot2_bf16(T.v[t].y, pp.y, x);
+        x = dot2_bf16(T.v[t].z, pp.z, x);
+        x = dot2_bf16(T.v[t].w, pp.w, x);
+        acc[h][t] = x;
       }
     }
+  };
+
+  // Which lanes publish p: with REP < LK the last log2(LK/REP) stages
+  // all-reduce (the low lane bits), and only the lane with those bits clear
+  // writes; hbase is fixed per lane, computed once here.
+  {
+    float zin[REP], zout[HPL];
+#pragma unroll
+    for (int h = 0; h < REP; ++h) zin[h] = 0.f;
+    hbase = key_reduce_scatter<LK, REP, HPL>(zin, lane, zout);
+    if (REP < LK) writer = (j & (LK / REP - 1)) == 0;
   }
 
-  // ---- partials: (m, l) and unnormalised o for this split ----
+  // Ring of NBUF register tiles; NBUF - 1 tiles are in flight while one
+  // computes.  Unrolled by NBUF so buffer indices are compile-time.
+  // Ring of NBUF register tiles; NBUF - 1 tiles are in flight while one
+  // computes.  Unrolled by NBUF so buffer indices are compile-time.  Loads
+  // and waits run for whole groups (loads past the end re-read the last tile,
+  // which the L2 holds) and only the compute is skipped past the end, so the
+  // loop has one back edge and always the same loads in flight.
+  Tile T[NBUF];
+#pragma unroll
+  for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
+  for (int it = 0; it < n_iter; it += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      load(it + u + NBUF - 1, T[(u + NBUF - 1) % NBUF]);
+      wait_tile(T[u], std::integral_constant<int, NBUF - 1>{});
+      if (it + u < n_iter) step(it + u, T[u]);
+    }
+  }
+  // Retire the loads still in flight before their registers are reused.
+#pragma unroll
+  for (int i = 0; i < NBUF; ++i) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int t = 0; t < NCH; ++t) tile_wait<0>(T[i].k[r][t]);
+#pragma unroll
+    for (int t = 0; t < VT; ++t) tile_wait<0>(T[i].v[t]);
+  }
+
+  // ---- partials of this split ----
   const int64_t cap = kDecodeSplitCap;
 #pragma unroll
-  for (int h = 0; h < REP; ++h) {
-    const float l = across_groups_sum<LK>(lsum[h]);
-    const int64_t slot = ((int64_t)b * st.Hq + h0 + h) * cap + split;
-    if (lane == 0) {
-      pa.dml[slot * 2 + 0] = m[h];
+  for (int u = 0; u < HPL; ++u) {
+    const float l = keys_sum<LK>(lsum[u]);
+    if (kr == 0 && writer) {
+      const int64_t slot = ((int64_t)b * st.Hq + h0 + hbase + u) * cap + split;
+      pa.dml[slot * 2 + 0] = m[u];
       pa.dml[slot * 2 + 1] = l;
     }
+  }
+#pragma unroll
+  for (int h = 0; h < REP; ++h) {
+    const int64_t slot = ((int64_t)b * st.Hq + h0 + h) * cap + split;
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
-      const float o = acc[h][t] + __shfl_xor(acc[h][t], 32);
+      const float o = swap32_sum(acc[h][t]);
       if (half == 0) pa.dout[slot * D + mm + 32 * t] = o;
     }
   }
@@ -698,16 +962,33 @@ bool fast_decode_supported(int D, int rep) {
 
 template <int D, int REP>
 static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                            const void *q, int32_t n_items, void *stream) {
-  hipLaunchKernelGGL((k_decode<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(64), 0,
-                     (hipStream_t)stream, st, la, pa, (const bf16 *)q);
+                            const void *q, int32_t n_items, const Launch &lc) {
+  hipExtLaunchKernelGGL((k_decode<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(64), 0,
+                     (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q);
+}
+
+template <int D, int REP>
+static int decode_waves_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_decode<D, REP>, 64, 0) != hipSuccess)
+    return 0;
+  return n;
+}
+
+int decode_waves_per_cu(int D, int rep) {
+#define KVC_OCC(DD, RR) \
+  if (D == DD && rep == RR) return decode_waves_t<DD, RR>();
+  KVC_OCC(128, 1) KVC_OCC(128, 2) KVC_OCC(128, 4) KVC_OCC(128, 8) KVC_OCC(128, 16)
+  KVC_OCC(64, 1) KVC_OCC(64, 2) KVC_OCC(64, 4) KVC_OCC(64, 8) KVC_OCC(64, 16)
+#undef KVC_OCC
+  return 0;
 }
 
 int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,
-                  int32_t n_items, void *stream) {
+                  int32_t n_items, const Launch &lc) {
 #define KVC_DEC(DD, RR)                                         \
   if (st.D == DD && la.rep == RR) {                             \
-    launch_decode_t<DD, RR>(st, la, pa, q, n_items, stream);    \
+    launch_decode_t<DD, RR>(st, la, pa, q, n_items, lc);    \
     return (int)hipGetLastError();                              \
   }
   KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8) KVC_DEC(128, 16)
@@ -1004,16 +1285,16 @@ bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && re
 
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                           const void *q, int32_t n_items, void *stream) {
-  hipLaunchKernelGGL((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(256), 0,
-                     (hipStream_t)stream, st, la, pa, (const bf16 *)q);
+                           const void *q, int32_t n_items, const Launch &lc) {
+  hipExtLaunchKernelGGL((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(256), 0,
+                     (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q);
 }
 
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,
-                   int32_t n_items, void *stream) {
+                   int32_t n_items, const Launch &lc) {
 #define KVC_CHK(DD, RR)                                         \
   if (st.D == DD && la.rep == RR) {                             \
-    launch_chunk_t<DD, RR>(st, la, pa, q, n_items, stream);     \
+    launch_chunk_t<DD, RR>(st, la, pa, q, n_items, lc);     \
     return (int)hipGetLastError();                              \
   }
   KVC_CHK(128, 1) KVC_CHK(128, 2) KVC_CHK(128, 4) KVC_CHK(128, 8) KVC_CHK(128, 16)
@@ -1029,6 +1310,7 @@ int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &p
 template <typename T>
 __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, PartialArgs pa,
                                                 T *__restrict__ out) {
+  __shared__ float wts[64];
   const int64_t row = blockIdx.x;  // (b * C + i) * Hq + h
   const int h = (int)(row % st.Hq);
   const int64_t bi = row / st.Hq;
@@ -1064,36 +1346,42 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
     ml = pa.pml + s0 * 2;
     os = pa.pout + s0 * D;
   }
-  float mx = -INFINITY;
-  for (int s = lane; s < ns; s += 64) {
-    if (ml[2 * s + 1] > 0.f) mx = fmaxf(mx, ml[2 * s]);
-  }
-  mx = wave_max(mx);
-  float lt = 0.f;
-  for (int s = lane; s < ns; s += 64) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.f) lt += l * exp2f(ml[2 * s] - mx);
-  }
-  lt = wave_sum(lt);
-  const float inv = 1.f / lt;
+  // split weights 2^(m_s - M) / L (splits with no visible key have l == 0)
+  const float ls = lane < ns ? ml[2 * lane + 1] : 0.f;
+  const float ms = (lane < ns && ls > 0.f) ? ml[2 * lane] : -INFINITY;
+  const float M = wave_max(ms);
+  const float w = ls > 0.f ? exp2f(ms - M) : 0.f;
+  const float Lt = wave_sum(w * ls);
+  wts[lane] = w / Lt;
+  __syncthreads();
   for (int d = lane; d < D; d += 64) {
-    float a = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float l = ml[2 * s + 1];
-      if (l > 0.f) a += os[(int64_t)s * D + d] * exp2f(ml[2 * s] - mx);
+    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float w = wts[s + u];
+        const float x = os[(int64_t)(s + u) * D + d];
+        a[u] += w != 0.f ? w * x : 0.f;  // splits without keys: slot never written
+      }
     }
-    o[d] = from_f<T>(a * inv);
+    for (; s < ns; ++s) {
+      const float w = wts[s];
+      const float x = os[(int64_t)s * D + d];
+      a[0] += w != 0.f ? w * x : 0.f;
+    }
+    o[d] = from_f<T>(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
   }
 }
 
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                   void *out, void *stream) {
+                   void *out, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * st.Hq;
   if (dtype == KVC_F32)
-    hipLaunchKernelGGL(k_combine<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_combine<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la, pa, (float *)out);
   else
-    hipLaunchKernelGGL(k_combine<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)stream,
+    hipExtLaunchKernelGGL(k_combine<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
                        st, la, pa, (bf16 *)out);
   return (int)hipGetLastError();
 }

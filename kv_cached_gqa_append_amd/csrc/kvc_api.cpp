@@ -36,6 +36,13 @@ struct kvc_cache {
   std::vector<int32_t> n_new;
   int32_t C = 0;
   std::vector<uint8_t> appended, attended;
+  // decode split planning: compute units, resident decode waves per CU by
+  // query heads per KV head (0 = not yet queried), and overrides
+  int32_t n_cu = 0;
+  int32_t dec_occ[17] = {0};
+  int32_t dec_split_fixed = 0;    // keys per split (multiple of 16); 0 = planned
+  int32_t dec_waves_target = 0;   // waves per decode launch; 0 = resident slots
+  int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   // kernel timing
   bool timing = false;
   std::vector<hipEvent_t> ev;      // 2 per launch
@@ -45,8 +52,7 @@ struct kvc_cache {
 
 namespace {
 
-// Smallest split sizes (keys) before the split count per row is capped.
-constexpr int32_t kDecodeSplitMin = 256;
+// Smallest chunk-attention split (keys) before the split count per row is capped.
 constexpr int32_t kChunkSplitMin = 1024;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
@@ -90,17 +96,65 @@ kvc::LayerArgs layer_args(const kvc_t *h, int layer) {
   return la;
 }
 
-// Timing helpers: events around one launch of `kind`.
-int timing_mark(kvc_t *h, int kind, void *stream) {
-  if (!h->timing) return -1;
-  if (2 * (h->ev_used + 1) > (int32_t)h->ev.size()) return -1;
+// Where the next launch of `kind` goes.  With kernel timing on it carries a
+// fresh pair of events that the dispatch stamps at its own start and end, so
+// the measured time is the kernel's alone and no marker packets are added to
+// the stream.
+kvc::Launch launch_on(kvc_t *h, int kind, void *stream) {
+  kvc::Launch lc;
+  lc.stream = stream;
+  if (!h->timing || 2 * (h->ev_used + 1) > (int32_t)h->ev.size()) return lc;
   const int i = h->ev_used++;
   h->ev_kind[i] = kind;
-  (void)hipEventRecord(h->ev[2 * i], (hipStream_t)stream);
-  return i;
+  lc.t0 = h->ev[2 * i];
+  lc.t1 = h->ev[2 * i + 1];
+  return lc;
 }
-void timing_close(kvc_t *h, int i, void *stream) {
-  if (i >= 0) (void)hipEventRecord(h->ev[2 * i + 1], (hipStream_t)stream);
+
+void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi);
+
+// Keys per decode split for this layer and step.  The decode launch should be
+// one round of equally long waves: the smallest split (in 16-key tiles) whose
+// wave count, summed over the decoding rows and KV heads, fits the waves the
+// chip holds at once.  A partial second round or a few long waves would leave
+// most of the chip idle at the end of the launch.  Each row keeps at most
+// kDecodeSplitCap splits.
+int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
+  const int TK = kvc::kDecodeTile;
+  std::vector<int64_t> tiles;
+  int64_t max_t = 0;
+  for (int32_t b = 0; b < h->cfg.batch; ++b) {
+    if (h->n_new[b] != 1) continue;
+    int64_t base, hi;
+    decode_span(la, h->lens_host[b], &base, &hi);
+    tiles.push_back((hi - base + TK - 1) / TK);
+    max_t = std::max(max_t, tiles.back());
+  }
+  const int64_t q_min = std::max<int64_t>(1, (max_t + kvc::kDecodeSplitCap - 1) /
+                                                 kvc::kDecodeSplitCap);
+  if (max_t == 0) return TK;
+  if (h->dec_split_fixed > 0)
+    return (int32_t)(std::max<int64_t>(h->dec_split_fixed / TK, q_min) * TK);
+  int64_t target = h->dec_waves_target;
+  if (target <= 0) {
+    int32_t &occ = h->dec_occ[la.rep <= 16 ? la.rep : 0];
+    if (occ == 0) occ = std::max(1, kvc::decode_waves_per_cu(D, la.rep));
+    target = (int64_t)h->n_cu * occ;
+  }
+  auto waves = [&](int64_t q) {
+    int64_t w = 0;
+    for (int64_t t : tiles) w += (t + q - 1) / q;
+    return w * la.hkv;
+  };
+  int64_t lo = q_min, hi = std::max(q_min, max_t);
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (waves(mid) <= target)
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return (int32_t)(lo * TK);
 }
 
 // Key span of a one-token query at p on this layer, in storage rows.
@@ -115,7 +169,7 @@ void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi
     lo = la.window > 0 ? std::max<int64_t>(0, p - la.window + 1) : 0;
     *hi = p + 1;
   }
-  *base = lo / kvc::kVBlock * kvc::kVBlock;
+  *base = lo / kvc::kRowAlign * kvc::kRowAlign;
 }
 
 // Key span of a chunk of n tokens starting at L on a non-ring layer.
@@ -206,8 +260,25 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     delete h;
     return KVC_E_HIP;
   }
+  if (hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
+          hipSuccess ||
+      h->n_cu <= 0) {
+    delete h;
+    return KVC_E_HIP;
+  }
+  // Experiment overrides of the decode split plan.
+  if (const char *e = std::getenv("KVC_DECODE_SPLIT")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= kvc::kDecodeTile && v <= (1 << 20) && v % kvc::kDecodeTile == 0)
+      h->dec_split_fixed = (int32_t)v;
+  }
+  if (const char *e = std::getenv("KVC_DECODE_WAVES")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= (1 << 24)) h->dec_waves_target = (int32_t)v;
+  }
   if (const char *e = std::getenv("KVC_LOG")) {
-    if (e[0] == '1')
+    h->log_level = std::atoi(e);
+    if (h->log_level >= 1)
       std::fprintf(stderr, "[kvc] %d layers, B %d, KV %.1f MiB (formula), buffer %.1f MiB\n",
                    cfg->n_layer, cfg->batch, h->lay.kv_bytes / 1048576.0,
                    h->lay.total / 1048576.0);
@@ -265,9 +336,7 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
   }
   const kvc::StepArgs st = step_args(h);
   const kvc::LayerArgs la = layer_args(h, layer);
-  const int t = timing_mark(h, KVC_K_APPEND, stream);
-  int err = kvc::launch_append(h->cfg.dtype, st, la, k, v, slot_out_dev, stream);
-  timing_close(h, t, stream);
+  int err = kvc::launch_append(h->cfg.dtype, st, la, k, v, slot_out_dev, launch_on(h, KVC_K_APPEND, stream));
   if (err) return KVC_E_HIP;
   h->appended[layer] = 1;
   return KVC_OK;
@@ -289,20 +358,15 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
                     kvc::fast_prefill_supported(D, la.rep);
   int err = 0;
   if (!fast) {
-    const int t = timing_mark(h, KVC_K_GENERIC, stream);
-    err = kvc::launch_generic(h->cfg.dtype, st, la, q, out, stream);
-    timing_close(h, t, stream);
+    err = kvc::launch_generic(h->cfg.dtype, st, la, q, out, launch_on(h, KVC_K_GENERIC, stream));
     if (err) return KVC_E_HIP;
   } else {
     // Plan: decode rows (one token) and chunk rows (two or more tokens).
-    int64_t max_dec = 0, max_chunk_span = 0;
+    int64_t max_chunk_span = 0;
     for (int32_t b = 0; b < B; ++b) {
       const int64_t L = h->lens_host[b], n = h->n_new[b];
       int64_t base, hi;
-      if (n == 1) {
-        decode_span(la, L, &base, &hi);
-        max_dec = std::max(max_dec, hi - base);
-      } else if (n >= 2 && !la.ring) {
+      if (n >= 2 && !la.ring) {
         chunk_span(la, L, n, &base, &hi);
         max_chunk_span = std::max(max_chunk_span, hi - base);
       }
@@ -313,8 +377,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
     pa.pml = h->lay.pml_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pml_off) : nullptr;
     pa.pout = h->lay.pout_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pout_off) : nullptr;
     pa.max_chunk = h->cfg.max_chunk;
-    pa.dec_split_keys = (int32_t)std::max<int64_t>(
-        kDecodeSplitMin, round_up(ceil_div(max_dec, kvc::kDecodeSplitCap), kvc::kVBlock));
+    pa.dec_split_keys = decode_split_keys(h, la, D);
     pa.pre_split_keys = (int32_t)std::max<int64_t>(
         kChunkSplitMin, round_up(ceil_div(max_chunk_span, kvc::kChunkSplitCap), kvc::kRowAlign));
     int64_t dec_items = 0, pre_items = 0;
@@ -334,27 +397,22 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
         pre_items += nqt * nks;
       }
     }
+    if (h->log_level >= 2 && layer == 0 && dec_items > 0)
+      std::fprintf(stderr, "[kvc] decode plan: %d keys per split, %lld waves\n",
+                   pa.dec_split_keys, (long long)dec_items * la.hkv);
     if (dec_items > 0) {
-      const int t = timing_mark(h, KVC_K_DECODE, stream);
-      err = kvc::launch_decode(st, la, pa, q, (int32_t)dec_items, stream);
-      timing_close(h, t, stream);
+      err = kvc::launch_decode(st, la, pa, q, (int32_t)dec_items, launch_on(h, KVC_K_DECODE, stream));
       if (err) return KVC_E_HIP;
     }
     if (pre_items > 0) {
-      const int t = timing_mark(h, KVC_K_PREFILL, stream);
-      err = kvc::launch_prefill(st, la, pa, q, (int32_t)pre_items, stream);
-      timing_close(h, t, stream);
+      err = kvc::launch_prefill(st, la, pa, q, (int32_t)pre_items, launch_on(h, KVC_K_PREFILL, stream));
       if (err) return KVC_E_HIP;
     }
-    const int t = timing_mark(h, KVC_K_COMBINE, stream);
-    err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, stream);
-    timing_close(h, t, stream);
+    err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
     if (err) return KVC_E_HIP;
   }
   if (staged) {
-    const int t = timing_mark(h, KVC_K_COMMIT, stream);
-    err = kvc::launch_commit(h->cfg.dtype, st, la, stream);
-    timing_close(h, t, stream);
+    err = kvc::launch_commit(h->cfg.dtype, st, la, launch_on(h, KVC_K_COMMIT, stream));
     if (err) return KVC_E_HIP;
   }
   h->attended[layer] = 1;

@@ -20,6 +20,8 @@ constexpr int kVBlock = 16;
 constexpr int kRowAlign = 32;
 // Caps on split-K partial slots per query row.
 constexpr int kDecodeSplitCap = 64;
+// Keys per decode tile; decode splits are whole tiles.
+constexpr int kDecodeTile = 16;
 constexpr int kChunkSplitCap = 16;
 // Query rows per chunk-attention workgroup (4 waves x 16 rows).
 constexpr int kChunkQTile = 64;
@@ -70,8 +72,15 @@ struct PartialArgs {
   float *dml, *dout;      // decode partials
   float *pml, *pout;      // chunk partials
   int32_t max_chunk;
-  int32_t dec_split_keys; // keys per decode split (multiple of 16)
+  int32_t dec_split_keys; // keys per decode split (multiple of 32)
   int32_t pre_split_keys; // keys per chunk split (multiple of 32)
+};
+
+// Where a launch goes: the caller's stream and, when kernel timing is on, a
+// pair of events the dispatch itself stamps at its start and end.
+struct Launch {
+  void *stream = nullptr;
+  void *t0 = nullptr, *t1 = nullptr;  // hipEvent_t or null
 };
 
 // Launchers (kernels.hip).  Return hipError_t as int (0 = success).
@@ -79,17 +88,19 @@ int launch_set_rows(int32_t *dst, const int32_t *vals, int32_t n, void *stream);
 int launch_reset_rows(int32_t *lens, const int32_t *rows, int32_t n, void *stream);
 int launch_advance(int32_t *lens, const int32_t *n_new, int32_t B, void *stream);
 int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void *k,
-                  const void *v, int32_t *slot_out, void *stream);
-int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, void *stream);
+                  const void *v, int32_t *slot_out, const Launch &lc);
+int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc);
 int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                  const void *q, int32_t n_items, void *stream);
+                  const void *q, int32_t n_items, const Launch &lc);
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                   const void *q, int32_t n_items, void *stream);
+                   const void *q, int32_t n_items, const Launch &lc);
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                   void *out, void *stream);
+                   void *out, const Launch &lc);
 int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const void *q,
-                   void *out, void *stream);
+                   void *out, const Launch &lc);
 bool fast_decode_supported(int D, int rep);
+// Decode workgroups (one wave each) resident per compute unit; 0 on error.
+int decode_waves_per_cu(int D, int rep);
 bool fast_prefill_supported(int D, int rep);
 
 }  // namespace kvc
