@@ -7,10 +7,12 @@ idle rows (n_new = 0, redrawn per step).  The history is filled through the
 real protocol in 64-token chunks before timing (untimed); q/k/v are
 synthetic N(0, 1) tensors already resident in HBM.
 
-One step = for each of the 32 layers kvc_append + kvc_attend, then one
-kvc_advance.  Warmup steps run first; the timed steps are bracketed by
-torch.cuda.synchronize().  Decode kernel durations come from HIP events the
-library records on the launch stream around each decode launch.
+One step = for each of the 32 layers kvc_append_attend (one kernel per layer
+for these one-token steps: RoPE + append, decode attention, split merge), then
+one kvc_advance; ``--two-calls`` runs kvc_append + kvc_attend instead (append,
+decode and combine kernels).  Warmup steps run first; the timed steps are
+bracketed by torch.cuda.synchronize().  Kernel durations come from HIP events
+that each dispatch stamps at its own start and end on the launch stream.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
 GPU.  ``--cpu-baseline-seconds 0`` skips the oracle timing.
@@ -36,7 +38,8 @@ import workloads as wl  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "kv_cached_gqa_append_amd", "csrc", "kernels.hip")
-COUNTER_SUMMARY = os.path.join(ROOT, "profiles", "k_decode_decode_b64_hbm.md")
+COUNTER_SUMMARY = {False: os.path.join(ROOT, "profiles", "k_decode_decode_b64_hbm.md"),
+                   True: os.path.join(ROOT, "profiles", "k_decode_fused_decode_b64_hbm.md")}
 COPY_BYTES = 2 ** 30   # the --copy-probe device copy: 1 GiB read, 1 GiB written
 
 
@@ -54,6 +57,16 @@ def decode_kernel_bytes(lens, n_new, work):
     kv = int(((lens[act] + 1) * hkv * D * s * 2).sum())
     qb = int(act.sum()) * hq * D * s
     return kv + qb
+
+
+def fused_kernel_bytes(lens, n_new, work):
+    """Algorithmic bytes of one single-kernel launch (one layer): the decode
+    bytes, every row's new (or padded) k and v read and written to its slot,
+    and every row's output written (zeros for idle rows)."""
+    s = work.dtype_bytes
+    hkv, D, hq, B = work.n_kv_head[0], work.head_dim, work.n_q_head, work.batch
+    return (decode_kernel_bytes(lens, n_new, work) + B * hkv * D * s * 2 * 2
+            + B * hq * D * s)
 
 
 def step_bytes(lens, n_new, work):
@@ -89,15 +102,16 @@ def plan_lens(work, steps, warmup):
     return lens0, [wl.n_new_decode_b64(s, work.batch) for s in range(total)]
 
 
-def timed_decode_bytes(work, steps, warmup):
+def timed_decode_bytes(work, steps, warmup, fused=False):
     """Algorithmic bytes of each timed decode launch, in launch order."""
+    per_launch = fused_kernel_bytes if fused else decode_kernel_bytes
     lens0, sched = plan_lens(work, steps, warmup)
     lens = lens0.copy()
     for s in range(warmup):
         lens = lens + sched[s]
     out = []
     for s in range(warmup, warmup + steps):
-        out += [decode_kernel_bytes(lens, sched[s], work)] * work.n_layer
+        out += [per_launch(lens, sched[s], work)] * work.n_layer
         lens = lens + sched[s]
     return out
 
@@ -110,14 +124,16 @@ def _kname(name):
     return name
 
 
-def summarize_trace(trace_csv, steps, warmup, layers):
+def summarize_trace(trace_csv, steps, warmup, layers, fused=False):
     """Markdown table of the timed region of a rocprofv3 kernel trace of this
-    bench: the dispatches from the first timed decode on."""
+    bench: the dispatches from the first timed step's n_new upload on."""
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
     names = [_kname(r["Kernel_Name"]) for r in rows]
     work = workload_for(layers)
     dec = [i for i, n in enumerate(names) if n == "k_decode"]
-    first = dec[-steps * work.n_layer] - 1          # the append before it
+    first = dec[-steps * work.n_layer]
+    while names[first] != "k_set_rows":            # the step's n_new upload
+        first -= 1
     sel = rows[first:]
     t0, t1 = int(sel[0]["Start_Timestamp"]), int(sel[-1]["End_Timestamp"])
     by = {}
@@ -126,7 +142,7 @@ def summarize_trace(trace_csv, steps, warmup, layers):
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     gaps = [(int(b["Start_Timestamp"]) - int(a["End_Timestamp"])) / 1e3
             for a, b in zip(sel[:-1], sel[1:])]
-    nb = timed_decode_bytes(work, steps, warmup)
+    nb = timed_decode_bytes(work, steps, warmup, fused)
     out = [f"timed region: {len(sel)} dispatches, {(t1 - t0) / 1e6:.3f} ms, "
            f"{(t1 - t0) / 1e3 / steps:.1f} us per step", "",
            "| kernel | dispatches | avg us | median us | min us | max us |",
@@ -144,11 +160,11 @@ def summarize_trace(trace_csv, steps, warmup, layers):
     return "\n".join(out)
 
 
-def summarize_counters(fetch_csv, write_csv, steps, warmup, layers):
+def summarize_counters(fetch_csv, write_csv, steps, warmup, layers, fused=False):
     """Markdown summary of FETCH_SIZE / WRITE_SIZE per timed decode dispatch,
     scaled by what the same counters read for the 1 GiB copy probe."""
     work = workload_for(layers)
-    nb = timed_decode_bytes(work, steps, warmup)
+    nb = timed_decode_bytes(work, steps, warmup, fused)
     vals = {}
     for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Dispatch_Id"]))
@@ -176,11 +192,11 @@ def summarize_counters(fetch_csv, write_csv, steps, warmup, layers):
     return "\n".join(out)
 
 
-def counter_traffic(bytes_per_launch):
+def counter_traffic(bytes_per_launch, fused):
     """HBM traffic per decode launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
     try:
-        text = open(COUNTER_SUMMARY).read()
+        text = open(COUNTER_SUMMARY[fused]).read()
     except OSError:
         return None
     kv = dict(l.split(": ", 1) for l in text.splitlines()
@@ -273,6 +289,8 @@ def main():
     ap.add_argument("--steps", type=int, default=56)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--two-calls", action="store_true",
+                    help="kvc_append + kvc_attend per layer instead of kvc_append_attend")
     ap.add_argument("--layers", type=int, default=0,
                     help="fewer layers (counter runs: per-launch work is unchanged)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -286,10 +304,12 @@ def main():
                          "--copy-probe) and exit")
     args = ap.parse_args()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers))
+        print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers,
+                              not args.two_calls))
         return
     if args.summarize_counters:
-        print(summarize_counters(*args.summarize_counters, args.steps, args.warmup, args.layers))
+        print(summarize_counters(*args.summarize_counters, args.steps, args.warmup, args.layers,
+                                 not args.two_calls))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
@@ -318,10 +338,16 @@ def main():
           for _ in range(work.n_layer)]
     outs = [torch.empty_like(x) for x in qs]
 
+    fused = not args.two_calls
+
     def run_step(n):
-        for l in range(work.n_layer):
-            cache.append(l, ks[l], vs[l], n)
-            cache.attend(l, qs[l], outs[l])
+        if fused:
+            for l in range(work.n_layer):
+                cache.append_attend(l, qs[l], ks[l], vs[l], n, out=outs[l])
+        else:
+            for l in range(work.n_layer):
+                cache.append(l, ks[l], vs[l], n)
+                cache.attend(l, qs[l], outs[l])
         cache.advance()
 
     for s in range(args.warmup):
@@ -332,7 +358,8 @@ def main():
     lens_cur = lens_at.copy()
     for s in range(args.warmup, total_steps):
         n = schedule[s]
-        kbytes += decode_kernel_bytes(lens_cur, n, work) * work.n_layer
+        kbytes += (fused_kernel_bytes if fused else decode_kernel_bytes)(lens_cur, n, work) \
+            * work.n_layer
         sbytes += step_bytes(lens_cur, n, work)
         tokens += int(n.sum())
         lens_cur = lens_cur + n
@@ -345,7 +372,7 @@ def main():
     dt = time.perf_counter() - t0
     kt = K.kvc_timing_end(cache.handle)
     assert cache.lens() == lens_cur.tolist()
-    dec_ms, dec_n = kt["decode"]
+    dec_ms, dec_n = kt["fused" if fused else "decode"]
     ms_step = dt * 1e3 / args.steps
     achieved = kbytes / (dec_ms / 1e3) / 1e9 if dec_ms > 0 else 0.0
     value = sbytes / dt / 1e9
@@ -370,7 +397,7 @@ def main():
         cpu = cpu_baseline(work, lens0, args.cpu_baseline_seconds)
         log(f"[bench] cpu baseline: {cpu['value']:.3f} tok/s ({cpu['sample']})")
 
-    traffic = counter_traffic(kbytes / max(dec_n, 1))
+    traffic = counter_traffic(kbytes / max(dec_n, 1), fused)
     line = {
         "metric": "decode cached-attn HBM GB/s (% of peak) + tokens/s, B=64 ctx<=8k bf16",
         "value": round(value, 1),
@@ -389,8 +416,10 @@ def main():
         "config": {"workload": "decode_b64", "n_layer": work.n_layer, "batch": B,
                    "n_q_head": work.n_q_head, "n_kv_head": work.n_kv_head[0], "head_dim": D,
                    "max_len": work.max_len, "lens_init": "U[1,8128]", "idle_rows_per_step": 6,
-                   "new_tokens_per_row": 1},
-        "roofline": {"bound": "hbm", "kernel": "k_decode<128,4>",
+                   "new_tokens_per_row": 1,
+                   "entry": "kvc_append_attend" if fused else "kvc_append+kvc_attend"},
+        "roofline": {"bound": "hbm",
+                     "kernel": "k_decode<128,4,fused>" if fused else "k_decode<128,4>",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic["bytes"] if traffic else None,

@@ -138,6 +138,23 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
  * follow this layer's kvc_append in the same step (else KVC_E_STATE). */
 int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
 
+/* kvc_append followed by kvc_attend for one layer, in one call: same
+ * arguments (q and out as for kvc_attend), same checks, same results, same
+ * step protocol (the layer counts as appended and attended).  A one-token
+ * step (C == 1) in bf16 with a decode-kernel head shape (D in {64, 128},
+ * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs as a single kernel: the rotation and
+ * store of each row's new key and value, decode attention over its key
+ * splits, and the merge of the splits (the last split of a row and KV head to
+ * finish merges them; tiny_agent "generate.py" _append_chunk writes a token
+ * and attends over it in one pass).  Other steps enqueue the two calls' work.
+ * While one such single-kernel launch runs, no other launch of the same
+ * handle may run concurrently (they share split counters in the buffer).
+ * Errors as for kvc_append; KVC_E_HIP if a launch fails after the append's
+ * work was enqueued. */
+int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k,
+                      const void *v, const int32_t *n_new_host, int32_t C,
+                      int32_t *slot_out_dev, void *out, void *stream);
+
 /* End the step: lens[b] += n_new[b] on the device and in the host mirror.
  * Every layer must have been appended and attended (else KVC_E_STATE). */
 int kvc_advance(kvc_t *h, void *stream);
@@ -176,9 +193,10 @@ int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info);
  *   kvc_timing_end:   wait for the recorded events, write the summed kernel
  *                     time in ms and the launch count per kind, stop.
  * Kinds: 0 append, 1 decode attention, 2 chunk attention, 3 split combine,
- * 4 ring commit, 5 generic attention. */
+ * 4 ring commit, 5 generic attention, 6 single-kernel append + decode +
+ * merge (kvc_append_attend). */
 enum { KVC_K_APPEND = 0, KVC_K_DECODE = 1, KVC_K_PREFILL = 2, KVC_K_COMBINE = 3,
-       KVC_K_COMMIT = 4, KVC_K_GENERIC = 5, KVC_K_NKINDS = 6 };
+       KVC_K_COMMIT = 4, KVC_K_GENERIC = 5, KVC_K_FUSED = 6, KVC_K_NKINDS = 7 };
 int kvc_timing_begin(kvc_t *h, int32_t max_launches);
 int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind);
 

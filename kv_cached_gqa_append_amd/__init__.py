@@ -27,7 +27,7 @@ LIB_PATH = os.path.join(HERE, "libkvc.so")
 KVC_OK, KVC_E_ARG, KVC_E_FULL, KVC_E_DTYPE, KVC_E_STATE, KVC_E_HIP = 0, -1, -2, -3, -4, -5
 KVC_F32, KVC_BF16 = 0, 1
 KVC_NB_KV, KVC_NB_ALLOC = 0, 1
-KERNEL_KINDS = ("append", "decode", "chunk", "combine", "commit", "generic")
+KERNEL_KINDS = ("append", "decode", "chunk", "combine", "commit", "generic", "fused")
 
 _DTYPES = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
 _TORCH_OF = {KVC_F32: torch.float32, KVC_BF16: torch.bfloat16}
@@ -111,6 +111,8 @@ def lib():
         L.kvc_append.restype = ctypes.c_int
         L.kvc_attend.argtypes = [VP, I32, VP, VP, VP]
         L.kvc_attend.restype = ctypes.c_int
+        L.kvc_append_attend.argtypes = [VP, I32, VP, VP, VP, P(I32), I32, VP, VP, VP]
+        L.kvc_append_attend.restype = ctypes.c_int
         L.kvc_advance.argtypes = [VP, VP]
         L.kvc_advance.restype = ctypes.c_int
         L.kvc_lens.argtypes = [VP, P(I32)]
@@ -222,6 +224,16 @@ def kvc_attend(h, layer: int, q: torch.Tensor, out: torch.Tensor, stream=None) -
            "kvc_attend")
 
 
+def kvc_append_attend(h, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_new,
+                      C: int, out: torch.Tensor, slot_out=None, stream=None) -> None:
+    arr, _ = _rows_array(n_new)
+    so = ctypes.c_void_p(slot_out.data_ptr()) if slot_out is not None else ctypes.c_void_p()
+    _check(lib().kvc_append_attend(h, int(layer), ctypes.c_void_p(q.data_ptr()),
+                                   ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+                                   arr, int(C), so, ctypes.c_void_p(out.data_ptr()),
+                                   _stream_handle(stream)), "kvc_append_attend")
+
+
 def kvc_advance(h, stream=None) -> None:
     _check(lib().kvc_advance(h, _stream_handle(stream)), "kvc_advance")
 
@@ -327,6 +339,25 @@ class Cache:
         else:
             self._check_tensor(out, self.n_q_head, C, "out")
         kvc_attend(self.handle, layer, q, out, stream)
+        return out
+
+    def append_attend(self, layer, q, k, v, n_new, out=None, slot_out=None, stream=None):
+        """append() then attend() of one layer in one call (one kernel for a
+        one-token bf16 step)."""
+        if len(n_new) != self.batch:
+            raise ValueError(f"n_new has {len(n_new)} entries, cache batch is {self.batch}")
+        C = int(k.shape[1])
+        hk = self.n_kv_head[layer]
+        self._check_tensor(k, hk, C, "k")
+        self._check_tensor(v, hk, C, "v")
+        self._check_tensor(q, self.n_q_head, C, "q")
+        if out is None:
+            out = torch.empty_like(q)
+        else:
+            self._check_tensor(out, self.n_q_head, C, "out")
+        if slot_out is not None and (slot_out.dtype != torch.int32 or slot_out.numel() != self.batch * C):
+            raise ValueError("slot_out must be int32 (B, C)")
+        kvc_append_attend(self.handle, layer, q, k, v, n_new, C, out, slot_out, stream)
         return out
 
     def advance(self, stream=None):

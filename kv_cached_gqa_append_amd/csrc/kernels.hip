@@ -57,6 +57,14 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
+// RoPE of one (d, d + D/2) pair by (cos, sin), with the multiply-adds spelled
+// out so every kernel rounds it identically.
+__device__ __forceinline__ void rope_pair(float x1, float x2, float c, float sn, float *y1,
+                                          float *y2) {
+  *y1 = fmaf(x1, c, -(x2 * sn));
+  *y2 = fmaf(x1, sn, x2 * c);
+}
+
 // DPP moves within a row of 16 lanes.
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -261,12 +269,8 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
   for (int e = threadIdx.x; e < half; e += 64) {
     const float x1 = to_f(ks[e]), x2 = to_f(ks[e + half]);
     float y1 = x1, y2 = x2;
-    if (rot) {
-      const float c = st.rope[(p * half + e) * 2 + 0];
-      const float s = st.rope[(p * half + e) * 2 + 1];
-      y1 = x1 * c - x2 * s;
-      y2 = x1 * s + x2 * c;
-    }
+    if (rot) rope_pair(x1, x2, st.rope[(p * half + e) * 2 + 0], st.rope[(p * half + e) * 2 + 1],
+                       &y1, &y2);
     kd[e] = from_f<T>(y1);
     kd[e + half] = from_f<T>(y2);
     // A padded token's V goes to the scratch row as zeros: the row can sit
@@ -542,11 +546,14 @@ struct DecodeShape {
   static constexpr int NCH = D / 8 / LK;        // 16-byte chunks per lane per key
   static constexpr int VT = D / 32;             // V head-dim rows per lane
   static constexpr int HPL = REP >= LK ? REP / LK : 1;   // heads whose scores a lane owns
-  // Register tile ring and occupancy target per SIMD.  REP 16 at D 128 holds
-  // 64 accumulators and 64 query registers per lane: it runs one wave per
-  // SIMD with the full register file rather than spill.
+  // Register tile ring and occupancy target per SIMD.  Two tiles in flight
+  // per wave (8 KB of K and V at D 128) keep HBM busy at two waves per SIMD;
+  // deeper rings measured no faster and only lengthen the queues every
+  // dependent round trip waits in.  REP 16 at D 128 holds 64 accumulators and
+  // 64 query registers per lane: it runs one wave per SIMD with the full
+  // register file rather than spill.
   static constexpr bool BIG = REP * D >= 2048;
-  static constexpr int NBUF = REP <= 4 ? 5 : (REP <= 8 ? 4 : 2);
+  static constexpr int NBUF = REP <= 8 ? 3 : 2;
   static constexpr int WAVES = BIG ? 1 : 2;
   static_assert(NCH >= 1 && NR >= 1 && D % 32 == 0, "unsupported decode shape");
 };
@@ -575,11 +582,13 @@ __device__ __forceinline__ i32x4 sgpr_rsrc(const void *base, int bytes) {
 // flight.  Each wait names the registers it covers ("+v"), so no use of a
 // tile can be scheduled before its wait; the build scans the generated
 // assembly for any other instruction touching a register between its load
-// and its wait.
+// and its wait.  The loads are non-temporal (nt): every K and V byte is read
+// once per step, and streaming them past the caches measured about 9 %
+// faster on the decode launch than cached loads.
 template <int OFF>
 __device__ __forceinline__ void tile_load(u32x4 &x, i32x4 rsrc, int voff, int soff) {
   static_assert(OFF >= 0 && OFF < 4096, "buffer immediate offsets are 12 bits");
-  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 ; tile load"
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 nt ; tile load"
                : "=v"(x)
                : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF));
 }
@@ -682,10 +691,154 @@ __device__ __forceinline__ float keys_sum(float x) {
 
 // NBUF: register tiles in the ring (NBUF - 1 in flight); WAVES: occupancy the
 // register allocator must meet.
-template <int D, int REP, int NBUF = DecodeShape<D, REP>::NBUF,
+// Append of a single-token step (C == 1) for (row b, KV head g): a real
+// token at position p goes to its slot (full layout: p, ring: p % W) with K
+// rotated and V copied; a padded token (valid == false) goes to the scratch
+// row with V zeroed.  Also the slot report and, for a real token entering a
+// new 32-row tile, the zeroing of V past the row's end in that tile (the
+// decode tiles read those rows masked).  Same stores as k_append.
+template <int D>
+__device__ __forceinline__ void decode_append(const StepArgs &st, const LayerArgs &la,
+                                              const FusedArgs &fa, int b, int g, int64_t p,
+                                              bool valid, int lane) {
+  const int64_t bg = (int64_t)b * la.hkv + g;
+  const int64_t r = la.ring ? (valid ? p % la.window : (int64_t)la.window)
+                            : (valid ? p : (int64_t)la.rows);
+  const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
+  const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
+  bf16 *kd = k_row<bf16>(la.k, bg, la.rows_alloc, r, D);
+  bf16 *vd = v_elem<bf16>(la.v, bg, la.rows_alloc, r, 0, D);
+  const bool rot = st.rope != nullptr && valid;
+  constexpr int half = D / 2;
+  for (int e = lane; e < half; e += 64) {
+    const float x1 = (float)ks[e], x2 = (float)ks[e + half];
+    float y1 = x1, y2 = x2;
+    if (rot) rope_pair(x1, x2, st.rope[(p * half + e) * 2 + 0], st.rope[(p * half + e) * 2 + 1],
+                       &y1, &y2);
+    kd[e] = (bf16)y1;
+    kd[e + half] = (bf16)y2;
+    vd[e * kVBlock] = valid ? vs[e] : (bf16)0.f;
+    vd[(e + half) * kVBlock] = valid ? vs[e + half] : (bf16)0.f;
+  }
+  if (fa.slot_out && g == 0 && lane == 0) fa.slot_out[b] = (int32_t)r;
+  if (valid) {
+    const int64_t W = la.window;
+    const int64_t old_top = la.ring ? (p < W ? p : W) : p;
+    const int64_t new_top = la.ring ? (p + 1 < W ? p + 1 : W) : p + 1;
+    if (old_top == 0 || (new_top - 1) / kRowAlign != (old_top - 1) / kRowAlign) {
+      int64_t end = (new_top + kRowAlign - 1) / kRowAlign * kRowAlign;
+      if (end > la.rows_alloc) end = la.rows_alloc;
+      for (int d = lane; d < D; d += 64)
+        for (int64_t rz = new_top; rz < end; ++rz)
+          *v_elem<bf16>(la.v, bg, la.rows_alloc, rz, d, D) = (bf16)0.f;
+    }
+  }
+}
+
+// One term of a split merge: a + w * x, skipping splits of weight 0 (a split
+// that saw no visible key never wrote its slot).  Shared by both merges so
+// they round identically.
+__device__ __forceinline__ float combine_acc(float a, float w, float x) {
+  return w != 0.f ? fmaf(w, x, a) : a;
+}
+__device__ __forceinline__ float combine_tree(const float (&a)[8]) {
+  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
+// Merge of the ns decode splits of the REP heads h0.. of row b into the
+// output o (REP x D) by one wave, with the same arithmetic in the same order
+// as k_combine.  The partials are read with agent-scope loads (served from
+// the device's point of coherence, past this XCD's L2).  Each lane owns D/64
+// consecutive elements; the loads of 8 splits of up to 4 heads are issued
+// together, so a merge of up to 8 splits costs one round trip per 4 heads.
+// wts: REP * 64 floats of LDS.
+template <int D, int REP>
+__device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepArgs &st, int b,
+                                              int h0, int ns, float *wts, bf16 *o, int lane) {
+  auto ld = [](const float *ptr) {
+    return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const int64_t cap = kDecodeSplitCap;
+  float lv[REP], mv[REP];
+#pragma unroll
+  for (int h = 0; h < REP; ++h) {
+    const float *ml = pa.dml + ((int64_t)b * st.Hq + h0 + h) * cap * 2;
+    lv[h] = lane < ns ? ld(ml + 2 * lane + 1) : 0.f;
+    mv[h] = lane < ns ? ld(ml + 2 * lane) : -INFINITY;
+  }
+#pragma unroll
+  for (int h = 0; h < REP; ++h) {
+    const float ms = (lane < ns && lv[h] > 0.f) ? mv[h] : -INFINITY;
+    const float M = wave_max(ms);
+    const float w = lv[h] > 0.f ? exp2f(ms - M) : 0.f;
+    const float Lt = wave_sum(w * lv[h]);
+    wts[h * 64 + lane] = w / Lt;
+  }
+  __syncthreads();
+  constexpr int DPL = D / 64;                 // elements per lane
+  constexpr int HG = REP < 4 ? REP : 4;       // heads per load round
+  const int d0 = lane * DPL;
+#pragma unroll
+  for (int hg = 0; hg < REP; hg += HG) {
+    float a[HG][DPL][8];
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[h][e][u] = 0.f;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float x[HG][8][DPL];
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        const float *os = pa.dout + ((int64_t)b * st.Hq + h0 + hg + h) * cap * D + d0;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) x[h][u][e] = ld(os + (int64_t)(s + u) * D + e);
+      }
+#pragma unroll
+      for (int h = 0; h < HG; ++h)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float w = wts[(hg + h) * 64 + s + u];
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) a[h][e][u] = combine_acc(a[h][e][u], w, x[h][u][e]);
+        }
+    }
+    for (; s < ns; ++s) {
+      float x[HG][DPL];
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        const float *os = pa.dout + ((int64_t)b * st.Hq + h0 + hg + h) * cap * D + d0;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) x[h][e] = ld(os + (int64_t)s * D + e);
+      }
+#pragma unroll
+      for (int h = 0; h < HG; ++h) {
+        const float w = wts[(hg + h) * 64 + s];
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) a[h][e][0] = combine_acc(a[h][e][0], w, x[h][e]);
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < HG; ++h)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[(hg + h) * D + d0 + e] = (bf16)combine_tree(a[h][e]);
+  }
+}
+
+// FUSED: the single-token step of a layer in one launch (C == 1): the wave
+// whose split holds the new key's row first appends it (RoPE, K row, V
+// column, slot report); rows with n_new == 0 get one item that writes their
+// padded token to the scratch row and zero outputs; and the last split of a
+// (row, KV head) to finish combines the splits into the output.
+template <int D, int REP, bool FUSED = false, int NBUF = DecodeShape<D, REP>::NBUF,
           int WAVES = DecodeShape<D, REP>::WAVES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
-void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q) {
+void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
+              FusedArgs fa) {
   using S = DecodeShape<D, REP>;
   constexpr int LK = S::LK, KR = S::KR, TK = S::TK, NR = S::NR, NCH = S::NCH, VT = S::VT;
   constexpr int HPL = S::HPL;
@@ -700,13 +853,22 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   find_item(
       st.B, blockIdx.x,
       [&](int r) -> int {
-        if (st.n_new[r] != 1) return 0;
+        const int nr = st.n_new[r];
+        if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
         int64_t base, lo, hi;
         decode_span_dev(la, st.lens[r], &base, &lo, &hi);
         return (int)cdiv(hi - base, SK);
       },
       &b, &split64);
   if (b < 0) return;
+  if constexpr (FUSED) {
+    if (st.n_new[b] == 0) {  // idle row: its padded token and zero outputs
+      decode_append<D>(st, la, fa, b, g, st.lens[b], false, lane);
+      bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
+      for (int e = lane; e < REP * D; e += 64) o[e] = (bf16)0.f;
+      return;
+    }
+  }
   const int split = (int)split64;
   const int h0 = g * REP;
   const int64_t p = st.lens[b];
@@ -714,18 +876,32 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   decode_span_dev(la, p, &base64, &lo64, &hi64);
   // Row indices fit in 32 bits (rows <= max_len < 2^31).
   const int lo = (int)lo64, hi = (int)hi64;
-  // The row's 16-key tiles are shared out evenly over its splits (sizes
-  // differ by at most one tile); SK is a multiple of TK, so the split count
-  // cdiv(hi - base, SK) is also cdiv(tiles, SK / TK) and every split gets a
-  // tile.
+  // The row's 16-key tiles are dealt round-robin to its splits: split s
+  // takes tiles s, s + nsplit, s + 2 nsplit, ... (counts differ by at most
+  // one).  The splits of a row then sweep its K and V regions side by side,
+  // so the waves in flight read from far fewer places in HBM than if each
+  // split streamed its own contiguous run.  SK is a multiple of TK, so the
+  // split count cdiv(hi - base, SK) is also cdiv(tiles, SK / TK) and every
+  // split gets a tile.
   const int ntile = (hi - (int)base64 + TK - 1) / TK;
   const int nsplit = (hi - (int)base64 + SK - 1) / SK;
-  const int tb = split * ntile / nsplit, te = (split + 1) * ntile / nsplit;
   // (uniform values; readfirstlane keeps them in scalar registers, where the
   // tile loads take their offsets)
-  const int t_begin = __builtin_amdgcn_readfirstlane((int)base64 + tb * TK);
-  const int n_iter = __builtin_amdgcn_readfirstlane(te - tb);
+  const int t_begin = __builtin_amdgcn_readfirstlane((int)base64 + split * TK);
+  const int t_stride = __builtin_amdgcn_readfirstlane(nsplit * TK);
+  const int n_iter = __builtin_amdgcn_readfirstlane((ntile - split + nsplit - 1) / nsplit);
   const int64_t bg = (int64_t)b * la.hkv + g;
+  if constexpr (FUSED) {
+    // The new key's storage row (full layout: p; ring: p % W) lies in exactly
+    // one split; that wave writes it before it streams its tiles.
+    const int r_new = la.ring ? (int)(p % la.window) : (int)p;
+    if ((r_new - (int)base64) / TK % nsplit == split)
+      decode_append<D>(st, la, fa, b, g, p, true, lane);
+    // The tile loads below come after these stores in program order (the
+    // barrier keeps the compiler from moving the stores past them), and the
+    // memory pipeline keeps one wave's accesses to one address in order.
+    asm volatile("" ::: "memory");
+  }
 
   // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
   const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
@@ -768,7 +944,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   };
   constexpr int LPT = NR * NCH + VT;  // loads per tile
   auto load = [&](int it, Tile &T) {
-    const int t0 = t_begin + (it < n_iter ? it : n_iter - 1) * TK;
+    const int t0 = t_begin + (it < n_iter ? it : n_iter - 1) * t_stride;
     // K rows and V blocks advance by the same bytes per row
     const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
     static_for<0, NR>([&](auto r) {
@@ -810,7 +986,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   // are masked in the scores; their V is finite (rows past a row's end are
   // zeroed when the append enters a new 32-row tile), so p = 0 cancels them.
   auto step = [&](int it, Tile &T) {
-    const int t0 = t_begin + it * TK;
+    const int t0 = t_begin + it * t_stride;
     const int par = it & 1;
     float a[NR][REP];
 #pragma unroll
@@ -936,13 +1112,45 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
 
   // ---- partials of this split ----
   const int64_t cap = kDecodeSplitCap;
+  float lh[HPL];
+#pragma unroll
+  for (int u = 0; u < HPL; ++u) lh[u] = keys_sum<LK>(lsum[u]);
+  if constexpr (FUSED) {
+    if (nsplit == 1) {
+      // One split: the output is o / l, rounded as the merge rounds a
+      // single split (weight 1 / l times o, then the sum with zeros).
+#pragma unroll
+      for (int h = 0; h < REP; ++h) {
+        int u = 0;
+        const int src = owner_lane<LK, REP>(h, &u);
+        const float l = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lh[u]), src));
+        const float w = 1.f / l;
+        bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + h0 + h) * D;
+#pragma unroll
+        for (int t = 0; t < VT; ++t) {
+          const float x = swap32_sum(acc[h][t]);
+          if (half == 0) o[mm + 32 * t] = (bf16)(combine_acc(0.f, w, x) + 0.f);
+        }
+      }
+      return;
+    }
+  }
+  // Partials (m, l, o) of this split.  The fused kernel writes them with
+  // agent-scope stores (written through to the device's point of coherence,
+  // which every XCD reads).
+  auto put = [&](float *ptr, float val) {
+    if constexpr (FUSED)
+      __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      *ptr = val;
+  };
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
-    const float l = keys_sum<LK>(lsum[u]);
     if (kr == 0 && writer) {
       const int64_t slot = ((int64_t)b * st.Hq + h0 + hbase + u) * cap + split;
-      pa.dml[slot * 2 + 0] = m[u];
-      pa.dml[slot * 2 + 1] = l;
+      put(pa.dml + slot * 2 + 0, m[u]);
+      put(pa.dml + slot * 2 + 1, lh[u]);
     }
   }
 #pragma unroll
@@ -951,8 +1159,28 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       const float o = swap32_sum(acc[h][t]);
-      if (half == 0) pa.dout[slot * D + mm + 32 * t] = o;
+      if (half == 0) put(pa.dout + slot * D + mm + 32 * t, o);
     }
+  }
+  if constexpr (FUSED) {
+    // Count this split's arrival once its partials are complete: the wait
+    // retires every store of the wave (acknowledged at the point of
+    // coherence) before lane 0's agent-scope increment.  The split that reads
+    // nsplit - 1 arrives last; it issues its agent-scope loads of the other
+    // splits' partials only after that read returned, so it sees them all.
+    // This is the order an agent-scope release / acquire pair would give,
+    // without the write-back and invalidation of the whole L2 that such
+    // fences cost on this chip (they would run once per wave).  The counter
+    // goes back to zero for the next launch.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    int prev = 0;
+    if (lane == 0)
+      prev = __hip_atomic_fetch_add(fa.cnt + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    prev = __builtin_amdgcn_readfirstlane(prev);
+    if (prev != nsplit - 1) return;
+    combine_group<D, REP>(pa, st, b, h0, nsplit, qs,
+                          static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + h0) * D, lane);
+    if (lane == 0) __hip_atomic_store(fa.cnt + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -964,7 +1192,17 @@ template <int D, int REP>
 static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                             const void *q, int32_t n_items, const Launch &lc) {
   hipExtLaunchKernelGGL((k_decode<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(64), 0,
-                     (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q);
+                        (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la,
+                        pa, (const bf16 *)q, FusedArgs{});
+}
+
+template <int D, int REP>
+static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                                  const void *q, const FusedArgs &fa, int32_t n_items,
+                                  const Launch &lc) {
+  hipExtLaunchKernelGGL((k_decode<D, REP, true>), dim3((unsigned)n_items, (unsigned)la.hkv),
+                        dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0,
+                        (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q, fa);
 }
 
 template <int D, int REP>
@@ -982,6 +1220,20 @@ int decode_waves_per_cu(int D, int rep) {
   KVC_OCC(64, 1) KVC_OCC(64, 2) KVC_OCC(64, 4) KVC_OCC(64, 8) KVC_OCC(64, 16)
 #undef KVC_OCC
   return 0;
+}
+
+int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                        const void *q, const FusedArgs &fa, int32_t n_items, const Launch &lc) {
+  if (st.C != 1) return (int)hipErrorInvalidValue;
+#define KVC_DEC(DD, RR)                                                  \
+  if (st.D == DD && la.rep == RR) {                                      \
+    launch_decode_fused_t<DD, RR>(st, la, pa, q, fa, n_items, lc);       \
+    return (int)hipGetLastError();                                       \
+  }
+  KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8) KVC_DEC(128, 16)
+  KVC_DEC(64, 1) KVC_DEC(64, 2) KVC_DEC(64, 4) KVC_DEC(64, 8) KVC_DEC(64, 16)
+#undef KVC_DEC
+  return (int)hipErrorInvalidValue;
 }
 
 int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,
@@ -1362,15 +1614,15 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
       for (int u = 0; u < 8; ++u) {
         const float w = wts[s + u];
         const float x = os[(int64_t)(s + u) * D + d];
-        a[u] += w != 0.f ? w * x : 0.f;  // splits without keys: slot never written
+        a[u] = combine_acc(a[u], w, x);  // splits without keys: slot never written
       }
     }
     for (; s < ns; ++s) {
       const float w = wts[s];
       const float x = os[(int64_t)s * D + d];
-      a[0] += w != 0.f ? w * x : 0.f;
+      a[0] = combine_acc(a[0], w, x);
     }
-    o[d] = from_f<T>(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
+    o[d] = from_f<T>(combine_tree(a));
   }
 }
 

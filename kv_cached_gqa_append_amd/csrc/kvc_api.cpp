@@ -43,6 +43,7 @@ struct kvc_cache {
   int32_t dec_split_fixed = 0;    // keys per split (multiple of 16); 0 = planned
   int32_t dec_waves_target = 0;   // waves per decode launch; 0 = resident slots
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
+  bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
   // kernel timing
   bool timing = false;
   std::vector<hipEvent_t> ev;      // 2 per launch
@@ -118,8 +119,9 @@ void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi
 // wave count, summed over the decoding rows and KV heads, fits the waves the
 // chip holds at once.  A partial second round or a few long waves would leave
 // most of the chip idle at the end of the launch.  Each row keeps at most
-// kDecodeSplitCap splits.
-int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
+// kDecodeSplitCap splits.  `extra` waves of the same launch (the idle-row
+// items of the single-kernel step) take slots too.
+int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D, int64_t extra = 0) {
   const int TK = kvc::kDecodeTile;
   std::vector<int64_t> tiles;
   int64_t max_t = 0;
@@ -141,6 +143,7 @@ int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
     if (occ == 0) occ = std::max(1, kvc::decode_waves_per_cu(D, la.rep));
     target = (int64_t)h->n_cu * occ;
   }
+  target = std::max<int64_t>(1, target - extra);
   auto waves = [&](int64_t q) {
     int64_t w = 0;
     for (int64_t t : tiles) w += (t + q - 1) / q;
@@ -254,8 +257,11 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
       return KVC_E_HIP;
     }
   }
+  // Row lengths, n_new and the fused decode's split-arrival counters start
+  // at zero (the counters return to zero at the end of every fused launch).
   if (hipMemsetAsync(h->base + h->lay.lens_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.nnew_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
+      hipMemsetAsync(h->base + h->lay.cnt_off, 0, h->lay.cnt_bytes, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {
     delete h;
     return KVC_E_HIP;
@@ -276,6 +282,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     const long v = std::strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 24)) h->dec_waves_target = (int32_t)v;
   }
+  if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_LOG")) {
     h->log_level = std::atoi(e);
     if (h->log_level >= 1)
@@ -307,9 +314,12 @@ int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream) 
   return KVC_OK;
 }
 
-int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
-               const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *stream) {
-  if (!h || !k || !v || !n_new_host) return KVC_E_ARG;
+namespace {
+
+// The checks of an append (argument ranges, capacity on the step's first
+// append, the same n_new and C on every other one, one append per layer) and,
+// on the step's first append, latching n_new and C and uploading n_new.
+int begin_append(kvc_t *h, int32_t layer, const int32_t *n_new_host, int32_t C, void *stream) {
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   if (C < 1 || C > h->cfg.max_chunk) return KVC_E_ARG;
   const int32_t B = h->cfg.batch;
@@ -334,6 +344,26 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
     std::fill(h->appended.begin(), h->appended.end(), 0);
     std::fill(h->attended.begin(), h->attended.end(), 0);
   }
+  return KVC_OK;
+}
+
+kvc::PartialArgs partial_args(const kvc_t *h) {
+  kvc::PartialArgs pa{};
+  pa.dml = reinterpret_cast<float *>(h->base + h->lay.dml_off);
+  pa.dout = reinterpret_cast<float *>(h->base + h->lay.dout_off);
+  pa.pml = h->lay.pml_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pml_off) : nullptr;
+  pa.pout = h->lay.pout_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pout_off) : nullptr;
+  pa.max_chunk = h->cfg.max_chunk;
+  return pa;
+}
+
+}  // namespace
+
+int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
+               const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *stream) {
+  if (!h || !k || !v || !n_new_host) return KVC_E_ARG;
+  const int rc = begin_append(h, layer, n_new_host, C, stream);
+  if (rc != KVC_OK) return rc;
   const kvc::StepArgs st = step_args(h);
   const kvc::LayerArgs la = layer_args(h, layer);
   int err = kvc::launch_append(h->cfg.dtype, st, la, k, v, slot_out_dev, launch_on(h, KVC_K_APPEND, stream));
@@ -371,12 +401,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
         max_chunk_span = std::max(max_chunk_span, hi - base);
       }
     }
-    kvc::PartialArgs pa{};
-    pa.dml = reinterpret_cast<float *>(h->base + h->lay.dml_off);
-    pa.dout = reinterpret_cast<float *>(h->base + h->lay.dout_off);
-    pa.pml = h->lay.pml_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pml_off) : nullptr;
-    pa.pout = h->lay.pout_off >= 0 ? reinterpret_cast<float *>(h->base + h->lay.pout_off) : nullptr;
-    pa.max_chunk = h->cfg.max_chunk;
+    kvc::PartialArgs pa = partial_args(h);
     pa.dec_split_keys = decode_split_keys(h, la, D);
     pa.pre_split_keys = (int32_t)std::max<int64_t>(
         kChunkSplitMin, round_up(ceil_div(max_chunk_span, kvc::kChunkSplitCap), kvc::kRowAlign));
@@ -415,6 +440,54 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
     err = kvc::launch_commit(h->cfg.dtype, st, la, launch_on(h, KVC_K_COMMIT, stream));
     if (err) return KVC_E_HIP;
   }
+  h->attended[layer] = 1;
+  return KVC_OK;
+}
+
+int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, const void *v,
+                      const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *out,
+                      void *stream) {
+  if (!h || !q || !k || !v || !out || !n_new_host) return KVC_E_ARG;
+  if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
+  const kvc::LayerArgs la = layer_args(h, layer);
+  const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
+  const bool fused = C == 1 && !h->no_fused && h->cfg.dtype == KVC_BF16 &&
+                     kvc::fast_decode_supported(D, la.rep);
+  if (!fused) {
+    const int rc = kvc_append(h, layer, k, v, n_new_host, C, slot_out_dev, stream);
+    if (rc != KVC_OK) return rc;
+    return kvc_attend(h, layer, q, out, stream);
+  }
+  const int rc = begin_append(h, layer, n_new_host, C, stream);
+  if (rc != KVC_OK) return rc;
+  const kvc::StepArgs st = step_args(h);
+  kvc::PartialArgs pa = partial_args(h);
+  int64_t idle = 0;
+  for (int32_t b = 0; b < B; ++b) idle += h->n_new[b] == 0;
+  pa.dec_split_keys = decode_split_keys(h, la, D, idle * la.hkv);
+  int64_t items = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (h->n_new[b] == 1) {
+      int64_t base, hi;
+      decode_span(la, h->lens_host[b], &base, &hi);
+      items += ceil_div(hi - base, pa.dec_split_keys);
+    } else {
+      items += 1;  // idle row: its padded token and zero outputs
+    }
+  }
+  if (h->log_level >= 2 && layer == 0)
+    std::fprintf(stderr, "[kvc] fused decode plan: %d keys per split, %lld waves\n",
+                 pa.dec_split_keys, (long long)items * la.hkv);
+  kvc::FusedArgs fa;
+  fa.k = k;
+  fa.v = v;
+  fa.slot_out = slot_out_dev;
+  fa.out = out;
+  fa.cnt = reinterpret_cast<int32_t *>(h->base + h->lay.cnt_off);
+  if (kvc::launch_decode_fused(st, la, pa, q, fa, (int32_t)items,
+                               launch_on(h, KVC_K_FUSED, stream)))
+    return KVC_E_HIP;
+  h->appended[layer] = 1;
   h->attended[layer] = 1;
   return KVC_OK;
 }

@@ -42,6 +42,8 @@ struct Layout {
   int64_t nnew_off = 0;       // int32 [B]
   int64_t dml_off = 0;        // float2 (m, l) [B][Hq][kDecodeSplitCap]
   int64_t dout_off = 0;       // float [B][Hq][kDecodeSplitCap][D]
+  int64_t cnt_off = 0;        // int32 [B][max Hkv]: split arrivals (fused decode), 0 between launches
+  int64_t cnt_bytes = 0;
   int64_t pml_off = -1;       // float2 [B][max_chunk][Hq][kChunkSplitCap]
   int64_t pout_off = -1;      // float [B][max_chunk][Hq][kChunkSplitCap][D]
   int64_t total = 0;
@@ -76,6 +78,16 @@ struct PartialArgs {
   int32_t pre_split_keys; // keys per chunk split (multiple of 32)
 };
 
+// The single-token step of one layer in one launch (append, decode, combine):
+// the new token's K (pre-RoPE) and V, the slot report, the output and the
+// per-(row, KV head) split arrival counters (zero between launches).
+struct FusedArgs {
+  const void *k = nullptr, *v = nullptr;  // (B, 1, Hkv, D)
+  int32_t *slot_out = nullptr;            // (B, 1) or null
+  void *out = nullptr;                    // (B, 1, Hq, D)
+  int32_t *cnt = nullptr;                 // [B][Hkv]
+};
+
 // Where a launch goes: the caller's stream and, when kernel timing is on, a
 // pair of events the dispatch itself stamps at its start and end.
 struct Launch {
@@ -92,6 +104,11 @@ int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void
 int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc);
 int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                   const void *q, int32_t n_items, const Launch &lc);
+// Rows with n_new in {0, 1}, C == 1: RoPE + append, decode attention and the
+// split combine in one launch; n_items counts decode splits plus one item per
+// idle row.
+int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                        const void *q, const FusedArgs &fa, int32_t n_items, const Launch &lc);
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                    const void *q, int32_t n_items, const Launch &lc);
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,

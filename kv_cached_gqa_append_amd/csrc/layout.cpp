@@ -97,6 +97,9 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
   const int64_t dq = B * Hq * kDecodeSplitCap;
   if (!take(&cur, dq * 8, &lay->dml_off) || !take(&cur, dq * D * 4, &lay->dout_off))
     return KVC_E_ARG;
+  // One counter per (row, KV head); Hq bounds every layer's Hkv.
+  lay->cnt_bytes = B * Hq * 4;
+  if (!take(&cur, lay->cnt_bytes, &lay->cnt_off)) return KVC_E_ARG;
   if (cfg->max_chunk >= 2) {
     const int64_t pq = B * (int64_t)cfg->max_chunk * Hq * kChunkSplitCap;
     if (!take(&cur, pq * 8, &lay->pml_off) || !take(&cur, pq * D * 4, &lay->pout_off))

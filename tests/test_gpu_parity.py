@@ -157,3 +157,103 @@ def test_guards_and_step_order():
     c.advance()
     assert c.lens() == [10, 5]
     torch.cuda.synchronize()
+
+
+# -- the single-kernel one-token step (kvc_append_attend) ------------------------
+def _same_cache(a, b, layer):
+    # Raw bits of the cache rows proper (rows never written hold the NaN
+    # poison in both).  The scratch row is left out: the padded tokens of a
+    # chunk all land there in one append, in no fixed order.
+    rows = a.cache.layer_layout(layer).rows
+    ka = a.cache.k_view(layer)[:, :, :rows].view(torch.int16)
+    kb = b.cache.k_view(layer)[:, :, :rows].view(torch.int16)
+    va = a.cache.v_view(layer)[:, :, :rows].view(torch.int16)
+    vb = b.cache.v_view(layer)[:, :, :rows].view(torch.int16)
+    assert torch.equal(ka, kb), f"layer {layer}: K differs"
+    assert torch.equal(va, vb), f"layer {layer}: V differs"
+
+
+def _fused_vs_two_calls(work, prompts, decode_steps, tag):
+    """Drive two caches with the same inputs, one through append_attend and
+    one through append + attend; both meet the oracle bar, and the one-token
+    steps agree bit for bit (same stores, same arithmetic in the same order)."""
+    a = Pair(work, poison=True, tag=tag)
+    b = Pair(work, poison=True, tag=tag)
+    for n, C in prompts:
+        a.step(n, C, fused=True)
+        b.step(n, C)
+    for n in decode_steps:
+        oa = a.step(n, 1, fused=True)
+        ob = b.step(n, 1)
+        for l, (x, y) in enumerate(zip(oa, ob)):
+            assert torch.equal(x, y), f"layer {l}: fused output differs from append + attend"
+    for l in range(work.n_layer):
+        _same_cache(a, b, l)
+        a.check_cache_rows(l)
+    say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
+
+
+def test_fused_decode_rings_and_idle_rows():
+    say("case: fused one-token steps, ring_bf16 (rings W=8 + global), idle rows")
+    work = wl.RING_BF16
+    prompts = [(np.array([12, 3, 9, 0]), 12)]
+    steps = [np.array([1, 1, 1, 1]), np.array([1, 0, 1, 1]), np.array([0, 1, 1, 0])]
+    steps += [wl.n_new_decode_b64(s, batch=4, idle=1) for s in range(20)]
+    _fused_vs_two_calls(work, prompts, steps, "fused_ring")
+
+
+def test_fused_decode_many_splits():
+    say("case: fused one-token steps with many key splits, D128 rep4, W=700 window mask")
+    work = wl.Workload("fused_splits", 2, 6, 32, (8, 8), 128, 3200, (0, 700), "bf16", 64,
+                       use_ring=False)
+    a = Pair(work, poison=True, tag="fs")
+    b = Pair(work, poison=True, tag="fs")
+    for n, C in wl.fill_plan([2900, 17, 1024, 1025, 256, 3100], 64):
+        a.step(n, C, check=False)
+        b.step(n, C, check=False)
+    for s in range(4):
+        n = wl.n_new_decode_b64(s, batch=6, idle=1)
+        oa = a.step(n, 1, fused=True)
+        ob = b.step(n, 1)
+        for l, (x, y) in enumerate(zip(oa, ob)):
+            assert torch.equal(x, y), f"step {s} layer {l}: fused output differs"
+    for l in range(work.n_layer):
+        _same_cache(a, b, l)
+    say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
+
+
+@pytest.mark.parametrize("D,rep", [(64, 1), (64, 16), (128, 2), (128, 8), (128, 16)])
+def test_fused_head_shapes(D, rep):
+    say(f"case: fused head shapes D={D} rep={rep}")
+    hkv = 2
+    work = wl.Workload(f"fshape_{D}_{rep}", 1, 3, hkv * rep, (hkv,), D, 400, (0,), "bf16", 40)
+    _fused_vs_two_calls(work, wl.fill_plan([300, 40, 5], 40),
+                        [np.array([1, 1, 1]), np.array([1, 0, 1])], f"fs{D}_{rep}")
+
+
+def test_fused_guards():
+    say("case: fused entry point keeps the step protocol")
+    work = wl.Workload("fguards", 2, 2, 8, (2, 2), 64, 20, (0, 4), "bf16", 16)
+    pair = Pair(work)
+    pair.step([8, 3], 8)
+    c, dev = pair.cache, pair.device
+    q, k, v = (t.to(dev) for t in wl.step_qkv(work, 0, 99, 1))
+    c.append_attend(0, q, k, v, [1, 1])
+    with pytest.raises(K.StepOrderError):
+        c.append_attend(0, q, k, v, [1, 1])                # same layer twice
+    with pytest.raises(K.StepOrderError):
+        c.append_attend(1, q, k, v, [1, 0])                # different n_new in a step
+    with pytest.raises(K.StepOrderError):
+        c.attend(0, q)                                     # already attended
+    c.append_attend(1, q, k, v, [1, 1])
+    c.advance()
+    assert c.lens() == [9, 4]
+    big = torch.zeros(2, 1, 2, 64, dtype=torch.bfloat16, device=dev)
+    for _ in range(11):
+        c.append_attend(0, q, big, big, [1, 0])
+        c.append_attend(1, q, big, big, [1, 0])
+        c.advance()
+    with pytest.raises(K.CacheFullError):
+        c.append_attend(0, q, big, big, [1, 0])            # row 0 at 20 = max_len
+    assert c.lens() == [20, 4]
+    torch.cuda.synchronize()
