@@ -935,6 +935,11 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const int64_t region = (int64_t)la.rows_alloc * D * 2;  // bytes per (b, g)
   const i32x4 rk = sgpr_rsrc(la.k + bg * region, (int)region);
   const i32x4 rv = sgpr_rsrc(la.v + bg * region, (int)region);
+  // Loads past a split's last tile (the ring keeps its loads in flight in
+  // whole groups) go through descriptors of zero records: every lane is out
+  // of range, so they return zeros without a memory access.
+  const i32x4 rk_none = sgpr_rsrc(la.k + bg * region, 0);
+  const i32x4 rv_none = sgpr_rsrc(la.v + bg * region, 0);
   const int koff = (kr * D + j * 8) * 2;
   const int voff = (mm * kVBlock + half * 8) * 2;
 
@@ -944,17 +949,19 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   };
   constexpr int LPT = NR * NCH + VT;  // loads per tile
   auto load = [&](int it, Tile &T) {
-    const int t0 = t_begin + (it < n_iter ? it : n_iter - 1) * t_stride;
+    const bool live = it < n_iter;
+    const int t0 = t_begin + (live ? it : 0) * t_stride;
+    const i32x4 ka = live ? rk : rk_none, va = live ? rv : rv_none;
     // K rows and V blocks advance by the same bytes per row
     const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
     static_for<0, NR>([&](auto r) {
       static_for<0, NCH>([&](auto t) {
         constexpr int off = decltype(r)::value * KR * D * 2 + decltype(t)::value * LK * 16;
-        tile_load<off>(T.k[decltype(r)::value][decltype(t)::value], rk, koff, so);
+        tile_load<off>(T.k[decltype(r)::value][decltype(t)::value], ka, koff, so);
       });
     });
     static_for<0, VT>([&](auto t) {
-      tile_load<decltype(t)::value * 32 * kVBlock * 2>(T.v[decltype(t)::value], rv, voff, so);
+      tile_load<decltype(t)::value * 32 * kVBlock * 2>(T.v[decltype(t)::value], va, voff, so);
     });
   };
   // Wait for tile T when AFTER tiles were issued after it.
@@ -1082,11 +1089,9 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   }
 
   // Ring of NBUF register tiles; NBUF - 1 tiles are in flight while one
-  // computes.  Unrolled by NBUF so buffer indices are compile-time.
-  // Ring of NBUF register tiles; NBUF - 1 tiles are in flight while one
   // computes.  Unrolled by NBUF so buffer indices are compile-time.  Loads
-  // and waits run for whole groups (loads past the end re-read the last tile,
-  // which the L2 holds) and only the compute is skipped past the end, so the
+  // and waits run for whole groups (loads past the end read nothing and
+  // return zeros) and only the compute is skipped past the end, so the
   // loop has one back edge and always the same loads in flight.
   Tile T[NBUF];
 #pragma unroll

@@ -119,13 +119,15 @@ void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi
 // wave count, summed over the decoding rows and KV heads, fits the waves the
 // chip holds at once.  A partial second round or a few long waves would leave
 // most of the chip idle at the end of the launch.  Each row keeps at most
-// kDecodeSplitCap splits.  `extra` waves of the same launch (the idle-row
-// items of the single-kernel step) take slots too.
-int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D, int64_t extra = 0) {
+// kDecodeSplitCap splits.  The idle rows' items of the single-kernel step
+// take slots too; both entry points plan with them counted, so a step splits
+// its rows the same way (and produces the same bits) through either.
+int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
   const int TK = kvc::kDecodeTile;
   std::vector<int64_t> tiles;
-  int64_t max_t = 0;
+  int64_t max_t = 0, extra = 0;
   for (int32_t b = 0; b < h->cfg.batch; ++b) {
+    extra += h->n_new[b] == 0 ? la.hkv : 0;
     if (h->n_new[b] != 1) continue;
     int64_t base, hi;
     decode_span(la, h->lens_host[b], &base, &hi);
@@ -462,9 +464,7 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   if (rc != KVC_OK) return rc;
   const kvc::StepArgs st = step_args(h);
   kvc::PartialArgs pa = partial_args(h);
-  int64_t idle = 0;
-  for (int32_t b = 0; b < B; ++b) idle += h->n_new[b] == 0;
-  pa.dec_split_keys = decode_split_keys(h, la, D, idle * la.hkv);
+  pa.dec_split_keys = decode_split_keys(h, la, D);
   int64_t items = 0;
   for (int32_t b = 0; b < B; ++b) {
     if (h->n_new[b] == 1) {

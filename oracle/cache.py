@@ -154,6 +154,23 @@ class OracleCache:
             out[b, :n] = _attn.attend_rows(qrot, krot, self.hist_v[layer][b], blocked)
         return out if compute else None
 
+    def query_rows(self, layer: int, b: int, n: int, q_b, idx) -> np.ndarray:
+        """Outputs of the queries ``idx`` (a subset of 0..n-1) of row b, whose
+        n new tokens were appended to layer ``layer`` in the current step
+        (``layer_step``, lens not yet advanced).  q_b: (n, Hq, D) raw queries
+        of the row.  The same definition as ``layer_step`` restricted to these
+        queries, for checking a few outputs of workloads too large to attend
+        in full.  Returns (len(idx), Hq, D) float64."""
+        idx = np.asarray(idx, dtype=np.int64)
+        q_b = np.asarray(q_b, dtype=np.float64)
+        T = int(self.lens[b]) + int(n)
+        if self.hist_k[layer][b].shape[0] != T:
+            raise ValueError("append this step's tokens (layer_step) before querying")
+        krot = _rope.rotate(self.hist_k[layer][b], np.arange(T), self.rope_base)
+        qrot = _rope.rotate(q_b[idx], self._query_positions(b, n)[idx], self.rope_base)
+        blocked = self._blocked(layer, b, n)[idx]
+        return _attn.attend_rows(qrot, krot, self.hist_v[layer][b], blocked)
+
     def advance(self, n_new) -> None:
         self.lens = self.lens + np.asarray(n_new, dtype=np.int64)
 

@@ -145,3 +145,87 @@ class Pair:
                 bad = (got_k < lo_b) | (got_k > hi_b)
                 assert not bad.any(), (f"layer {layer} row {b}: K is not the dtype rounding of "
                                        f"its rotation ({int(bad.sum())} elements)")
+
+
+class SampledOracle:
+    """The oracle on a few rows of a workload too large to check in full.
+
+    It keeps the raw history of the sampled rows only.  Tokens appended on
+    the GPU are recorded as they go and handed to the oracle in one step when
+    a check needs them (the oracle is chunk-invariant: pinned by the
+    chunked-equals-single check).  ``check`` compares chosen queries of the
+    current step against ``OracleCache.query_rows``.
+    """
+
+    def __init__(self, work, rows):
+        self.work = work
+        self.rows = [int(r) for r in rows]
+        self.ref = oracle.OracleCache(len(self.rows), work.n_q_head, work.n_kv_head,
+                                      work.head_dim, work.max_len, work.window, work.rope_base)
+        self.pending = [[[] for _ in self.rows] for _ in range(work.n_layer)]
+
+    def record(self, layer, k, v, n_new):
+        """Remember the valid tokens of the sampled rows (k, v on the GPU)."""
+        for j, b in enumerate(self.rows):
+            n = int(n_new[b])
+            if n:
+                self.pending[layer][j].append((f64(k[b, :n]), f64(v[b, :n])))
+
+    def catch_up(self):
+        """Append every recorded token to the oracle in one step."""
+        w = self.work
+        counts = [sum(x[0].shape[0] for x in self.pending[0][j]) for j in range(len(self.rows))]
+        for l in range(w.n_layer):
+            assert [sum(x[0].shape[0] for x in self.pending[l][j])
+                    for j in range(len(self.rows))] == counts
+        C = max(counts)
+        if C == 0:
+            return
+        layers = []
+        for l in range(w.n_layer):
+            hk = w.n_kv_head[l]
+            K = np.zeros((len(self.rows), C, hk, w.head_dim))
+            V = np.zeros_like(K)
+            for j in range(len(self.rows)):
+                if counts[j]:
+                    K[j, :counts[j]] = np.concatenate([x[0] for x in self.pending[l][j]])
+                    V[j, :counts[j]] = np.concatenate([x[1] for x in self.pending[l][j]])
+            q = np.broadcast_to(np.float64(0.0), (len(self.rows), C, w.n_q_head, w.head_dim))
+            layers.append((q, K, V))
+        self.ref.step(np.asarray(counts), layers, compute=False)
+        self.pending = [[[] for _ in self.rows] for _ in range(w.n_layer)]
+
+    def check_step(self, n_new, qkv, outs, queries, what):
+        """The current step on the sampled rows: append its tokens to the
+        oracle, compare outputs of ``queries(b, n) -> indices`` for every
+        sampled row and layer, then advance.  qkv[l] = (q, k, v) on the GPU;
+        outs[l] the GPU outputs.  Returns (max abs, max rel l2)."""
+        w = self.work
+        self.catch_up()
+        nn = np.array([int(n_new[b]) for b in self.rows])
+        worst, worst_rel = 0.0, 0.0
+        for l in range(w.n_layer):
+            q, k, v = qkv[l]
+            C = q.shape[1]
+            sel = torch.tensor(self.rows, device=q.device)
+            ks, vs = f64(k[sel]), f64(v[sel])
+            qz = np.broadcast_to(np.float64(0.0), (len(self.rows), C, w.n_q_head, w.head_dim))
+            self.ref.layer_step(l, nn, qz, ks, vs, compute=False)
+            got_all = f64(outs[l][sel])
+            for j, b in enumerate(self.rows):
+                n = int(nn[j])
+                if n == 0:
+                    assert np.all(got_all[j] == 0.0), f"{what}: idle row {b} layer {l} not zero"
+                    continue
+                idx = np.asarray(queries(b, n), dtype=np.int64)
+                exp = self.ref.query_rows(l, j, n, f64(q[b, :n]), idx)
+                got = got_all[j, idx]
+                d = np.abs(got - exp)
+                mx = float(d.max())
+                rel = float(np.linalg.norm(got - exp) / max(np.linalg.norm(exp), 1e-300))
+                assert mx <= BF16_MAX_ABS, f"{what}: row {b} layer {l} max abs {mx:.3e}"
+                assert rel <= BF16_REL_L2, f"{what}: row {b} layer {l} rel l2 {rel:.3e}"
+                assert np.all(got_all[j, n:] == 0.0), f"{what}: row {b} padded outputs not zero"
+                worst, worst_rel = max(worst, mx), max(worst_rel, rel)
+        self.ref.advance(nn)
+        return worst, worst_rel

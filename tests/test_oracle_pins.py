@@ -507,3 +507,24 @@ def test_reset_empties_rows():
     oc.step(np.array([4, 4]), [(_f64(q), _f64(k), _f64(v))])
     oc.reset([1])
     assert list(oc.lens) == [4, 0] and oc.hist_k[0][1].shape[0] == 0
+
+
+def test_query_rows_is_layer_step_restricted():
+    # Sampled queries of a step (used to check outputs of large workloads)
+    # equal the full step's outputs for those queries, bit for bit, on a
+    # global and a sliding layer, after an uneven history built in one go.
+    work = wl.Workload("pin_qrows", 2, 3, 8, (2, 4), 16, 60, (0, 5), "f32", 16)
+    full, part = _oracle_for(work), _oracle_for(work)
+    n0 = np.array([13, 0, 7])
+    layers = [tuple(_f64(t) for t in wl.step_qkv(work, l, 0, 13)) for l in range(2)]
+    full.step(n0, layers, compute=False)
+    part.step(n0, layers, compute=False)
+    n1 = np.array([9, 3, 1])
+    layers = [tuple(_f64(t) for t in wl.step_qkv(work, l, 1, 9)) for l in range(2)]
+    for l in range(2):
+        exp = full.layer_step(l, n1, *layers[l])
+        part.layer_step(l, n1, *layers[l], compute=False)
+        for b in range(3):
+            idx = np.arange(int(n1[b]))[::2]
+            got = part.query_rows(l, b, int(n1[b]), layers[l][0][b], idx)
+            assert np.array_equal(got, exp[b, idx])

@@ -119,6 +119,27 @@ def row_qkv(wl: Workload, layer: int, step: int, row: int, C: int, tag: str = ""
     return q, k, v
 
 
+def device_normal(shape, dtype, device, *key) -> torch.Tensor:
+    """N(0,1) draw for ``key`` made on ``device`` by a seeded torch generator
+    there (float32, rounded to ``dtype``): for histories too large to draw on
+    the CPU.  The values differ from ``normal``'s for the same key; a checker
+    copies the rows it needs back to the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed_of("device", *key))
+    return torch.randn(*shape, generator=g, dtype=torch.float32, device=device).to(dtype)
+
+
+def device_step_qkv(wl: Workload, layer: int, step: int, C: int, device, tag: str = ""):
+    """q (B, C, Hq, D), k, v (B, C, Hkv_l, D) drawn on ``device``."""
+    B, D = wl.batch, wl.head_dim
+    hq, hkv = wl.n_q_head, wl.n_kv_head[layer]
+    dt = wl.torch_dtype
+    q = device_normal((B, C, hq, D), dt, device, wl.name, tag, layer, step, "q")
+    k = device_normal((B, C, hkv, D), dt, device, wl.name, tag, layer, step, "k")
+    v = device_normal((B, C, hkv, D), dt, device, wl.name, tag, layer, step, "v")
+    return q, k, v
+
+
 def rng(*key) -> np.random.Generator:
     return np.random.default_rng(seed_of(*key))
 
