@@ -131,10 +131,16 @@ def summarize_trace(trace_csv, steps, warmup, layers, fused=False):
     names = [_kname(r["Kernel_Name"]) for r in rows]
     work = workload_for(layers)
     dec = [i for i, n in enumerate(names) if n == "k_decode"]
+    # the timed steps' decode launches are the last steps * n_layer (the
+    # prefill leg after them launches none); the region ends at the last
+    # timed step's advance
     first = dec[-steps * work.n_layer]
     while names[first] != "k_set_rows":            # the step's n_new upload
         first -= 1
-    sel = rows[first:]
+    last = dec[-1]
+    while names[last] != "k_advance":              # the last timed step's advance
+        last += 1
+    sel = rows[first:last + 1]
     t0, t1 = int(sel[0]["Start_Timestamp"]), int(sel[-1]["End_Timestamp"])
     by = {}
     for r in sel:
@@ -192,6 +198,42 @@ def summarize_counters(fetch_csv, write_csv, steps, warmup, layers, fused=False)
     return "\n".join(out)
 
 
+def summarize_mfma(csv_path, chunks, chunk=64):
+    """Markdown summary of a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+    GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 run of --prefill-only: MFMA
+    busy fraction of the chunk-attention dispatches (busy cycles summed over
+    the SIMDs / (active cycles x SIMDs)) and the bf16 MFMA flops they issued
+    (MOPS x 512) against the algorithmic flops.  The trace reports
+    GRBM_GUI_ACTIVE summed over the 8 XCDs' counters; active cycles are that
+    sum / 8."""
+    simds, xcds = 256 * 4, 8
+    per = {}
+    for r in csv.DictReader(open(csv_path)):
+        if "k_chunk" not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    ids = sorted(per)
+    busy = np.array([per[i]["SQ_VALU_MFMA_BUSY_CYCLES"] for i in ids])
+    gui = np.array([per[i]["GRBM_GUI_ACTIVE"] for i in ids]) / xcds
+    mops = np.array([per[i]["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for i in ids])
+    util = busy / (gui * simds)
+    work = wl.LONG_5TO1.replace(n_layer=1, n_kv_head=(8,), window=(0,))
+    alg = prefill_flops(work, chunks * chunk)
+    out = [f"k_chunk dispatches: {len(ids)}", "",
+           "| dispatches | MFMA busy (mean) | MFMA busy (cycle-weighted) | bf16 MFMA flops issued | "
+           "algorithmic flops | issued / algorithmic |", "|---|---|---|---|---|---|",
+           f"| {len(ids)} | {util.mean():.4f} | {busy.sum() / (gui.sum() * simds):.4f} | "
+           f"{mops.sum() * 512:.4e} | {alg:.4e} | {mops.sum() * 512 / alg:.3f} |", "",
+           "| chunk index | active cycles | MFMA busy | issued TFLOP/s |", "|---|---|---|---|"]
+    for i in list(range(0, len(ids), max(1, len(ids) // 10))) + [len(ids) - 1]:
+        d = per[ids[i]]
+        out.append(f"| {i} | {gui[i]:.0f} | {util[i]:.4f} | "
+                   f"{mops[i] * 512 / (d['ns'] * 1e-9) / 1e12:.1f} |")
+    return "\n".join(out)
+
+
 def counter_traffic(bytes_per_launch, fused):
     """HBM traffic per decode launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
@@ -231,6 +273,57 @@ def fill_history(cache, work, target, dev):
             log(f"[bench] fill step {si + 1}/{len(plan)} ({time.perf_counter() - t0:.1f}s)")
     torch.cuda.synchronize()
     log(f"[bench] history filled: {len(plan)} chunk steps in {time.perf_counter() - t0:.1f}s")
+
+
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def prefill_flops(work, n_tokens):
+    """Algorithmic FLOPs of attending a B-row prefill of n_tokens tokens on
+    one global layer: query at position p sees p + 1 keys; 4 * D flops per
+    (query head, key) for QK^T and PV."""
+    return 4.0 * work.head_dim * work.n_q_head * work.batch * n_tokens * (n_tokens + 1) / 2
+
+
+def prefill_leg(dev, chunks, chunk=64):
+    """Chunked prefill of one global layer of the long-context workload (B 8,
+    Hq 64 / Hkv 8, D 128, bf16) to chunks * 64 tokens through the protocol,
+    timing every chunk-attention launch: the MFMA-bound part of that
+    workload's prefill."""
+    work = wl.LONG_5TO1.replace(n_layer=1, n_kv_head=(8,), window=(0,))
+    cache = K.Cache(K.config_from_workload(work), dev)
+    B, D = work.batch, work.head_dim
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "prefill"))
+    q = torch.randn(B, chunk, work.n_q_head, D, generator=g, device=dev).to(work.torch_dtype)
+    k = torch.randn(B, chunk, 8, D, generator=g, device=dev).to(work.torch_dtype)
+    v = torch.randn(B, chunk, 8, D, generator=g, device=dev).to(work.torch_dtype)
+    out = torch.empty_like(q)
+    n = np.full(B, chunk)
+    K.kvc_timing_begin(cache.handle, chunks * 4 + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(chunks):
+        cache.append(0, k, v, n)
+        cache.attend(0, q, out)
+        cache.advance()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kt = K.kvc_timing_end(cache.handle)
+    ms, launches = kt["chunk"]
+    flops = prefill_flops(work, chunks * chunk)
+    tflops = flops / (ms / 1e3) / 1e12
+    log(f"[bench] prefill: {chunks} chunks of {chunk} to {chunks * chunk} tokens, chunk kernel "
+        f"{ms:.1f} ms ({tflops:.0f} TFLOP/s), wall {dt * 1e3:.1f} ms")
+    cache.close()
+    return {"workload": f"long_5to1 global layer: B{B}, Hq{work.n_q_head}/Hkv8, D{D}, bf16, "
+                        f"{chunks} chunks of {chunk} to {chunks * chunk} tokens",
+            "kernel": "k_chunk<128,8>", "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(tflops, 1), "peak": PEAK_BF16_TFLOPS,
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "flops": flops,
+            "chunk_kernel_ms": round(ms, 3), "launches": launches,
+            "wall_ms": round(dt * 1e3, 3),
+            "tokens_per_s": round(B * chunks * chunk / dt, 1)}
 
 
 def cpu_baseline(work, lens_all, seconds):
@@ -289,12 +382,19 @@ def main():
     ap.add_argument("--steps", type=int, default=56)
     ap.add_argument("--warmup", type=int, default=4)
     ap.add_argument("--cpu-baseline-seconds", type=float, default=15.0)
+    ap.add_argument("--prefill-chunks", type=int, default=510,
+                    help="chunks of the prefill leg (0 skips it)")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="run only the prefill leg (counter runs) and print its object")
     ap.add_argument("--two-calls", action="store_true",
                     help="kvc_append + kvc_attend per layer instead of kvc_append_attend")
     ap.add_argument("--layers", type=int, default=0,
                     help="fewer layers (counter runs: per-launch work is unchanged)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy, the reference for HBM counters")
+    ap.add_argument("--summarize-mfma", metavar="COUNTER_CSV",
+                    help="print the MFMA summary of a rocprofv3 --pmc run of --prefill-only "
+                         "(same --prefill-chunks) and exit")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="print the timed-region summary of a rocprofv3 kernel trace of this "
                          "bench (same --steps / --warmup / --layers) and exit")
@@ -303,6 +403,9 @@ def main():
                          "bench (FETCH_SIZE, WRITE_SIZE; same --steps / --warmup / --layers, "
                          "--copy-probe) and exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        print(summarize_mfma(args.summarize_mfma, args.prefill_chunks))
+        return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers,
                               not args.two_calls))
@@ -315,11 +418,14 @@ def main():
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
               "(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.prefill_only:
+        print(json.dumps({"prefill": prefill_leg(dev, args.prefill_chunks)}), flush=True)
+        return
     work = workload_for(args.layers)
     total_steps = args.steps + args.warmup
     lens0, schedule = plan_lens(work, args.steps, args.warmup)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     cfg = K.config_from_workload(work)
     log(f"[bench] buffer {K.kvc_nbytes(cfg, K.KVC_NB_ALLOC) / 2**30:.2f} GiB "
         f"(KV {K.kvc_nbytes(cfg, K.KVC_NB_KV) / 2**30:.2f} GiB)")
@@ -391,6 +497,12 @@ def main():
         log("[bench] copy probe: 1 GiB read + 1 GiB written")
         del src, dst
 
+    prefill = None
+    if args.prefill_chunks > 0:
+        del cache
+        torch.cuda.empty_cache()
+        prefill = prefill_leg(dev, args.prefill_chunks)
+
     cpu = None
     if args.cpu_baseline_seconds > 0:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -427,6 +539,7 @@ def main():
                      "avg_launch_us": round(dec_ms * 1e3 / dec_n, 2) if dec_n else None,
                      "bytes_per_launch": int(kbytes / max(dec_n, 1))},
         "kernels": kinds,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
