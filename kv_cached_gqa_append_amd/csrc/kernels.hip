@@ -575,6 +575,16 @@ __device__ __forceinline__ i32x4 sgpr_rsrc(const void *base, int bytes) {
   return r;
 }
 
+// One of two descriptors, chosen by a wave-uniform condition, element by
+// element (a select between two objects would go through memory), kept in
+// scalar registers.
+__device__ __forceinline__ i32x4 rsrc_sel(bool c, i32x4 a, i32x4 b) {
+  i32x4 u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) u[e] = __builtin_amdgcn_readfirstlane(c ? a[e] : b[e]);
+  return u;
+}
+
 // Streaming tile loads are issued from inline assembly and their waits are
 // placed by hand.  The compiler's own wait insertion cannot follow a ring of
 // loads that stays in flight across a loop's back edge: it waits for every
@@ -1256,21 +1266,20 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 
 // ---------------------------------------------------------------------------
 // Chunk attention (rows with two or more new tokens), bf16, MFMA.
-// Workgroup = 4 waves = 64 query rows of one (row b, KV head g); query row
-// r = i * REP + hl (token-major).  Key tiles of 32 rows are staged in LDS:
-// K row-major (padded rows), V as two transposed 16-row blocks.  Per wave:
+// Workgroup = 8 waves = up to 256 query rows of one (row b, KV head g), so
+// each key tile is read from HBM once for all of them; query row
+// r = i * REP + hl (token-major), wave w holds rows w*32 .. w*32+31 as two
+// 16-row blocks.  Key tiles of 32 rows pass through a 3-stage LDS ring:
+// every thread loads 16 bytes of K and 16 bytes of V per tile with raw buffer
+// loads (hand-placed waits, two tiles in flight), writes them to LDS (K
+// row-major with padded rows, V as two transposed 16-row blocks), and one
+// barrier per tile publishes them.  Per wave and tile:
 //   S^T (32 keys x 16 queries) = K . Q^T   with v_mfma_f32_16x16x32_bf16
 //   O^T (D x 16 queries)     += V^T . P^T  with the same instruction,
-// so the score accumulator already has the layout P^T needs as an operand.
-// Mask per (key, query) only matters on edge tiles but is applied uniformly.
+// each K and V operand read from LDS once and used for both query blocks;
+// the score accumulator already has the layout P^T needs as an operand.
+// Masking (per key and query) is applied uniformly.
 // ---------------------------------------------------------------------------
-template <int D>
-struct ChunkLds {
-  static constexpr int KSTR = D + 8;                 // padded K row (elements)
-  bf16 k[32 * KSTR];
-  bf16 v[2 * D * kVBlock];
-};
-
 struct KeySeg {
   const char *kreg, *vreg;  // region bases
   int ralloc;               // rows per head in the region
@@ -1279,47 +1288,24 @@ struct KeySeg {
   int kind;                 // 0: position = row; 1: ring history; 2: staging (pos = L + row)
 };
 
-template <int D>
-__device__ __forceinline__ void chunk_load_tile(ChunkLds<D> &lds, const KeySeg &sg, int64_t bg,
-                                                int64_t t0) {
-  const int tid = threadIdx.x;
-  constexpr int KCH = 32 * D / 8;        // 16-byte chunks of the K tile
-  constexpr int VCH = 2 * D * kVBlock / 8;
-  const bf16 *ksrc = reinterpret_cast<const bf16 *>(sg.kreg) + (bg * sg.ralloc + t0) * D;
-  for (int c = tid; c < KCH; c += 256) {
-    const int rr = c / (D / 8), cc = c % (D / 8);
-    const uint4 x = *reinterpret_cast<const uint4 *>(ksrc + rr * D + cc * 8);
-    *reinterpret_cast<uint4 *>(&lds.k[rr * ChunkLds<D>::KSTR + cc * 8]) = x;
-  }
-  const bf16 *vsrc = reinterpret_cast<const bf16 *>(sg.vreg) +
-                     ((bg * (sg.ralloc / kVBlock) + t0 / kVBlock) * D) * kVBlock;
-  const bool edge = t0 < sg.vlo || t0 + 32 > sg.vhi;
-  for (int c = tid; c < VCH; c += 256) {
-    uint4 x = *reinterpret_cast<const uint4 *>(vsrc + c * 8);
-    if (edge) {
-      // chunk c covers rows (c / (2D)) * 16 + (c % 2) * 8 + 0..7 of the tile
-      const int64_t r0 = t0 + (c / (2 * D)) * 16 + (c % 2) * 8;
-      uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int64_t ra = r0 + 2 * e2, rb = ra + 1;
-        const uint32_t keep = ((ra >= sg.vlo && ra < sg.vhi) ? 0x0000ffffu : 0u) |
-                              ((rb >= sg.vlo && rb < sg.vhi) ? 0xffff0000u : 0u);
-        w[e2] &= keep;
-      }
-      x = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-    *reinterpret_cast<uint4 *>(&lds.v[c * 8]) = x;
-  }
-}
-
 template <int D, int REP>
-__global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
+__global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
                                                const bf16 *__restrict__ q) {
-  __shared__ ChunkLds<D> lds;
-  constexpr int NDS = D / 32;  // 32-wide d steps (QK contraction)
-  constexpr int NDB = D / 16;  // 16-wide d blocks (PV output)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int NDS = D / 32;              // 32-wide d steps (QK contraction)
+  constexpr int NDB = D / 16;              // 16-wide d blocks (PV output)
+  constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
+  constexpr int KCH = 32 * D / 8;          // 16-byte chunks of a K tile (= of a V tile)
+  constexpr int NSTAGE = 3;
+  // Tiles in flight per thread (one K and one V 16-byte chunk each): the
+  // workgroup is the only one on its CU, so its own loads must cover the
+  // memory latency.
+  constexpr int CP = D >= 128 ? 6 : 8;
+  static_assert(KCH <= 512, "one K chunk and one V chunk per thread");
+  __shared__ __align__(16) bf16 lk[NSTAGE][32 * KSTR];
+  __shared__ __align__(16) bf16 lv[NSTAGE][2 * D * kVBlock];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, nl = lane & 15;
   const int g = blockIdx.y;
   const int SKP = pa.pre_split_keys;
@@ -1351,18 +1337,23 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
   const int64_t bg = (int64_t)b * la.hkv + g;
   const int W = la.window;
 
-  // -- this wave's 16 query rows; lane (q4, nl) holds query row nl ------------
-  const int r = qt * kChunkQTile + wave * 16 + nl;
-  const bool rvalid = r < n * REP;
-  const int qi = r / REP, hl = r % REP;
-  const int64_t qpos = L + qi;
-  bf16x8_t qf[NDS];
-  {
+  // -- this wave's two 16-row query blocks; lane (q4, nl) holds row nl --------
+  int rq[2], qi[2], hl[2];
+  bool rvalid[2];
+  int64_t qpos[2];
+  bf16x8_t qf[2][NDS];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    rq[blk] = qt * kChunkQTile + wave * 32 + blk * 16 + nl;
+    rvalid[blk] = rq[blk] < n * REP;
+    qi[blk] = rq[blk] / REP;
+    hl[blk] = rq[blk] % REP;
+    qpos[blk] = L + qi[blk];
     float raw[NDS][8];
-    const bf16 *qsrc = q + (((int64_t)b * st.C + qi) * st.Hq + g * REP + hl) * D;
+    const bf16 *qsrc = q + (((int64_t)b * st.C + qi[blk]) * st.Hq + g * REP + hl[blk]) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      if (rvalid) {
+      if (rvalid[blk]) {
         const uint4 x = *reinterpret_cast<const uint4 *>(qsrc + ds * 32 + q4 * 8);
         const uint32_t w[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
@@ -1375,15 +1366,15 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
         for (int e = 0; e < 8; ++e) raw[ds][e] = 0.f;
       }
     }
-    if (st.rope && rvalid) {
+    if (st.rope && rvalid[blk]) {
       constexpr int HS = NDS / 2;  // partner d + D/2 sits HS steps later
 #pragma unroll
       for (int ds = 0; ds < HS; ++ds)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int d = ds * 32 + q4 * 8 + e;
-          const float c = st.rope[(qpos * (D / 2) + d) * 2 + 0];
-          const float sn = st.rope[(qpos * (D / 2) + d) * 2 + 1];
+          const float c = st.rope[(qpos[blk] * (D / 2) + d) * 2 + 0];
+          const float sn = st.rope[(qpos[blk] * (D / 2) + d) * 2 + 1];
           const float x1 = raw[ds][e], x2 = raw[ds + HS][e];
           raw[ds][e] = x1 * c - x2 * sn;
           raw[ds + HS][e] = x1 * sn + x2 * c;
@@ -1392,8 +1383,9 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qf[ds][e] = (bf16)raw[ds][e];
+      for (int e = 0; e < 8; ++e) qf[blk][ds][e] = (bf16)raw[ds][e];
   }
+  const bool wave_live = __builtin_amdgcn_readfirstlane((int)(__ballot(rvalid[0]) != 0)) != 0;
 
   // -- key segments -------------------------------------------------------------
   // Positions of the whole q-tile span [pmin, pmax].
@@ -1402,7 +1394,6 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
   const int64_t pmin = L + (int64_t)(qt * kChunkQTile) / REP;
   const int64_t pmax = L + rlast / REP;
   KeySeg seg0{}, seg1{};
-  bool has0 = false, has1 = false;
   if (!la.ring) {
     seg0.kreg = la.k;
     seg0.vreg = la.v;
@@ -1415,11 +1406,10 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
       if (a < wlo) a = wlo;
     }
     seg0.first = a;
-    seg0.end = e;
+    seg0.end = e > a ? e : a;
     seg0.vlo = clo;
     seg0.vhi = chi;
     seg0.kind = 0;
-    has0 = seg0.first < seg0.end;
   } else {
     const int64_t nh = L < W ? L : W;
     seg0.kreg = la.k;
@@ -1430,7 +1420,6 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
     seg0.vlo = 0;
     seg0.vhi = nh;
     seg0.kind = 1;
-    has0 = nh > 0;
     seg1.kreg = la.sk;
     seg1.vreg = la.sv;
     seg1.ralloc = la.stage_rows_alloc;
@@ -1439,101 +1428,247 @@ __global__ __launch_bounds__(256) void k_chunk(StepArgs st, LayerArgs la, Partia
     seg1.vlo = 0;
     seg1.vhi = n;
     seg1.kind = 2;
-    has1 = true;
   }
+  // Tiles of the two segments, visited one after the other.
+  const int n0 = __builtin_amdgcn_readfirstlane((int)cdiv(seg0.end - seg0.first, 32));
+  const int n1 = __builtin_amdgcn_readfirstlane(la.ring ? (int)cdiv(seg1.end - seg1.first, 32) : 0);
+  const int ntiles = n0 + n1;
+
+  // -- buffer resources: this head's K and V in each segment, and an empty one
+  const int64_t reg0 = (int64_t)seg0.ralloc * D * 2;
+  const i32x4 dk0 = sgpr_rsrc(seg0.kreg + bg * reg0, (int)reg0);
+  const i32x4 dv0 = sgpr_rsrc(seg0.vreg + bg * reg0, (int)reg0);
+  const int64_t reg1 = la.ring ? (int64_t)seg1.ralloc * D * 2 : 0;
+  const i32x4 dk1 = la.ring ? sgpr_rsrc(seg1.kreg + bg * reg1, (int)reg1) : dk0;
+  const i32x4 dv1 = la.ring ? sgpr_rsrc(seg1.vreg + bg * reg1, (int)reg1) : dv0;
+  const i32x4 dnone = sgpr_rsrc(seg0.kreg, 0);
+  // Threads past a tile's chunk count (D < 128: whole waves) load nothing.
+  const bool loader = wave * 64 < KCH;
+  const int voffs = tid * 16;
+
+  // Tile i: its segment, first storage row and bounds (uniform scalars).
+  struct TileInfo {
+    int kind;
+    int64_t t0, vlo, vhi;
+  };
+  const int64_t f0 = seg0.first, lo0 = seg0.vlo, hi0 = seg0.vhi;
+  const int64_t f1 = seg1.first, lo1 = seg1.vlo, hi1 = seg1.vhi;
+  const int kind0 = seg0.kind, kind1 = seg1.kind;
+  auto tile_of = [=](int i) __attribute__((always_inline)) -> TileInfo {
+    // field by field: a select between two whole structs would go through memory
+    const bool first = i < n0;
+    TileInfo t;
+    t.kind = first ? kind0 : kind1;
+    t.t0 = first ? f0 + (int64_t)i * 32 : f1 + (int64_t)(i - n0) * 32;
+    t.vlo = first ? lo0 : lo1;
+    t.vhi = first ? hi0 : hi1;
+    return t;
+  };
+  // Issue the loads of tile i (zeros and no memory access past the last
+  // tile or for threads without a chunk): one K and one V 16-byte chunk.
+  auto issue = [&](int i, u32x4 &rk, u32x4 &rv) __attribute__((always_inline)) {
+    const bool live = loader && i < ntiles;
+    const bool second = i >= n0;
+    const TileInfo ti = tile_of(live ? i : 0);
+    const int64_t t0 = ti.t0;
+    const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
+    const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
+    // K rows and V blocks advance by the same bytes per row
+    const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
+    tile_load<0>(rk, ka, voffs, so);
+    tile_load<0>(rv, va, voffs, so);
+  };
+  // Write tile i's chunks (already waited for) to LDS stage s; V rows outside
+  // the segment's data are zeroed (their p is 0, and 0 times garbage could be
+  // NaN).
+  auto store = [&](int i, const u32x4 &rk, const u32x4 &rv, int s) __attribute__((always_inline)) {
+    if (!loader) return;
+    const TileInfo ti = tile_of(i < ntiles ? i : 0);
+    const int64_t t0 = ti.t0, vlo = ti.vlo, vhi = ti.vhi;
+    const int c = tid;
+    const int rr = c / (D / 8), cc = c % (D / 8);
+    *reinterpret_cast<u32x4 *>(&lk[s][rr * KSTR + cc * 8]) = rk;
+    u32x4 x = rv;
+    if (t0 < vlo || t0 + 32 > vhi) {
+      // chunk c covers rows (c / (2D)) * 16 + (c % 2) * 8 + 0..7 of the tile
+      const int64_t r0 = t0 + (c / (2 * D)) * 16 + (c % 2) * 8;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int64_t ra = r0 + 2 * e2, rb = ra + 1;
+        const uint32_t keep = ((ra >= vlo && ra < vhi) ? 0x0000ffffu : 0u) |
+                              ((rb >= vlo && rb < vhi) ? 0xffff0000u : 0u);
+        x[e2] &= keep;
+      }
+    }
+    *reinterpret_cast<u32x4 *>(&lv[s][c * 8]) = x;
+  };
 
   const float scale = kLog2e * rsqrtf((float)D);
-  float mrun = -INFINITY, lrun = 0.f;
-  floatx4 oacc[NDB];
+  // positions fit in 32 bits (max_len < 2^31)
+  const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
+  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  floatx4 oacc[2][NDB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[blk][db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  auto run_segment = [&](const KeySeg &sg) {
-    for (int64_t t0 = sg.first; t0 < sg.end; t0 += 32) {
-      __syncthreads();
-      chunk_load_tile<D>(lds, sg, bg, t0);
-      __syncthreads();
-      // S^T = K Q^T
-      floatx4 sacc[2];
+  auto compute = [&](int i, int s) __attribute__((always_inline)) {
+    const TileInfo ti = tile_of(i);
+    const int kind = ti.kind;
+    const int64_t t0 = ti.t0, vlo = ti.vlo, vhi = ti.vhi;
+    // S^T = K Q^T for both query blocks, each K operand read once
+    floatx4 sacc[2][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-              &lds.k[(kb * 16 + nl) * ChunkLds<D>::KSTR + ds * 32 + q4 * 8]);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ds], sacc[kb], 0, 0, 0);
-        }
+      for (int kb = 0; kb < 2; ++kb) sacc[blk][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t *>(&lk[s][(kb * 16 + nl) * KSTR + ds * 32 + q4 * 8]);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          sacc[blk][kb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[blk][ds], sacc[blk][kb], 0, 0, 0);
       }
-      // mask + scale; sacc[kb][jj] is key row t0 + kb*16 + 4*q4 + jj, query nl
+    // mask + scale + online softmax per block; sacc[blk][kb][jj] is key row
+    // t0 + kb*16 + 4*q4 + jj, query row nl of the block.  A tile whose keys
+    // every query of the q tile sees (data rows below its first position and,
+    // on a windowed layer, inside its last position's window) needs no mask:
+    // only the tiles at the diagonal and the edges do.
+    const int t0i = (int)t0, vloi = (int)vlo, vhii = (int)vhi;
+    const bool full = kind == 0 && t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
+                      (W == 0 || pmax_i - t0i < W);
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
       float sv[2][4];
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int64_t t = t0 + kb * 16 + q4 * 4 + jj;
-          int64_t pos;
-          if (sg.kind == 0)
-            pos = t;
-          else if (sg.kind == 1)
-            pos = ring_slot_pos(t, L, W);
-          else
-            pos = L + t;
-          bool ok = rvalid && t >= sg.vlo && t < sg.vhi && pos >= 0 && pos <= qpos;
-          if (W > 0) ok = ok && (qpos - pos < W);
-          const float x = ok ? sacc[kb][jj] * scale : -INFINITY;
-          sv[kb][jj] = x;
-          tmax = fmaxf(tmax, x);
-        }
+          for (int jj = 0; jj < 4; ++jj) {
+            sv[kb][jj] = sacc[blk][kb][jj] * scale;
+            tmax = fmaxf(tmax, sv[kb][jj]);
+          }
+      } else {
+        const int qp = (int)qpos[blk];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const int t = t0i + kb * 16 + q4 * 4 + jj;
+            int pos;
+            if (kind == 0)
+              pos = t;
+            else if (kind == 1)
+              pos = (int)ring_slot_pos(t, L, W);
+            else
+              pos = Li + t;
+            bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp;
+            if (W > 0) ok = ok && (qp - pos < W);
+            const float x = ok ? sacc[blk][kb][jj] * scale : -INFINITY;
+            sv[kb][jj] = x;
+            tmax = fmaxf(tmax, x);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(mrun, tmax);
+      const float mn = fmaxf(mrun[blk], tmax);
       const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = exp2f(mrun - mu);
-      bf16x8_t pf;
+      const float alpha = __builtin_amdgcn_exp2f(mrun[blk] - mu);
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float pe = exp2f(sv[kb][jj] - mu);
+          const float pe = __builtin_amdgcn_exp2f(sv[kb][jj] - mu);
           ps += pe;
-          pf[kb * 4 + jj] = (bf16)pe;
+          pf[blk][kb * 4 + jj] = (bf16)pe;
         }
-      lrun = lrun * alpha + ps;
-      mrun = mn;
+      lrun[blk] = lrun[blk] * alpha + ps;
+      mrun[blk] = mn;
+      // rescale only when some query's running max moved
+      if (__ballot(alpha != 1.f) != 0) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      // O^T += V^T P^T; k-slot 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int d = db * 16 + nl;
-        const uint2 lo8 = *reinterpret_cast<const uint2 *>(&lds.v[(0 * D + d) * kVBlock + q4 * 4]);
-        const uint2 hi8 = *reinterpret_cast<const uint2 *>(&lds.v[(1 * D + d) * kVBlock + q4 * 4]);
-        const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
-        oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av), pf,
-                                                           oacc[db], 0, 0, 0);
+        for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha;
       }
     }
+    // O^T += V^T P^T; k-slot 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + nl;
+      const uint2 lo8 = *reinterpret_cast<const uint2 *>(&lv[s][(0 * D + d) * kVBlock + q4 * 4]);
+      const uint2 hi8 = *reinterpret_cast<const uint2 *>(&lv[s][(1 * D + d) * kVBlock + q4 * 4]);
+      const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        oacc[blk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, av), pf[blk], oacc[blk][db], 0, 0, 0);
+    }
   };
-  if (has0) run_segment(seg0);
-  if (has1) run_segment(seg1);
+
+  // LDS stores of a tile complete, then every wave meets: the tile is
+  // published (global loads stay in flight: no vmcnt wait here).
+  auto lds_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+
+  // Pipeline, P = CP register sets: at step i, tile i + 1 (set (i + 1) % P)
+  // is waited for and written to LDS stage (i + 1) % 3, tile i + 1 + P is
+  // issued into the same set, one barrier publishes the stage, and tile i is
+  // computed from stage i % 3; tiles i + 2 .. i + 1 + P stay in flight (a
+  // stage is rewritten two steps after it was last read, behind a barrier).
+  // Steps run in groups of P so set indices are compile-time; the last group
+  // is padded with empty steps, so every path keeps the same loads in flight.
+  // The queries' loads above are retired before the first tile load.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  u32x4 rk[CP], rv[CP];
+  static_for<0, CP>([&](auto t) { issue(decltype(t)::value, rk[decltype(t)::value], rv[decltype(t)::value]); });
+  tile_wait<2 * (CP - 1)>(rk[0]);
+  tile_wait<2 * (CP - 1)>(rv[0]);
+  store(0, rk[0], rv[0], 0);
+  issue(CP, rk[0], rv[0]);
+  for (int i0 = 0; i0 < ntiles; i0 += CP) {
+    static_for<0, CP>([&](auto u) {
+      constexpr int S = (decltype(u)::value + 1) % CP;   // set of tile i + 1
+      const int i = i0 + decltype(u)::value;
+      tile_wait<2 * (CP - 1)>(rk[S]);
+      tile_wait<2 * (CP - 1)>(rv[S]);
+      store(i + 1, rk[S], rv[S], (i + 1) % NSTAGE);
+      issue(i + 1 + CP, rk[S], rv[S]);
+      lds_barrier();
+      if (wave_live && i < ntiles) compute(i, i % NSTAGE);
+    });
+  }
+  // Retire the loads still in flight before their registers go away.
+  static_for<0, CP>([&](auto t) {
+    tile_wait<0>(rk[decltype(t)::value]);
+    tile_wait<0>(rv[decltype(t)::value]);
+  });
+  asm volatile("" ::: "memory");
 
   // -- partials for this split ---------------------------------------------------
-  float lt = lrun + __shfl_xor(lrun, 16);
-  lt += __shfl_xor(lt, 32);
-  if (rvalid) {
-    const int64_t slot = (((int64_t)b * pa.max_chunk + qi) * st.Hq + g * REP + hl) * kChunkSplitCap + ks;
-    if (q4 == 0) {
-      pa.pml[slot * 2 + 0] = lt > 0.f ? mrun : -INFINITY;
-      pa.pml[slot * 2 + 1] = lt;
-    }
-    if (lt > 0.f) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+  for (int blk = 0; blk < 2; ++blk) {
+    float lt = lrun[blk] + __shfl_xor(lrun[blk], 16);
+    lt += __shfl_xor(lt, 32);
+    if (rvalid[blk]) {
+      const int64_t slot =
+          (((int64_t)b * pa.max_chunk + qi[blk]) * st.Hq + g * REP + hl[blk]) * kChunkSplitCap + ks;
+      if (q4 == 0) {
+        pa.pml[slot * 2 + 0] = lt > 0.f ? mrun[blk] : -INFINITY;
+        pa.pml[slot * 2 + 1] = lt;
+      }
+      if (lt > 0.f) {
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) pa.pout[slot * D + db * 16 + q4 * 4 + jj] = oacc[db][jj];
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            pa.pout[slot * D + db * 16 + q4 * 4 + jj] = oacc[blk][db][jj];
+      }
     }
   }
 }
@@ -1543,7 +1678,7 @@ bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && re
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, const Launch &lc) {
-  hipExtLaunchKernelGGL((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(256), 0,
+  hipExtLaunchKernelGGL((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(512), 0,
                      (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q);
 }
 

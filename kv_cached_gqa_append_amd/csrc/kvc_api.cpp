@@ -54,7 +54,7 @@ struct kvc_cache {
 namespace {
 
 // Smallest chunk-attention split (keys) before the split count per row is capped.
-constexpr int32_t kChunkSplitMin = 1024;
+constexpr int32_t kChunkSplitMin = 256;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }

@@ -23,8 +23,8 @@ constexpr int kDecodeSplitCap = 64;
 // Keys per decode tile; decode splits are whole tiles.
 constexpr int kDecodeTile = 16;
 constexpr int kChunkSplitCap = 16;
-// Query rows per chunk-attention workgroup (4 waves x 16 rows).
-constexpr int kChunkQTile = 64;
+// Query rows per chunk-attention workgroup (8 waves x 32 rows).
+constexpr int kChunkQTile = 256;
 
 struct LayerLayout {
   int64_t k_off = 0, v_off = 0;           // byte offsets in the device buffer
