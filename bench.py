@@ -7,12 +7,15 @@ idle rows (n_new = 0, redrawn per step).  The history is filled through the
 real protocol in 64-token chunks before timing (untimed); q/k/v are
 synthetic N(0, 1) tensors already resident in HBM.
 
-One step = for each of the 32 layers kvc_append_attend (one kernel per layer
-for these one-token steps: RoPE + append, decode attention, split merge), then
-one kvc_advance; ``--two-calls`` runs kvc_append + kvc_attend instead (append,
-decode and combine kernels).  Warmup steps run first; the timed steps are
-bracketed by torch.cuda.synchronize().  Kernel durations come from HIP events
-that each dispatch stamps at its own start and end on the launch stream.
+One step = for each of the 32 layers kvc_append + kvc_attend (append, decode
+attention and split-combine kernels), then one kvc_advance; the decode
+attention kernel is the roofline kernel.  A second timed leg then runs the
+same steps through kvc_append_attend (one kernel per layer: RoPE + append,
+decode attention, split merge) and reports it next to the headline
+(``--fused`` makes it the headline, ``--no-other-leg`` skips it).  Warmup
+steps run first; the timed steps are bracketed by torch.cuda.synchronize().
+Kernel durations come from HIP events that each dispatch stamps at its own
+start and end on the launch stream.
 
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
 GPU.  ``--cpu-baseline-seconds 0`` skips the oracle timing.
@@ -93,9 +96,10 @@ def workload_for(layers):
     return work
 
 
-def plan_lens(work, steps, warmup):
-    """Initial lengths (clipped so every step fits) and the n_new schedule."""
-    total = steps + warmup
+def plan_lens(work, steps, warmup, legs=1):
+    """Initial lengths (clipped so every step of every timed leg fits) and the
+    n_new schedule."""
+    total = (steps + warmup) * legs
     lens0 = wl.initial_lens_decode_b64(work.batch)
     if lens0.max() + total > work.max_len:
         lens0 = np.minimum(lens0, work.max_len - total)
@@ -103,9 +107,10 @@ def plan_lens(work, steps, warmup):
 
 
 def timed_decode_bytes(work, steps, warmup, fused=False):
-    """Algorithmic bytes of each timed decode launch, in launch order."""
+    """Algorithmic bytes of each timed decode launch, in launch order (runs
+    of one timed leg, --no-other-leg)."""
     per_launch = fused_kernel_bytes if fused else decode_kernel_bytes
-    lens0, sched = plan_lens(work, steps, warmup)
+    lens0, sched = plan_lens(work, steps, warmup, 2)
     lens = lens0.copy()
     for s in range(warmup):
         lens = lens + sched[s]
@@ -386,8 +391,11 @@ def main():
                     help="chunks of the prefill leg (0 skips it)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (counter runs) and print its object")
-    ap.add_argument("--two-calls", action="store_true",
-                    help="kvc_append + kvc_attend per layer instead of kvc_append_attend")
+    ap.add_argument("--fused", action="store_true",
+                    help="headline leg through kvc_append_attend (one kernel per layer) instead "
+                         "of kvc_append + kvc_attend")
+    ap.add_argument("--no-other-leg", action="store_true",
+                    help="skip the second timed leg through the other entry point")
     ap.add_argument("--layers", type=int, default=0,
                     help="fewer layers (counter runs: per-launch work is unchanged)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -408,11 +416,11 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers,
-                              not args.two_calls))
+                              args.fused))
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.steps, args.warmup, args.layers,
-                                 not args.two_calls))
+                                 args.fused))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
@@ -424,8 +432,10 @@ def main():
         print(json.dumps({"prefill": prefill_leg(dev, args.prefill_chunks)}), flush=True)
         return
     work = workload_for(args.layers)
-    total_steps = args.steps + args.warmup
-    lens0, schedule = plan_lens(work, args.steps, args.warmup)
+    legs = 1 if args.no_other_leg else 2
+    # lengths clipped for two legs either way, so runs with and without the
+    # second leg time the same workload
+    lens0, schedule = plan_lens(work, args.steps, args.warmup, 2)
     cfg = K.config_from_workload(work)
     log(f"[bench] buffer {K.kvc_nbytes(cfg, K.KVC_NB_ALLOC) / 2**30:.2f} GiB "
         f"(KV {K.kvc_nbytes(cfg, K.KVC_NB_KV) / 2**30:.2f} GiB)")
@@ -444,49 +454,71 @@ def main():
           for _ in range(work.n_layer)]
     outs = [torch.empty_like(x) for x in qs]
 
-    fused = not args.two_calls
+    def timed_leg(fused, sched):
+        """W warmup steps, then K timed steps of the schedule through one entry
+        point; whole-step and roofline-kernel figures."""
+        def run_step(n):
+            if fused:
+                for l in range(work.n_layer):
+                    cache.append_attend(l, qs[l], ks[l], vs[l], n, out=outs[l])
+            else:
+                for l in range(work.n_layer):
+                    cache.append(l, ks[l], vs[l], n)
+                    cache.attend(l, qs[l], outs[l])
+            cache.advance()
 
-    def run_step(n):
-        if fused:
-            for l in range(work.n_layer):
-                cache.append_attend(l, qs[l], ks[l], vs[l], n, out=outs[l])
-        else:
-            for l in range(work.n_layer):
-                cache.append(l, ks[l], vs[l], n)
-                cache.attend(l, qs[l], outs[l])
-        cache.advance()
+        for n in sched[:args.warmup]:
+            run_step(n)
+        torch.cuda.synchronize()
+        lens_cur = np.asarray(cache.lens(), dtype=np.int64)
+        kbytes, sbytes, tokens = 0, 0, 0
+        per_launch = fused_kernel_bytes if fused else decode_kernel_bytes
+        for n in sched[args.warmup:]:
+            kbytes += per_launch(lens_cur, n, work) * work.n_layer
+            sbytes += step_bytes(lens_cur, n, work)
+            tokens += int(n.sum())
+            lens_cur = lens_cur + n
+        K.kvc_timing_begin(cache.handle, args.steps * work.n_layer * 4 + 16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for n in sched[args.warmup:]:
+            run_step(n)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        kt = K.kvc_timing_end(cache.handle)
+        assert cache.lens() == lens_cur.tolist()
+        dec_ms, dec_n = kt["fused" if fused else "decode"]
+        r = {"fused": fused, "dt": dt, "ms_step": dt * 1e3 / args.steps, "tokens": tokens,
+             "value": sbytes / dt / 1e9, "kbytes": kbytes, "dec_n": dec_n,
+             "dec_us": dec_ms * 1e3 / dec_n if dec_n else None,
+             "achieved": kbytes / (dec_ms / 1e3) / 1e9 if dec_ms > 0 else 0.0,
+             "kinds": {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                           "us_avg": round(v[0] * 1e3 / v[1], 2) if v[1] else None}
+                       for k, v in kt.items() if v[1]}}
+        log(f"[bench] {'kvc_append_attend' if fused else 'kvc_append+kvc_attend'}: "
+            f"{args.steps} steps in {dt:.3f}s: {r['ms_step']:.3f} ms/step, "
+            f"{tokens / dt:.0f} tok/s, whole-step {r['value']:.0f} GB/s, decode kernel "
+            f"{r['achieved']:.0f} GB/s")
+        log(f"[bench] kernels: {json.dumps(r['kinds'])}")
+        return r
 
-    for s in range(args.warmup):
-        run_step(schedule[s])
-    torch.cuda.synchronize()
-    lens_at = np.asarray(cache.lens(), dtype=np.int64)
-    kbytes, sbytes, tokens = 0, 0, 0
-    lens_cur = lens_at.copy()
-    for s in range(args.warmup, total_steps):
-        n = schedule[s]
-        kbytes += (fused_kernel_bytes if fused else decode_kernel_bytes)(lens_cur, n, work) \
-            * work.n_layer
-        sbytes += step_bytes(lens_cur, n, work)
-        tokens += int(n.sum())
-        lens_cur = lens_cur + n
-    K.kvc_timing_begin(cache.handle, args.steps * work.n_layer * 4 + 16)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.warmup, total_steps):
-        run_step(schedule[s])
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    kt = K.kvc_timing_end(cache.handle)
-    assert cache.lens() == lens_cur.tolist()
-    dec_ms, dec_n = kt["fused" if fused else "decode"]
-    ms_step = dt * 1e3 / args.steps
-    achieved = kbytes / (dec_ms / 1e3) / 1e9 if dec_ms > 0 else 0.0
-    value = sbytes / dt / 1e9
-    kinds = {k: {"ms_total": round(v[0], 3), "launches": v[1],
-                 "us_avg": round(v[0] * 1e3 / v[1], 2) if v[1] else None} for k, v in kt.items()}
-    log(f"[bench] {args.steps} steps in {dt:.3f}s: {ms_step:.3f} ms/step, "
-        f"{tokens / dt:.0f} tok/s, whole-step {value:.0f} GB/s, decode kernel {achieved:.0f} GB/s")
-    log(f"[bench] kernels: {json.dumps(kinds)}")
+    per_leg = args.steps + args.warmup
+    head = timed_leg(args.fused, schedule[:per_leg])
+    other = None
+    if legs == 2:
+        o = timed_leg(not args.fused, schedule[per_leg:])
+        other = {"entry": "kvc_append_attend" if o["fused"] else "kvc_append+kvc_attend",
+                 "value": round(o["value"], 1), "unit": "GB/s",
+                 "ms_per_step": round(o["ms_step"], 4),
+                 "tokens_per_s": round(o["tokens"] / o["dt"], 1),
+                 "kernel": "k_decode<128,4,fused>" if o["fused"] else "k_decode<128,4>",
+                 "kernel_achieved": round(o["achieved"], 1),
+                 "kernel_frac": round(o["achieved"] / PEAK_HBM_GBS, 4),
+                 "avg_launch_us": round(o["dec_us"], 2) if o["dec_us"] else None,
+                 "kernels": o["kinds"]}
+    fused = head["fused"]
+    dt, ms_step, tokens, value = head["dt"], head["ms_step"], head["tokens"], head["value"]
+    achieved, kbytes, dec_n, kinds = head["achieved"], head["kbytes"], head["dec_n"], head["kinds"]
 
     if args.copy_probe:
         src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).random_()
@@ -527,7 +559,8 @@ def main():
         "pct_of_peak_hbm": round(100.0 * value / PEAK_HBM_GBS, 2),
         "config": {"workload": "decode_b64", "n_layer": work.n_layer, "batch": B,
                    "n_q_head": work.n_q_head, "n_kv_head": work.n_kv_head[0], "head_dim": D,
-                   "max_len": work.max_len, "lens_init": "U[1,8128]", "idle_rows_per_step": 6,
+                   "max_len": work.max_len, "lens_init": f"U[1,8128] clipped at {int(lens0.max())}",
+                   "idle_rows_per_step": 6,
                    "new_tokens_per_row": 1,
                    "entry": "kvc_append_attend" if fused else "kvc_append+kvc_attend"},
         "roofline": {"bound": "hbm",
@@ -536,9 +569,10 @@ def main():
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic["bytes"] if traffic else None,
                      "traffic_ratio": traffic["ratio"] if traffic else None,
-                     "avg_launch_us": round(dec_ms * 1e3 / dec_n, 2) if dec_n else None,
+                     "avg_launch_us": round(head["dec_us"], 2) if head["dec_us"] else None,
                      "bytes_per_launch": int(kbytes / max(dec_n, 1))},
         "kernels": kinds,
+        "other_entry_point": other,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

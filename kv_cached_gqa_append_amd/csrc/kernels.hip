@@ -701,34 +701,29 @@ __device__ __forceinline__ float keys_sum(float x) {
 
 // NBUF: register tiles in the ring (NBUF - 1 in flight); WAVES: occupancy the
 // register allocator must meet.
-// Append of a single-token step (C == 1) for (row b, KV head g): a real
-// token at position p goes to its slot (full layout: p, ring: p % W) with K
-// rotated and V copied; a padded token (valid == false) goes to the scratch
-// row with V zeroed.  Also the slot report and, for a real token entering a
-// new 32-row tile, the zeroing of V past the row's end in that tile (the
-// decode tiles read those rows masked).  Same stores as k_append.
+// Stores of one token of a single-token step (C == 1) for (row b, KV head
+// g), the same stores k_append makes: lane e < D/2 holds the pair (e, e +
+// D/2) of the (rotated) key, y1 and y2, and of the value, v1 and v2.  A real
+// token (valid) at position p goes to its slot (full layout: p, ring: p % W);
+// a padded one to the scratch row with its value zeroed.  Also the slot
+// report and, for a real token entering a new 32-row tile, the zeroing of V
+// past the row's end in that tile (the decode tiles read those rows masked).
 template <int D>
-__device__ __forceinline__ void decode_append(const StepArgs &st, const LayerArgs &la,
-                                              const FusedArgs &fa, int b, int g, int64_t p,
-                                              bool valid, int lane) {
+__device__ __forceinline__ void store_token_row(const LayerArgs &la, const FusedArgs &fa, int b,
+                                                int g, int64_t p, bool valid, float y1, float y2,
+                                                bf16 v1, bf16 v2, int lane) {
+  static_assert(D / 2 <= 64, "one (d, d + D/2) pair per lane");
   const int64_t bg = (int64_t)b * la.hkv + g;
   const int64_t r = la.ring ? (valid ? p % la.window : (int64_t)la.window)
                             : (valid ? p : (int64_t)la.rows);
-  const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
-  const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
-  bf16 *kd = k_row<bf16>(la.k, bg, la.rows_alloc, r, D);
-  bf16 *vd = v_elem<bf16>(la.v, bg, la.rows_alloc, r, 0, D);
-  const bool rot = st.rope != nullptr && valid;
   constexpr int half = D / 2;
-  for (int e = lane; e < half; e += 64) {
-    const float x1 = (float)ks[e], x2 = (float)ks[e + half];
-    float y1 = x1, y2 = x2;
-    if (rot) rope_pair(x1, x2, st.rope[(p * half + e) * 2 + 0], st.rope[(p * half + e) * 2 + 1],
-                       &y1, &y2);
-    kd[e] = (bf16)y1;
-    kd[e + half] = (bf16)y2;
-    vd[e * kVBlock] = valid ? vs[e] : (bf16)0.f;
-    vd[(e + half) * kVBlock] = valid ? vs[e + half] : (bf16)0.f;
+  if (lane < half) {
+    bf16 *kd = k_row<bf16>(la.k, bg, la.rows_alloc, r, D);
+    bf16 *vd = v_elem<bf16>(la.v, bg, la.rows_alloc, r, 0, D);
+    kd[lane] = (bf16)y1;
+    kd[lane + half] = (bf16)y2;
+    vd[lane * kVBlock] = valid ? v1 : (bf16)0.f;
+    vd[(lane + half) * kVBlock] = valid ? v2 : (bf16)0.f;
   }
   if (fa.slot_out && g == 0 && lane == 0) fa.slot_out[b] = (int32_t)r;
   if (valid) {
@@ -745,6 +740,21 @@ __device__ __forceinline__ void decode_append(const StepArgs &st, const LayerArg
   }
 }
 
+// The padded token of an idle row (n_new == 0) of a single-token step: its
+// key as given and a zero value go to the scratch row.
+template <int D>
+__device__ __forceinline__ void store_idle_token(const LayerArgs &la, const FusedArgs &fa, int b,
+                                                 int g, int64_t p, int lane) {
+  const int64_t bg = (int64_t)b * la.hkv + g;
+  const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
+  float y1 = 0.f, y2 = 0.f;
+  if (lane < D / 2) {
+    y1 = (float)ks[lane];
+    y2 = (float)ks[lane + D / 2];
+  }
+  store_token_row<D>(la, fa, b, g, p, false, y1, y2, (bf16)0.f, (bf16)0.f, lane);
+}
+
 // One term of a split merge: a + w * x, skipping splits of weight 0 (a split
 // that saw no visible key never wrote its slot).  Shared by both merges so
 // they round identically.
@@ -759,16 +769,23 @@ __device__ __forceinline__ float combine_tree(const float (&a)[8]) {
 // output o (REP x D) by one wave, with the same arithmetic in the same order
 // as k_combine.  The partials are read with agent-scope loads (served from
 // the device's point of coherence, past this XCD's L2).  Each lane owns D/64
-// consecutive elements; the loads of 8 splits of up to 4 heads are issued
-// together, so a merge of up to 8 splits costs one round trip per 4 heads.
-// wts: REP * 64 floats of LDS.
+// consecutive elements.  The first 8 splits of the first 4 heads are loaded
+// together with every head's (m, l), so a merge of up to 8 splits of up to
+// 4 heads costs one round trip to memory; later splits and heads load 8
+// splits of 4 heads at a time.  wts: REP * 64 floats of LDS.
 template <int D, int REP>
 __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepArgs &st, int b,
                                               int h0, int ns, float *wts, bf16 *o, int lane) {
   auto ld = [](const float *ptr) {
     return __hip_atomic_load(ptr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+  constexpr int DPL = D / 64;                 // elements per lane
+  constexpr int HG = REP < 4 ? REP : 4;       // heads per load round
   const int64_t cap = kDecodeSplitCap;
+  const int d0 = lane * DPL;
+  auto part = [&](int h, int sp) {
+    return pa.dout + (((int64_t)b * st.Hq + h0 + h) * cap + sp) * D + d0;
+  };
   float lv[REP], mv[REP];
 #pragma unroll
   for (int h = 0; h < REP; ++h) {
@@ -776,6 +793,13 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
     lv[h] = lane < ns ? ld(ml + 2 * lane + 1) : 0.f;
     mv[h] = lane < ns ? ld(ml + 2 * lane) : -INFINITY;
   }
+  float first[HG][8][DPL];
+#pragma unroll
+  for (int h = 0; h < HG; ++h)
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) first[h][u][e] = u < ns ? ld(part(h, u) + e) : 0.f;
 #pragma unroll
   for (int h = 0; h < REP; ++h) {
     const float ms = (lane < ns && lv[h] > 0.f) ? mv[h] : -INFINITY;
@@ -785,9 +809,6 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
     wts[h * 64 + lane] = w / Lt;
   }
   __syncthreads();
-  constexpr int DPL = D / 64;                 // elements per lane
-  constexpr int HG = REP < 4 ? REP : 4;       // heads per load round
-  const int d0 = lane * DPL;
 #pragma unroll
   for (int hg = 0; hg < REP; hg += HG) {
     float a[HG][DPL][8];
@@ -797,17 +818,29 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
       for (int e = 0; e < DPL; ++e)
 #pragma unroll
         for (int u = 0; u < 8; ++u) a[h][e][u] = 0.f;
+    // x[h][u][e]: splits s0 .. s0 + 7 (those below ns) of heads hg ..
+    float x[HG][8][DPL];
+    auto fetch = [&](int s0) {
+      if (hg == 0 && s0 == 0) {
+#pragma unroll
+        for (int h = 0; h < HG; ++h)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) x[h][u][e] = first[h][u][e];
+      } else {
+#pragma unroll
+        for (int h = 0; h < HG; ++h)
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+#pragma unroll
+            for (int e = 0; e < DPL; ++e)
+              x[h][u][e] = s0 + u < ns ? ld(part(hg + h, s0 + u) + e) : 0.f;
+      }
+    };
     int s = 0;
     for (; s + 8 <= ns; s += 8) {
-      float x[HG][8][DPL];
-#pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float *os = pa.dout + ((int64_t)b * st.Hq + h0 + hg + h) * cap * D + d0;
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-#pragma unroll
-          for (int e = 0; e < DPL; ++e) x[h][u][e] = ld(os + (int64_t)(s + u) * D + e);
-      }
+      fetch(s);
 #pragma unroll
       for (int h = 0; h < HG; ++h)
 #pragma unroll
@@ -817,19 +850,18 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
           for (int e = 0; e < DPL; ++e) a[h][e][u] = combine_acc(a[h][e][u], w, x[h][u][e]);
         }
     }
-    for (; s < ns; ++s) {
-      float x[HG][DPL];
+    if (s < ns) {  // the last ns % 8 splits, summed in order into slot 0
+      fetch(s);
 #pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float *os = pa.dout + ((int64_t)b * st.Hq + h0 + hg + h) * cap * D + d0;
+      for (int u = 0; u < 8; ++u) {
+        if (s + u < ns) {
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) x[h][e] = ld(os + (int64_t)s * D + e);
-      }
+          for (int h = 0; h < HG; ++h) {
+            const float w = wts[(hg + h) * 64 + s + u];
 #pragma unroll
-      for (int h = 0; h < HG; ++h) {
-        const float w = wts[(hg + h) * 64 + s];
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) a[h][e][0] = combine_acc(a[h][e][0], w, x[h][e]);
+            for (int e = 0; e < DPL; ++e) a[h][e][0] = combine_acc(a[h][e][0], w, x[h][u][e]);
+          }
+        }
       }
     }
 #pragma unroll
@@ -856,13 +888,16 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   __shared__ __align__(16) uint16_t pls[2][REP][TK];       // p of a tile, bf16
 
   const int lane = threadIdx.x;
-  const int g = blockIdx.y;
+  const int g = pa.dec_transpose ? blockIdx.x : blockIdx.y;
+  const int item = pa.dec_transpose ? blockIdx.y : blockIdx.x;
   const int SK = pa.dec_split_keys;
   int b;
   int64_t split64;
+  auto row_at = [&](int r) { return pa.dec_ordered ? (int)pa.dec_order[r] : r; };
   find_item(
-      st.B, blockIdx.x,
-      [&](int r) -> int {
+      st.B, item,
+      [&](int r0) -> int {
+        const int r = row_at(r0);
         const int nr = st.n_new[r];
         if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
         int64_t base, lo, hi;
@@ -871,9 +906,10 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
       },
       &b, &split64);
   if (b < 0) return;
+  b = __builtin_amdgcn_readfirstlane(row_at(b));
   if constexpr (FUSED) {
     if (st.n_new[b] == 0) {  // idle row: its padded token and zero outputs
-      decode_append<D>(st, la, fa, b, g, st.lens[b], false, lane);
+      store_idle_token<D>(la, fa, b, g, st.lens[b], lane);
       bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
       for (int e = lane; e < REP * D; e += 64) o[e] = (bf16)0.f;
       return;
@@ -901,16 +937,28 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const int t_stride = __builtin_amdgcn_readfirstlane(nsplit * TK);
   const int n_iter = __builtin_amdgcn_readfirstlane((ntile - split + nsplit - 1) / nsplit);
   const int64_t bg = (int64_t)b * la.hkv + g;
+  // Fused: the new key's storage row (full layout: p; ring: p % W) lies in
+  // exactly one split.  That wave loads the token's key, value and rotation
+  // here, with the queries' loads (one round trip for both), and stores the
+  // rotated row once the queries are staged, before its tile loads.
+  bool appender = false;
+  float ax1 = 0.f, ax2 = 0.f, arc = 1.f, ars = 0.f;
+  bf16 av1 = (bf16)0.f, av2 = (bf16)0.f;
   if constexpr (FUSED) {
-    // The new key's storage row (full layout: p; ring: p % W) lies in exactly
-    // one split; that wave writes it before it streams its tiles.
     const int r_new = la.ring ? (int)(p % la.window) : (int)p;
-    if ((r_new - (int)base64) / TK % nsplit == split)
-      decode_append<D>(st, la, fa, b, g, p, true, lane);
-    // The tile loads below come after these stores in program order (the
-    // barrier keeps the compiler from moving the stores past them), and the
-    // memory pipeline keeps one wave's accesses to one address in order.
-    asm volatile("" ::: "memory");
+    appender = (r_new - (int)base64) / TK % nsplit == split;
+    if (appender && lane < D / 2) {
+      const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
+      const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
+      ax1 = (float)ks[lane];
+      ax2 = (float)ks[lane + D / 2];
+      av1 = vs[lane];
+      av2 = vs[lane + D / 2];
+      if (st.rope) {
+        arc = st.rope[(p * (D / 2) + lane) * 2 + 0];
+        ars = st.rope[(p * (D / 2) + lane) * 2 + 1];
+      }
+    }
   }
 
   // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
@@ -940,6 +988,17 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
         const int d = (j + LK * t) * 8 + 2 * e2;
         qp[h][t][e2] = pack_bf16(qs[h * D + d], qs[h * D + d + 1]);
       }
+  if constexpr (FUSED) {
+    if (appender) {
+      float y1 = ax1, y2 = ax2;
+      if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
+      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
+    }
+    // The tile loads below come after these stores in program order (the
+    // barrier keeps the compiler from moving the stores past them), and the
+    // memory pipeline keeps one wave's accesses to one address in order.
+    asm volatile("" ::: "memory");
+  }
 
   // -- buffer resources over this head's K and V ------------------------------
   const int64_t region = (int64_t)la.rows_alloc * D * 2;  // bytes per (b, g)
@@ -1206,7 +1265,9 @@ bool fast_decode_supported(int D, int rep) {
 template <int D, int REP>
 static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                             const void *q, int32_t n_items, const Launch &lc) {
-  hipExtLaunchKernelGGL((k_decode<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(64), 0,
+  const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
+                                     : dim3((unsigned)n_items, (unsigned)la.hkv);
+  hipExtLaunchKernelGGL((k_decode<D, REP>), grid, dim3(64), 0,
                         (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la,
                         pa, (const bf16 *)q, FusedArgs{});
 }
@@ -1215,7 +1276,9 @@ template <int D, int REP>
 static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                                   const void *q, const FusedArgs &fa, int32_t n_items,
                                   const Launch &lc) {
-  hipExtLaunchKernelGGL((k_decode<D, REP, true>), dim3((unsigned)n_items, (unsigned)la.hkv),
+  const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
+                                     : dim3((unsigned)n_items, (unsigned)la.hkv);
+  hipExtLaunchKernelGGL((k_decode<D, REP, true>), grid,
                         dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0,
                         (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q, fa);
 }

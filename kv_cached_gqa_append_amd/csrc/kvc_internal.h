@@ -76,7 +76,14 @@ struct PartialArgs {
   int32_t max_chunk;
   int32_t dec_split_keys; // keys per decode split (multiple of 32)
   int32_t pre_split_keys; // keys per chunk split (multiple of 32)
+  // Decode dispatch: grid (KV heads, items) when dec_transpose, else (items,
+  // KV heads); items in the row order dec_order[0..B) when dec_ordered
+  // (B <= kDecodeOrderMax), else in row index order.  The host sets both.
+  int32_t dec_transpose;
+  int32_t dec_ordered;
+  uint16_t dec_order[256];
 };
+constexpr int kDecodeOrderMax = 256;
 
 // The single-token step of one layer in one launch (append, decode, combine):
 // the new token's K (pre-RoPE) and V, the slot report, the output and the
