@@ -17,6 +17,13 @@ steps run first; the timed steps are bracketed by torch.cuda.synchronize().
 Kernel durations come from HIP events that each dispatch stamps at its own
 start and end on the launch stream.
 
+Further legs, each reported in its own object of the same JSON line:
+``prefill`` (the chunk-attention kernel's MFMA rate on one global layer of
+the long-context workload, prefilled in 510 chunks of 64), ``mixed`` (the
+mixed workload: B32, max_len 32768, right-padded C = 64 steps mixing one-token
+and chunk rows) and ``long_decode`` (one-token steps of the 66-layer 5:1
+long-context stack at 32k, through both entry points).
+
 Prints one JSON line.  ``--gpus N`` with N > 1 exits: this path runs on one
 GPU.  ``--cpu-baseline-seconds 0`` skips the oracle timing.
 """
@@ -331,6 +338,214 @@ def prefill_leg(dev, chunks, chunk=64):
             "tokens_per_s": round(B * chunks * chunk / dt, 1)}
 
 
+def mixed_layer_work(work, lens, n):
+    """Algorithmic work of one layer of a right-padded mixed step: query i of
+    row b (i < n_b) sits at position lens_b + i and sees lens_b + i + 1 keys.
+    Returns (attention bytes, append bytes, FLOPs of the chunk rows (n >= 2),
+    FLOPs of every row).  Attention bytes: each active row's visible K and V
+    read once per KV head, its valid queries read and outputs written.
+    Append bytes: every new k and v row read and written."""
+    s = work.dtype_bytes
+    hkv, hq, D = work.n_kv_head[0], work.n_q_head, work.head_dim
+    lens = np.asarray(lens, dtype=np.int64)
+    n = np.asarray(n, dtype=np.int64)
+    act = n > 0
+    att = int(((lens[act] + n[act]) * hkv * D * s * 2).sum()) + int(n.sum()) * hq * D * s * 2
+    app = int(n.sum()) * hkv * D * s * 2 * 2
+    keys = n * lens + n * (n + 1) // 2          # summed over the row's queries
+    fl_all = 4.0 * D * hq * float(keys.sum())
+    fl_chunk = 4.0 * D * hq * float(keys[n >= 2].sum())
+    return att, app, fl_chunk, fl_all
+
+
+def mixed_leg(dev, steps, warmup, layers):
+    """The mixed workload (B 32, Hq 32 / Hkv 8, D 128, bf16, max_len 32768,
+    right-padded C = 64 steps where half the rows decode one token and the
+    rest take n_new ~ U{0..64}; initial lengths ~ U[0, 30000]) over
+    ``layers`` full layers.  Attention GB/s = algorithmic bytes over the
+    summed decode, chunk and combine kernel time; the chunk kernel's MFMA
+    utilisation = the chunk rows' FLOPs over its own time; tokens/s = new
+    tokens over the wall time of whole steps (append + attend per layer,
+    advance)."""
+    base = wl.MIXED_B32
+    work = base.replace(n_layer=layers, n_kv_head=base.n_kv_head[:1] * layers,
+                        window=(0,) * layers)
+    lens0 = wl.initial_lens_mixed_b32(work.batch)
+    cfg = K.config_from_workload(work)
+    log(f"[bench] mixed: {layers} layers, buffer {K.kvc_nbytes(cfg, K.KVC_NB_ALLOC) / 2**30:.2f} GiB")
+    cache = K.Cache(cfg, dev)
+    fill_history(cache, work, lens0, dev)
+    B, D, C = work.batch, work.head_dim, work.max_chunk
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "mixed"))
+    mk = lambda h: torch.randn(B, C, h, D, generator=g, device=dev).to(work.torch_dtype)
+    qs = [mk(work.n_q_head) for _ in range(layers)]
+    ks = [mk(8) for _ in range(layers)]
+    vs = [mk(8) for _ in range(layers)]
+    outs = [torch.empty_like(x) for x in qs]
+    sched = [wl.n_new_mixed_b32(s, B, C) for s in range(warmup + steps)]
+
+    def run_step(n):
+        for l in range(layers):
+            cache.append(l, ks[l], vs[l], n)
+            cache.attend(l, qs[l], outs[l])
+        cache.advance()
+
+    for n in sched[:warmup]:
+        run_step(n)
+    torch.cuda.synchronize()
+    lens = np.asarray(cache.lens(), dtype=np.int64)
+    att = app = flc = fla = tokens = 0
+    for n in sched[warmup:]:
+        a, p, fc, fa = mixed_layer_work(work, lens, n)
+        att, app, flc, fla = att + a * layers, app + p * layers, flc + fc * layers, fla + fa * layers
+        tokens += int(n.sum())
+        lens = lens + n
+    K.kvc_timing_begin(cache.handle, steps * layers * 6 + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in sched[warmup:]:
+        run_step(n)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kt = K.kvc_timing_end(cache.handle)
+    assert cache.lens() == lens.tolist()
+    cache.close()
+    att_ms = sum(kt[k][0] for k in ("decode", "chunk", "combine"))
+    chunk_ms = kt["chunk"][0]
+    gbs = att / (att_ms / 1e3) / 1e9
+    tf = flc / (chunk_ms / 1e3) / 1e12 if chunk_ms > 0 else 0.0
+    kinds = {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                 "us_avg": round(v[0] * 1e3 / v[1], 2) if v[1] else None}
+             for k, v in kt.items() if v[1]}
+    log(f"[bench] mixed: {steps} steps in {dt:.3f}s ({dt * 1e3 / steps:.2f} ms/step over {layers} "
+        f"layers), {tokens / dt:.0f} new tok/s, attention kernels {gbs:.0f} GB/s, chunk kernel "
+        f"{tf:.0f} TFLOP/s")
+    log(f"[bench] mixed kernels: {json.dumps(kinds)}")
+    return {"workload": (f"mixed_b32: {layers} full layers, B{B}, Hq{work.n_q_head}/Hkv8, D{D}, "
+                         f"bf16, max_len {work.max_len}, C={C}, half the rows n_new=1 and the "
+                         f"rest U{{0..{C}}}, initial lens U[0,30000]"),
+            "steps": steps, "warmup": warmup, "ms_per_step": round(dt * 1e3 / steps, 4),
+            "tokens_per_s": round(tokens / dt, 1),
+            "attention": {"bound": "hbm", "unit": "GB/s", "achieved": round(gbs, 1),
+                          "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                          "bytes": att, "kernel_ms": round(att_ms, 3),
+                          "kernels": "k_decode<128,4> + k_chunk<128,4> + k_combine"},
+            "chunk_mfma": {"kernel": "k_chunk<128,4>", "unit": "TFLOP/s",
+                           "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                           "frac": round(tf / PEAK_BF16_TFLOPS, 4), "flops": flc},
+            "flops_all_rows": fla, "append_bytes": app, "kernels": kinds}
+
+
+def long_decode_leg(dev, steps, warmup, class_steps=8):
+    """Decode of the long-context 5:1 stack (66 layers: 55 sliding W = 512
+    rings, 11 global; B 8, Hq 64 / Hkv 8, D 128, bf16, max_len 32768) after
+    its 510-chunk prefill to 32,640 tokens, one token per row per step, timed
+    through both entry points in turn (kvc_append + kvc_attend, then
+    kvc_append_attend).  Attention GB/s = algorithmic bytes (global layers
+    read every key, ring layers min(p + 1, W) keys; queries read, outputs
+    written; for the single kernel also the new k, v rows read and written)
+    over the summed attention kernel time; a few more steps, timed a layer at
+    a time, split that into global and ring layers."""
+    work = wl.LONG_5TO1
+    cfg = K.config_from_workload(work)
+    full = K.config_from_workload(work.replace(use_ring=False))
+    nb_ring, nb_full = K.kvc_nbytes(cfg, K.KVC_NB_KV), K.kvc_nbytes(full, K.KVC_NB_KV)
+    log(f"[bench] long decode: KV {nb_ring / 2**30:.2f} GiB with rings "
+        f"({nb_full / 2**30:.2f} GiB as full caches)")
+    cache = K.Cache(cfg, dev)
+    B, D, L = work.batch, work.head_dim, work.n_layer
+    prefill = 510 * 64
+    fill_history(cache, work, np.full(B, prefill), dev)
+    assert 2 * (warmup + steps + class_steps) <= work.max_len - prefill
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "decode"))
+    mk = lambda h: torch.randn(B, 1, h, D, generator=g, device=dev).to(work.torch_dtype)
+    qs = [mk(work.n_q_head) for _ in range(L)]
+    ks = [mk(8) for _ in range(L)]
+    vs = [mk(8) for _ in range(L)]
+    outs = [torch.empty_like(x) for x in qs]
+    n = np.ones(B, dtype=np.int64)
+    s = work.dtype_bytes
+    glob = [l for l in range(L) if work.window[l] == 0]
+
+    def one_entry(fused):
+        att_kinds = ("fused",) if fused else ("decode", "combine")
+
+        def layer_bytes(l, lens):
+            vis = lens + 1 if work.window[l] == 0 else np.minimum(lens + 1, work.window[l])
+            b = int((vis * 8 * D * s * 2).sum()) + B * work.n_q_head * D * s * 2
+            return b + (B * 8 * D * s * 2 * 2 if fused else 0)
+
+        def run_layer(l):
+            if fused:
+                cache.append_attend(l, qs[l], ks[l], vs[l], n, out=outs[l])
+            else:
+                cache.append(l, ks[l], vs[l], n)
+                cache.attend(l, qs[l], outs[l])
+
+        for _ in range(warmup):
+            for l in range(L):
+                run_layer(l)
+            cache.advance()
+        torch.cuda.synchronize()
+        lens = np.asarray(cache.lens(), dtype=np.int64)
+        att = sum(layer_bytes(l, lens + i) for i in range(steps) for l in range(L))
+        K.kvc_timing_begin(cache.handle, steps * L * 4 + 16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            for l in range(L):
+                run_layer(l)
+            cache.advance()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        kt = K.kvc_timing_end(cache.handle)
+        att_ms = sum(kt[k][0] for k in att_kinds)
+        # per layer kind: each layer's launches timed on their own
+        per = {"global": [0, 0.0, 0], "ring": [0, 0.0, 0]}
+        lens = np.asarray(cache.lens(), dtype=np.int64)
+        for _ in range(class_steps):
+            for l in range(L):
+                K.kvc_timing_begin(cache.handle, 8)
+                run_layer(l)
+                t = K.kvc_timing_end(cache.handle)
+                p = per["global" if l in glob else "ring"]
+                p[0] += layer_bytes(l, lens)
+                p[1] += sum(t[k][0] for k in att_kinds)
+                p[2] += 1
+            cache.advance()
+            lens = lens + n
+        gbs = att / (att_ms / 1e3) / 1e9
+        by_kind = {k: {"layers": len(glob) if k == "global" else L - len(glob),
+                       "gbs": round(v[0] / (v[1] / 1e3) / 1e9, 1) if v[1] else None,
+                       "frac": (round(v[0] / (v[1] / 1e3) / 1e9 / PEAK_HBM_GBS, 4)
+                                if v[1] else None),
+                       "us_per_layer": round(v[1] * 1e3 / v[2], 2) if v[2] else None}
+                   for k, v in per.items()}
+        entry = "kvc_append_attend" if fused else "kvc_append+kvc_attend"
+        log(f"[bench] long decode, {entry}: {steps} steps in {dt:.3f}s "
+            f"({dt * 1e3 / steps:.3f} ms/step), {B * steps / dt:.0f} tok/s, attention kernels "
+            f"{gbs:.0f} GB/s; by layer kind {json.dumps(by_kind)}")
+        kinds = {k: {"ms_total": round(v[0], 3), "launches": v[1],
+                     "us_avg": round(v[0] * 1e3 / v[1], 2) if v[1] else None}
+                 for k, v in kt.items() if v[1]}
+        return {"entry": entry, "ms_per_step": round(dt * 1e3 / steps, 4),
+                "tokens_per_s": round(B * steps / dt, 1),
+                "attention": {"bound": "hbm", "unit": "GB/s", "achieved": round(gbs, 1),
+                              "peak": PEAK_HBM_GBS, "frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "bytes": att, "kernel_ms": round(att_ms, 3)},
+                "by_layer_kind": by_kind, "kernels": kinds}
+
+    legs = [one_entry(False), one_entry(True)]
+    cache.close()
+    return {"workload": (f"long_5to1 decode after a {prefill}-token prefill: {L} layers "
+                         f"({L - len(glob)} sliding W=512 rings, {len(glob)} global), B{B}, "
+                         f"Hq{work.n_q_head}/Hkv8, D{D}, bf16, max_len {work.max_len}"),
+            "steps": steps, "warmup": warmup, "class_steps": class_steps,
+            "kv_nbytes": {"rings": nb_ring, "full": nb_full},
+            "entries": legs}
+
 def cpu_baseline(work, lens_all, seconds):
     """Time the oracle on a bounded sample of the same workload."""
     import oracle
@@ -391,6 +606,14 @@ def main():
                     help="chunks of the prefill leg (0 skips it)")
     ap.add_argument("--prefill-only", action="store_true",
                     help="run only the prefill leg (counter runs) and print its object")
+    ap.add_argument("--mixed-steps", type=int, default=8,
+                    help="timed steps of the mixed leg (0 skips it)")
+    ap.add_argument("--mixed-layers", type=int, default=32,
+                    help="layers of the mixed leg")
+    ap.add_argument("--long-decode-steps", type=int, default=40,
+                    help="timed steps of the long-context decode leg (0 skips it)")
+    ap.add_argument("--only", choices=("mixed", "long_decode"),
+                    help="run only that leg and print its object")
     ap.add_argument("--fused", action="store_true",
                     help="headline leg through kvc_append_attend (one kernel per layer) instead "
                          "of kvc_append + kvc_attend")
@@ -430,6 +653,14 @@ def main():
     torch.cuda.set_device(dev)
     if args.prefill_only:
         print(json.dumps({"prefill": prefill_leg(dev, args.prefill_chunks)}), flush=True)
+        return
+    if args.only == "mixed":
+        print(json.dumps({"mixed": mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)}),
+              flush=True)
+        return
+    if args.only == "long_decode":
+        print(json.dumps({"long_decode": long_decode_leg(dev, args.long_decode_steps, 4)}),
+              flush=True)
         return
     work = workload_for(args.layers)
     legs = 1 if args.no_other_leg else 2
@@ -529,11 +760,21 @@ def main():
         log("[bench] copy probe: 1 GiB read + 1 GiB written")
         del src, dst
 
+    cache.close()
+    del cache, qs, ks, vs, outs
+    torch.cuda.empty_cache()
     prefill = None
     if args.prefill_chunks > 0:
-        del cache
-        torch.cuda.empty_cache()
         prefill = prefill_leg(dev, args.prefill_chunks)
+        torch.cuda.empty_cache()
+    mixed = None
+    if args.mixed_steps > 0:
+        mixed = mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)
+        torch.cuda.empty_cache()
+    long_decode = None
+    if args.long_decode_steps > 0:
+        long_decode = long_decode_leg(dev, args.long_decode_steps, 4)
+        torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_baseline_seconds > 0:
@@ -574,6 +815,8 @@ def main():
         "kernels": kinds,
         "other_entry_point": other,
         "prefill": prefill,
+        "mixed": mixed,
+        "long_decode": long_decode,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

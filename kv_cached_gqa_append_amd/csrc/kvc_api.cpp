@@ -42,6 +42,7 @@ struct kvc_cache {
   int32_t dec_occ[17] = {0};
   int32_t dec_split_fixed = 0;    // keys per split (multiple of 16); 0 = planned
   int32_t dec_waves_target = 0;   // waves per decode launch; 0 = resident slots
+  int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
   // kernel timing
@@ -134,11 +135,12 @@ int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
     tiles.push_back((hi - base + TK - 1) / TK);
     max_t = std::max(max_t, tiles.back());
   }
-  const int64_t q_min = std::max<int64_t>(1, (max_t + kvc::kDecodeSplitCap - 1) /
+  const int64_t q_cap = std::max<int64_t>(1, (max_t + kvc::kDecodeSplitCap - 1) /
                                                  kvc::kDecodeSplitCap);
   if (max_t == 0) return TK;
+  const int64_t q_min = std::max<int64_t>(q_cap, h->dec_min_tiles);
   if (h->dec_split_fixed > 0)
-    return (int32_t)(std::max<int64_t>(h->dec_split_fixed / TK, q_min) * TK);
+    return (int32_t)(std::max<int64_t>(h->dec_split_fixed / TK, q_cap) * TK);
   int64_t target = h->dec_waves_target;
   if (target <= 0) {
     int32_t &occ = h->dec_occ[la.rep <= 16 ? la.rep : 0];
@@ -309,6 +311,10 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_DECODE_WAVES")) {
     const long v = std::strtol(e, nullptr, 10);
     if (v >= 1 && v <= (1 << 24)) h->dec_waves_target = (int32_t)v;
+  }
+  if (const char *e = std::getenv("KVC_DECODE_MIN_TILES")) {
+    const long v = std::strtol(e, nullptr, 10);
+    if (v >= 1 && v <= 4096) h->dec_min_tiles = (int32_t)v;
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_LOG")) {

@@ -22,6 +22,9 @@ constexpr int kRowAlign = 32;
 constexpr int kDecodeSplitCap = 64;
 // Keys per decode tile; decode splits are whole tiles.
 constexpr int kDecodeTile = 16;
+// Fewest tiles a planned decode split takes: short rows (ring layers) are not
+// cut into splits so small that the merge costs more than the keys.
+constexpr int kDecodeSplitMinTiles = 4;
 constexpr int kChunkSplitCap = 16;
 // Query rows per chunk-attention workgroup (8 waves x 32 rows).
 constexpr int kChunkQTile = 256;
