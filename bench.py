@@ -117,7 +117,7 @@ def timed_decode_bytes(work, steps, warmup, fused=False):
     """Algorithmic bytes of each timed decode launch, in launch order (runs
     of one timed leg, --no-other-leg)."""
     per_launch = fused_kernel_bytes if fused else decode_kernel_bytes
-    lens0, sched = plan_lens(work, steps, warmup, 2)
+    lens0, sched = plan_lens(work, steps, warmup, 3)
     lens = lens0.copy()
     for s in range(warmup):
         lens = lens + sched[s]
@@ -437,12 +437,12 @@ def mixed_leg(dev, steps, warmup, layers):
             "flops_all_rows": fla, "append_bytes": app, "kernels": kinds}
 
 
-def long_decode_leg(dev, steps, warmup, class_steps=8):
+def long_decode_leg(dev, steps, warmup, class_steps=4):
     """Decode of the long-context 5:1 stack (66 layers: 55 sliding W = 512
     rings, 11 global; B 8, Hq 64 / Hkv 8, D 128, bf16, max_len 32768) after
     its 510-chunk prefill to 32,640 tokens, one token per row per step, timed
     through both entry points in turn (kvc_append + kvc_attend, then
-    kvc_append_attend).  Attention GB/s = algorithmic bytes (global layers
+    kvc_append_attend), then as replays of a captured static step.  Attention GB/s = algorithmic bytes (global layers
     read every key, ring layers min(p + 1, W) keys; queries read, outputs
     written; for the single kernel also the new k, v rows read and written)
     over the summed attention kernel time; a few more steps, timed a layer at
@@ -457,7 +457,7 @@ def long_decode_leg(dev, steps, warmup, class_steps=8):
     B, D, L = work.batch, work.head_dim, work.n_layer
     prefill = 510 * 64
     fill_history(cache, work, np.full(B, prefill), dev)
-    assert 2 * (warmup + steps + class_steps) <= work.max_len - prefill
+    assert 2 * (warmup + steps + class_steps) + warmup + steps <= work.max_len - prefill
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed_of(work.name, "decode"))
     mk = lambda h: torch.randn(B, 1, h, D, generator=g, device=dev).to(work.torch_dtype)
@@ -538,6 +538,19 @@ def long_decode_leg(dev, steps, warmup, class_steps=8):
                 "by_layer_kind": by_kind, "kernels": kinds}
 
     legs = [one_entry(False), one_entry(True)]
+
+    def graph_step_bytes(lens, nn):
+        tot = 0
+        for l in range(L):
+            vis = lens + 1 if work.window[l] == 0 else np.minimum(lens + 1, work.window[l])
+            tot += int((vis * 8 * D * s * 2).sum()) + B * (work.n_q_head * D * s * 2 + 8 * D * s * 4)
+        return tot
+
+    gl = graph_leg(cache, work, qs, ks, vs, [n] * (warmup + steps), warmup, steps,
+                   graph_step_bytes)
+    log(f"[bench] long decode, graph replays: {gl['ms_per_step']:.3f} ms/step, "
+        f"{gl['tokens_per_s']:.0f} tok/s, whole-step {gl['value']:.0f} GB/s")
+    legs.append(gl)
     cache.close()
     return {"workload": (f"long_5to1 decode after a {prefill}-token prefill: {L} layers "
                          f"({L - len(glob)} sliding W=512 rings, {len(glob)} global), B{B}, "
@@ -545,6 +558,44 @@ def long_decode_leg(dev, steps, warmup, class_steps=8):
             "steps": steps, "warmup": warmup, "class_steps": class_steps,
             "kv_nbytes": {"rings": nb_ring, "full": nb_full},
             "entries": legs}
+
+def graph_leg(cache, work, qs, ks, vs, sched, warmup, steps, step_bytes_fn):
+    """One-token steps replayed from a captured HIP graph (kvc_static_begin,
+    kvc_append_attend per layer, kvc_advance; counts copied into the graph's
+    device input before each replay).  Whole-step figures only: kernel
+    timing events cannot be recorded inside a replay."""
+    dev = cache.buffer.device
+    cache.sync_lens()
+    g = K.StaticDecodeGraph(cache, fused=True)
+    for l in range(work.n_layer):
+        g.q[l].copy_(qs[l])
+        g.k[l].copy_(ks[l])
+        g.v[l].copy_(vs[l])
+    n_dev = torch.tensor(np.stack(sched[:warmup + steps]), dtype=torch.int32, device=dev)
+    for s in range(warmup):
+        g.n_new.copy_(n_dev[s])
+        g.replay()
+    torch.cuda.synchronize()
+    lens = cache.device_lens().cpu().numpy().astype(np.int64)
+    sbytes, tokens = 0, 0
+    for n in sched[warmup:warmup + steps]:
+        sbytes += step_bytes_fn(lens, n)
+        tokens += int(n.sum())
+        lens = lens + n
+    t0 = time.perf_counter()
+    for s in range(warmup, warmup + steps):
+        g.n_new.copy_(n_dev[s])
+        g.replay()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    cache.sync_lens()
+    assert cache.lens() == lens.tolist()
+    assert cache.static_status() == 0
+    del g
+    return {"entry": "static step in a HIP graph (kvc_static_begin + kvc_append_attend)",
+            "value": round(sbytes / dt / 1e9, 1), "unit": "GB/s",
+            "ms_per_step": round(dt * 1e3 / steps, 4),
+            "tokens_per_s": round(tokens / dt, 1), "steps": steps, "warmup": warmup}
 
 def cpu_baseline(work, lens_all, seconds):
     """Time the oracle on a bounded sample of the same workload."""
@@ -610,7 +661,7 @@ def main():
                     help="timed steps of the mixed leg (0 skips it)")
     ap.add_argument("--mixed-layers", type=int, default=32,
                     help="layers of the mixed leg")
-    ap.add_argument("--long-decode-steps", type=int, default=40,
+    ap.add_argument("--long-decode-steps", type=int, default=32,
                     help="timed steps of the long-context decode leg (0 skips it)")
     ap.add_argument("--only", choices=("mixed", "long_decode"),
                     help="run only that leg and print its object")
@@ -664,9 +715,9 @@ def main():
         return
     work = workload_for(args.layers)
     legs = 1 if args.no_other_leg else 2
-    # lengths clipped for two legs either way, so runs with and without the
-    # second leg time the same workload
-    lens0, schedule = plan_lens(work, args.steps, args.warmup, 2)
+    # lengths clipped for three legs either way, so runs with and without the
+    # other legs time the same workload
+    lens0, schedule = plan_lens(work, args.steps, args.warmup, 3)
     cfg = K.config_from_workload(work)
     log(f"[bench] buffer {K.kvc_nbytes(cfg, K.KVC_NB_ALLOC) / 2**30:.2f} GiB "
         f"(KV {K.kvc_nbytes(cfg, K.KVC_NB_KV) / 2**30:.2f} GiB)")
@@ -737,7 +788,7 @@ def main():
     head = timed_leg(args.fused, schedule[:per_leg])
     other = None
     if legs == 2:
-        o = timed_leg(not args.fused, schedule[per_leg:])
+        o = timed_leg(not args.fused, schedule[per_leg:2 * per_leg])
         other = {"entry": "kvc_append_attend" if o["fused"] else "kvc_append+kvc_attend",
                  "value": round(o["value"], 1), "unit": "GB/s",
                  "ms_per_step": round(o["ms_step"], 4),
@@ -747,6 +798,12 @@ def main():
                  "kernel_frac": round(o["achieved"] / PEAK_HBM_GBS, 4),
                  "avg_launch_us": round(o["dec_us"], 2) if o["dec_us"] else None,
                  "kernels": o["kinds"]}
+    graph = None
+    if legs == 2:
+        graph = graph_leg(cache, work, qs, ks, vs, schedule[2 * per_leg:], args.warmup, args.steps,
+                          lambda lens, n: step_bytes(lens, n, work))
+        log(f"[bench] graph replays: {graph['ms_per_step']:.3f} ms/step, "
+            f"{graph['tokens_per_s']:.0f} tok/s, whole-step {graph['value']:.0f} GB/s")
     fused = head["fused"]
     dt, ms_step, tokens, value = head["dt"], head["ms_step"], head["tokens"], head["value"]
     achieved, kbytes, dec_n, kinds = head["achieved"], head["kbytes"], head["dec_n"], head["kinds"]
@@ -814,6 +871,7 @@ def main():
                      "bytes_per_launch": int(kbytes / max(dec_n, 1))},
         "kernels": kinds,
         "other_entry_point": other,
+        "graph": graph,
         "prefill": prefill,
         "mixed": mixed,
         "long_decode": long_decode,

@@ -159,8 +159,49 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k,
  * Every layer must have been appended and attended (else KVC_E_STATE). */
 int kvc_advance(kvc_t *h, void *stream);
 
-/* Copy the host mirror of the row lengths into lens_host[B]. */
+/* Copy the host mirror of the row lengths into lens_host[B].  KVC_E_STATE
+ * while the mirror is behind the device (after a static step, until
+ * kvc_sync_lens). */
 int kvc_lens(const kvc_t *h, int32_t *lens_host);
+
+/* Static one-token steps: a step whose work does not depend on anything the
+ * host reads, so that it can be captured once in a HIP graph and replayed
+ * (tinyllm "kv_cache.py", SlotKVCache: fixed shapes for a CUDA-graph decode
+ * step; its end_step splits into the device update a replay runs and a host
+ * update the caller runs after each replay).
+ *
+ *     kvc_static_begin(h, n_new_dev, s);
+ *     for each layer l: kvc_append_attend(h, l, q, k, v, NULL, 1, slot, out, s);
+ *                       (or kvc_append(.., NULL, 1, ..) + kvc_attend)
+ *     kvc_advance(h, s);
+ *
+ * kvc_static_begin enqueues one small kernel that reads the step's token
+ * counts from device memory (n_new_dev: int32 [B], each 0 or 1, read when the
+ * kernel runs, so a replay uses the values there at that time), checks them
+ * against the device row lengths, and plans every layer's decode splits on
+ * the device: the plan is the one the host makes for an eager step, so a
+ * static step gives the same bits.  Launch grids are fixed bounds; waves
+ * past the planned work exit at once.  If any count is outside {0, 1}
+ * (KVC_STATIC_BAD_COUNT) or any row would pass max_len (KVC_STATIC_FULL), the
+ * whole step runs with every count 0 (nothing appended, every output zero,
+ * lengths unchanged) and the reason is or-ed into sticky device flags.
+ * Within the step, appends pass n_new_host = NULL and C = 1; kvc_advance
+ * updates the device lengths only and leaves the host mirror stale: eager
+ * appends, kvc_reset and kvc_lens return KVC_E_STATE until kvc_sync_lens.
+ * Kernel timing must be off while a step is being captured.  No call of a
+ * static step allocates, frees, synchronises or copies through host memory;
+ * all of them are safe under stream capture. */
+enum { KVC_STATIC_BAD_COUNT = 1, KVC_STATIC_FULL = 2 };
+int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream);
+
+/* Read and clear the sticky flags of static steps (bits KVC_STATIC_*):
+ * copies them to *flags_host, waits for `stream`, then enqueues their
+ * clearing.  Not inside a step. */
+int kvc_static_status(kvc_t *h, int32_t *flags_host, void *stream);
+
+/* Refresh the host mirror of the row lengths from the device (waits for
+ * `stream`).  Not inside a step. */
+int kvc_sync_lens(kvc_t *h, void *stream);
 
 /* Where layer `layer` lives inside the device buffer (for inspection).
  * K rows are row-major: byte offset k_offset + ((b*Hkv + g)*rows_alloc + r)*D*s.

@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(HERE, "libkvc.so")
 KVC_OK, KVC_E_ARG, KVC_E_FULL, KVC_E_DTYPE, KVC_E_STATE, KVC_E_HIP = 0, -1, -2, -3, -4, -5
 KVC_F32, KVC_BF16 = 0, 1
 KVC_NB_KV, KVC_NB_ALLOC = 0, 1
+KVC_STATIC_BAD_COUNT, KVC_STATIC_FULL = 1, 2
 KERNEL_KINDS = ("append", "decode", "chunk", "combine", "commit", "generic", "fused")
 
 _DTYPES = {torch.float32: KVC_F32, torch.bfloat16: KVC_BF16}
@@ -117,6 +118,12 @@ def lib():
         L.kvc_advance.restype = ctypes.c_int
         L.kvc_lens.argtypes = [VP, P(I32)]
         L.kvc_lens.restype = ctypes.c_int
+        L.kvc_static_begin.argtypes = [VP, VP, VP]
+        L.kvc_static_begin.restype = ctypes.c_int
+        L.kvc_static_status.argtypes = [VP, P(I32), VP]
+        L.kvc_static_status.restype = ctypes.c_int
+        L.kvc_sync_lens.argtypes = [VP, VP]
+        L.kvc_sync_lens.restype = ctypes.c_int
         L.kvc_layer_layout.argtypes = [VP, I32, P(KvcLayerInfo)]
         L.kvc_layer_layout.restype = ctypes.c_int
         L.kvc_buffer_info.argtypes = [VP, P(KvcBufferInfo)]
@@ -200,6 +207,8 @@ def kvc_destroy(h) -> None:
 
 
 def _rows_array(values):
+    if values is None:  # a static step: the counts are on the device
+        return None, 0
     vals = [int(x) for x in values]
     return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals)
 
@@ -236,6 +245,22 @@ def kvc_append_attend(h, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.
 
 def kvc_advance(h, stream=None) -> None:
     _check(lib().kvc_advance(h, _stream_handle(stream)), "kvc_advance")
+
+
+def kvc_static_begin(h, n_new_dev: torch.Tensor, stream=None) -> None:
+    _check(lib().kvc_static_begin(h, ctypes.c_void_p(n_new_dev.data_ptr()),
+                                  _stream_handle(stream)), "kvc_static_begin")
+
+
+def kvc_static_status(h, stream=None) -> int:
+    v = ctypes.c_int32(0)
+    _check(lib().kvc_static_status(h, ctypes.byref(v), _stream_handle(stream)),
+           "kvc_static_status")
+    return int(v.value)
+
+
+def kvc_sync_lens(h, stream=None) -> None:
+    _check(lib().kvc_sync_lens(h, _stream_handle(stream)), "kvc_sync_lens")
 
 
 def kvc_lens(h, batch: int):
@@ -321,7 +346,8 @@ class Cache:
             raise ValueError(f"{name} must be contiguous")
 
     def append(self, layer, k, v, n_new, slot_out=None, stream=None):
-        if len(n_new) != self.batch:
+        """n_new: host counts [B], or None inside a static step."""
+        if n_new is not None and len(n_new) != self.batch:
             raise ValueError(f"n_new has {len(n_new)} entries, cache batch is {self.batch}")
         C = int(k.shape[1])
         hk = self.n_kv_head[layer]
@@ -343,8 +369,9 @@ class Cache:
 
     def append_attend(self, layer, q, k, v, n_new, out=None, slot_out=None, stream=None):
         """append() then attend() of one layer in one call (one kernel for a
-        one-token bf16 step)."""
-        if len(n_new) != self.batch:
+        one-token bf16 step).  n_new: host counts [B], or None inside a
+        static step."""
+        if n_new is not None and len(n_new) != self.batch:
             raise ValueError(f"n_new has {len(n_new)} entries, cache batch is {self.batch}")
         C = int(k.shape[1])
         hk = self.n_kv_head[layer]
@@ -362,6 +389,23 @@ class Cache:
 
     def advance(self, stream=None):
         kvc_advance(self.handle, stream)
+
+    def static_begin(self, n_new_dev: torch.Tensor, stream=None):
+        """Begin a static one-token step whose counts (int32 [B], 0 or 1) are
+        read from ``n_new_dev`` when the step runs."""
+        if (n_new_dev.dtype != torch.int32 or n_new_dev.numel() != self.batch
+                or not n_new_dev.is_contiguous() or n_new_dev.device != self.buffer.device):
+            raise ValueError(f"n_new_dev must be a contiguous int32 tensor of {self.batch} "
+                             f"entries on {self.buffer.device}")
+        kvc_static_begin(self.handle, n_new_dev, stream)
+
+    def static_status(self, stream=None) -> int:
+        """Read and clear the sticky flags of static steps (KVC_STATIC_*)."""
+        return kvc_static_status(self.handle, stream)
+
+    def sync_lens(self, stream=None):
+        """Refresh the host mirror of the row lengths from the device."""
+        kvc_sync_lens(self.handle, stream)
 
     def reset(self, rows, stream=None):
         kvc_reset(self.handle, rows, stream)
@@ -409,3 +453,47 @@ class Cache:
         s = self._elem()
         return self.buffer[info.v_offset: info.v_offset + n * s].view(self.dtype).view(
             self.batch, info.n_kv_head, info.rows_alloc // 16, self.head_dim, 16)
+
+
+class StaticDecodeGraph:
+    """A one-token step over every layer of ``cache``, captured once in a HIP
+    graph (through ``torch.cuda.CUDAGraph``) and replayed.
+
+    The step reads its inputs from tensors this object owns: ``n_new`` (int32
+    [B], 0 or 1 per row), ``q[l]`` (B, 1, Hq, D), ``k[l]`` and ``v[l]``
+    (B, 1, Hkv_l, D); it writes ``out[l]`` and, with ``slots``, ``slot[l]``
+    (int32 (B, 1)).  Fill the inputs, call ``replay()``; each replay is one
+    kvc_static_begin, every layer's kvc_append_attend (``fused``) or
+    kvc_append + kvc_attend, and kvc_advance.  The host mirror of the row
+    lengths is stale after a replay: call ``cache.sync_lens()`` before eager
+    steps.
+    """
+
+    def __init__(self, cache: "Cache", fused=True, slots=False):
+        dev = cache.buffer.device
+        B, Hq, D = cache.batch, cache.n_q_head, cache.head_dim
+        self.cache = cache
+        self.n_new = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.q = [torch.zeros(B, 1, Hq, D, dtype=cache.dtype, device=dev)
+                  for _ in range(cache.n_layer)]
+        self.k = [torch.zeros(B, 1, h, D, dtype=cache.dtype, device=dev) for h in cache.n_kv_head]
+        self.v = [torch.zeros(B, 1, h, D, dtype=cache.dtype, device=dev) for h in cache.n_kv_head]
+        self.out = [torch.zeros_like(x) for x in self.q]
+        self.slot = ([torch.zeros(B, 1, dtype=torch.int32, device=dev)
+                      for _ in range(cache.n_layer)] if slots else [None] * cache.n_layer)
+        torch.cuda.synchronize(dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            cache.static_begin(self.n_new)
+            for l in range(cache.n_layer):
+                if fused:
+                    cache.append_attend(l, self.q[l], self.k[l], self.v[l], None, out=self.out[l],
+                                        slot_out=self.slot[l])
+                else:
+                    cache.append(l, self.k[l], self.v[l], None, slot_out=self.slot[l])
+                    cache.attend(l, self.q[l], self.out[l])
+            cache.advance()
+
+    def replay(self):
+        self.graph.replay()
+

@@ -107,6 +107,19 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Launch on lc's stream.  With timing events the dispatch itself stamps them
+// (hipExtLaunchKernel); without, a plain launch, which stream capture records
+// as a kernel node of the graph.
+template <typename... KArgs, typename... Args>
+static void launch_kernel(void (*kern)(KArgs...), dim3 grid, dim3 block, const Launch &lc,
+                          Args... args) {
+  if (lc.t0 || lc.t1)
+    hipExtLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0,
+                          (hipEvent_t)lc.t1, 0, args...);
+  else
+    hipLaunchKernelGGL(kern, grid, block, 0, (hipStream_t)lc.stream, args...);
+}
+
 // Element pointers.
 template <typename T>
 __device__ __forceinline__ T *k_row(char *base, int64_t bg, int rows_alloc, int64_t r, int D) {
@@ -199,6 +212,120 @@ int launch_advance(int32_t *lens, const int32_t *n_new, int32_t B, void *stream)
 }
 
 // ---------------------------------------------------------------------------
+// Static one-token step prologue: one wave per layer class.  Every wave
+// checks the caller's counts against the device lengths (a count outside
+// {0, 1} or a row that would pass max_len rejects the whole step: every
+// count becomes 0, so nothing is appended and every output is zero, and the
+// reason is or-ed into the sticky flags); wave 0 publishes the counts.  Each
+// wave then plans its class's decode splits from the device lengths, exactly
+// as the host planner does for an eager step (smallest split in tiles, not
+// below the class's floor nor below 1/64 of the longest row, whose waves plus
+// the idle rows' items fit one round), and the dispatch order (rows by tiles
+// per split, descending; ties by row).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t wave_sum_i64(int64_t x) {
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const int y = __shfl_xor(x, o);
+    x = y > x ? y : x;
+  }
+  return x;
+}
+__device__ __forceinline__ int wave_or_i(int x) {
+  for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o);
+  return x;
+}
+
+__global__ __launch_bounds__(64) void k_static_begin(StaticBeginArgs a) {
+  __shared__ int32_t tl[kDecodeOrderMax], nsl[kDecodeOrderMax];
+  const int lane = threadIdx.x, c = blockIdx.x;
+  const StaticClass cl = a.cls[c];
+  int bad = 0;
+  for (int b = lane; b < a.B; b += 64) {
+    const int n = a.n_src[b];
+    if (n < 0 || n > 1)
+      bad |= kStaticBadCount;
+    else if ((int64_t)a.lens[b] + n > a.max_len)
+      bad |= kStaticFull;
+  }
+  bad = __builtin_amdgcn_readfirstlane(wave_or_i(bad));
+  if (c == 0) {
+    for (int b = lane; b < a.B; b += 64) a.n_new[b] = bad ? 0 : a.n_src[b];
+    if (lane == 0 && bad) a.flags[0] = a.flags[0] | bad;
+  }
+  LayerArgs la{};
+  la.window = cl.window;
+  la.ring = cl.ring;
+  auto tiles = [&](int b) -> int {  // tiles of a decoding row, 0 for an idle one
+    if (bad || a.n_src[b] != 1) return 0;
+    int64_t base, lo, hi;
+    decode_span_dev(la, a.lens[b], &base, &lo, &hi);
+    return (int)cdiv(hi - base, kDecodeTile);
+  };
+  int max_t = 0, idle = 0;
+  for (int b = lane; b < a.B; b += 64) {
+    const int t = tiles(b);
+    max_t = t > max_t ? t : max_t;
+    idle += (bad || a.n_src[b] != 1) ? 1 : 0;
+  }
+  max_t = __builtin_amdgcn_readfirstlane(wave_max_i(max_t));
+  idle = __builtin_amdgcn_readfirstlane((int)wave_sum_i64(idle));
+  int q = 1;
+  if (max_t > 0) {
+    const int q_cap = (int)cdiv(max_t, kDecodeSplitCap);
+    if (cl.fixed_q > 0) {
+      q = cl.fixed_q > q_cap ? cl.fixed_q : q_cap;
+    } else {
+      int64_t target = (int64_t)cl.target - (int64_t)idle * cl.hkv;
+      if (target < 1) target = 1;
+      int lo = q_cap > cl.min_tiles ? q_cap : cl.min_tiles;
+      int hi = lo > max_t ? lo : max_t;
+      while (lo < hi) {
+        const int mid = (lo + hi) / 2;
+        int64_t w = 0;
+        for (int b = lane; b < a.B; b += 64) w += cdiv(tiles(b), mid);
+        w = wave_sum_i64(w) * cl.hkv;
+        if (__builtin_amdgcn_readfirstlane((int)(w <= target)))
+          hi = mid;
+        else
+          lo = mid + 1;
+      }
+      q = lo;
+    }
+  }
+  if (lane == 0) a.plan_sk[c] = q * kDecodeTile;
+  if (a.plan_order && a.B <= kDecodeOrderMax) {
+    // per = tiles / splits (0 for idle rows); rank = rows with a larger per,
+    // plus rows before this one with an equal per
+    for (int b = lane; b < a.B; b += 64) {
+      const int t = tiles(b);
+      tl[b] = t;
+      nsl[b] = t > 0 ? (int)cdiv(t, q) : 1;
+    }
+    __syncthreads();
+    for (int b = lane; b < a.B; b += 64) {
+      const int64_t t = tl[b], ns = nsl[b];
+      int rank = 0;
+      for (int o = 0; o < a.B; ++o) {
+        const int64_t lhs = (int64_t)tl[o] * ns, rhs = t * nsl[o];
+        rank += (lhs > rhs || (lhs == rhs && o < b)) ? 1 : 0;
+      }
+      a.plan_order[(int64_t)c * a.B + rank] = (uint16_t)b;
+    }
+  }
+}
+
+int launch_static_begin(const StaticBeginArgs &a, void *stream) {
+  if (a.n_class < 1 || a.n_class > kStaticClassMax) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_static_begin, dim3((unsigned)a.n_class), dim3(64), 0, (hipStream_t)stream,
+                     a);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // fused RoPE + append: one wave per (row b, token i, KV head g)
 // ---------------------------------------------------------------------------
 template <typename T>
@@ -285,11 +412,9 @@ int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void
                   const void *v, int32_t *slot_out, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * la.hkv;
   if (dtype == KVC_F32)
-    hipExtLaunchKernelGGL(k_append<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la, (const float *)k, (const float *)v, slot_out);
+    launch_kernel(k_append<float>, dim3((unsigned)rows), dim3(64), lc, st, la, (const float *)k, (const float *)v, slot_out);
   else
-    hipExtLaunchKernelGGL(k_append<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st,
-                       la, (const bf16 *)k, (const bf16 *)v, slot_out);
+    launch_kernel(k_append<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la, (const bf16 *)k, (const bf16 *)v, slot_out);
   return (int)hipGetLastError();
 }
 
@@ -325,11 +450,9 @@ __global__ __launch_bounds__(64) void k_commit(StepArgs st, LayerArgs la) {
 int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * la.hkv;
   if (dtype == KVC_F32)
-    hipExtLaunchKernelGGL(k_commit<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la);
+    launch_kernel(k_commit<float>, dim3((unsigned)rows), dim3(64), lc, st, la);
   else
-    hipExtLaunchKernelGGL(k_commit<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st,
-                       la);
+    launch_kernel(k_commit<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la);
   return (int)hipGetLastError();
 }
 
@@ -450,11 +573,9 @@ int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const voi
                    const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * st.Hq;
   if (dtype == KVC_F32)
-    hipExtLaunchKernelGGL(k_generic<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la, (const float *)q, (float *)out);
+    launch_kernel(k_generic<float>, dim3((unsigned)rows), dim3(64), lc, st, la, (const float *)q, (float *)out);
   else
-    hipExtLaunchKernelGGL(k_generic<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la, (const bf16 *)q, (bf16 *)out);
+    launch_kernel(k_generic<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la, (const bf16 *)q, (bf16 *)out);
   return (int)hipGetLastError();
 }
 
@@ -890,10 +1011,12 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const int lane = threadIdx.x;
   const int g = pa.dec_transpose ? blockIdx.x : blockIdx.y;
   const int item = pa.dec_transpose ? blockIdx.y : blockIdx.x;
-  const int SK = pa.dec_split_keys;
+  const int SK = __builtin_amdgcn_readfirstlane(pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
   int b;
   int64_t split64;
-  auto row_at = [&](int r) { return pa.dec_ordered ? (int)pa.dec_order[r] : r; };
+  auto row_at = [&](int r) {
+    return pa.dec_order_dev ? (int)pa.dec_order_dev[r] : pa.dec_ordered ? (int)pa.dec_order[r] : r;
+  };
   find_item(
       st.B, item,
       [&](int r0) -> int {
@@ -1267,9 +1390,7 @@ static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const Parti
                             const void *q, int32_t n_items, const Launch &lc) {
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
                                      : dim3((unsigned)n_items, (unsigned)la.hkv);
-  hipExtLaunchKernelGGL((k_decode<D, REP>), grid, dim3(64), 0,
-                        (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la,
-                        pa, (const bf16 *)q, FusedArgs{});
+  launch_kernel((k_decode<D, REP>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, FusedArgs{});
 }
 
 template <int D, int REP>
@@ -1278,9 +1399,7 @@ static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const
                                   const Launch &lc) {
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
                                      : dim3((unsigned)n_items, (unsigned)la.hkv);
-  hipExtLaunchKernelGGL((k_decode<D, REP, true>), grid,
-                        dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0,
-                        (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q, fa);
+  launch_kernel((k_decode<D, REP, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, fa);
 }
 
 template <int D, int REP>
@@ -1741,8 +1860,7 @@ bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && re
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, const Launch &lc) {
-  hipExtLaunchKernelGGL((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(512), 0,
-                     (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0, st, la, pa, (const bf16 *)q);
+  launch_kernel((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(512), lc, st, la, pa, (const bf16 *)q);
 }
 
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,
@@ -1786,7 +1904,7 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
   if (n == 1) {
     int64_t base, lo, hi;
     decode_span_dev(la, L, &base, &lo, &hi);
-    ns = (int)cdiv(hi - base, pa.dec_split_keys);
+    ns = (int)cdiv(hi - base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
     const int64_t s0 = ((int64_t)b * st.Hq + h) * kDecodeSplitCap;
     ml = pa.dml + s0 * 2;
     os = pa.dout + s0 * D;
@@ -1833,11 +1951,9 @@ int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const Par
                    void *out, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * st.Hq;
   if (dtype == KVC_F32)
-    hipExtLaunchKernelGGL(k_combine<float>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la, pa, (float *)out);
+    launch_kernel(k_combine<float>, dim3((unsigned)rows), dim3(64), lc, st, la, pa, (float *)out);
   else
-    hipExtLaunchKernelGGL(k_combine<bf16>, dim3((unsigned)rows), dim3(64), 0, (hipStream_t)lc.stream, (hipEvent_t)lc.t0, (hipEvent_t)lc.t1, 0,
-                       st, la, pa, (bf16 *)out);
+    launch_kernel(k_combine<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la, pa, (bf16 *)out);
   return (int)hipGetLastError();
 }
 

@@ -45,6 +45,11 @@ struct kvc_cache {
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
+  // static one-token steps (counts in device memory, planned on the device)
+  bool step_static = false;           // the current step is one
+  bool lens_stale = false;            // a static step advanced the device lengths only
+  std::vector<int32_t> layer_class;   // layer -> plan class
+  std::vector<kvc::StaticClass> classes;
   // kernel timing
   bool timing = false;
   std::vector<hipEvent_t> ev;      // 2 per launch
@@ -292,6 +297,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (hipMemsetAsync(h->base + h->lay.lens_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.nnew_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.cnt_off, 0, h->lay.cnt_bytes, s) != hipSuccess ||
+      hipMemsetAsync(h->base + h->lay.flags_off, 0, 4, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {
     delete h;
     return KVC_E_HIP;
@@ -317,6 +323,23 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     if (v >= 1 && v <= 4096) h->dec_min_tiles = (int32_t)v;
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
+  // Plan classes of static steps: layers with the same KV heads, window and layout.
+  for (int32_t l = 0; l < cfg->n_layer; ++l) {
+    const LayerLayout &L = h->lay.layers[l];
+    int32_t c = 0;
+    while (c < (int32_t)h->classes.size() &&
+           !(h->classes[c].hkv == L.hkv && h->classes[c].window == L.window &&
+             h->classes[c].ring == L.ring))
+      ++c;
+    if (c == (int32_t)h->classes.size()) {
+      kvc::StaticClass sc{};
+      sc.hkv = L.hkv;
+      sc.window = L.window;
+      sc.ring = L.ring;
+      h->classes.push_back(sc);
+    }
+    h->layer_class.push_back(c);
+  }
   if (const char *e = std::getenv("KVC_LOG")) {
     h->log_level = std::atoi(e);
     if (h->log_level >= 1)
@@ -336,7 +359,7 @@ void kvc_destroy(kvc_t *h) {
 
 int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream) {
   if (!h || n_rows < 0 || (n_rows > 0 && !rows_host)) return KVC_E_ARG;
-  if (h->in_step) return KVC_E_STATE;
+  if (h->in_step || h->lens_stale) return KVC_E_STATE;
   for (int32_t i = 0; i < n_rows; ++i)
     if (rows_host[i] < 0 || rows_host[i] >= h->cfg.batch) return KVC_E_ARG;
   if (n_rows == 0) return KVC_OK;
@@ -357,6 +380,13 @@ int begin_append(kvc_t *h, int32_t layer, const int32_t *n_new_host, int32_t C, 
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   if (C < 1 || C > h->cfg.max_chunk) return KVC_E_ARG;
   const int32_t B = h->cfg.batch;
+  if (h->step_static) {  // the counts are on the device; no host copy of them
+    if (n_new_host || C != 1) return KVC_E_ARG;
+    if (h->appended[layer]) return KVC_E_STATE;
+    return use_device(h) ? KVC_OK : KVC_E_HIP;
+  }
+  if (!n_new_host) return KVC_E_ARG;
+  if (h->lens_stale) return KVC_E_STATE;
   if (!h->in_step) {
     for (int32_t b = 0; b < B; ++b)
       if (n_new_host[b] < 0 || n_new_host[b] > C) return KVC_E_ARG;
@@ -392,11 +422,42 @@ kvc::PartialArgs partial_args(const kvc_t *h) {
   return pa;
 }
 
+// Target waves of one decode round for a layer: resident decode waves per CU
+// (queried once per query-heads-per-KV-head) times the CUs, unless overridden.
+int64_t decode_wave_target(kvc_t *h, const kvc::LayerArgs &la, int D) {
+  if (h->dec_waves_target > 0) return h->dec_waves_target;
+  int32_t &occ = h->dec_occ[la.rep <= 16 ? la.rep : 0];
+  if (occ == 0) occ = std::max(1, kvc::decode_waves_per_cu(D, la.rep));
+  return (int64_t)h->n_cu * occ;
+}
+
+// A static step's decode plan for a layer: the class's split length and row
+// order from the device table, and a grid that bounds the items any counts
+// and lengths can produce.  The plan is a split count per row whose waves
+// plus the idle rows' items fit one round, or one split per row when none
+// does (then at most B items), and never more than kDecodeSplitCap splits
+// per row.
+int32_t static_plan(const kvc_t *h, int32_t layer, kvc::PartialArgs *pa) {
+  const int32_t c = h->layer_class[layer];
+  const kvc::StaticClass &cl = h->classes[c];
+  pa->dec_plan = reinterpret_cast<const int32_t *>(h->base + h->lay.plan_off) + c;
+  pa->dec_order_dev =
+      h->cfg.batch <= kvc::kDecodeOrderMax
+          ? reinterpret_cast<const uint16_t *>(h->base + h->lay.plan_off + 4 * h->cfg.n_layer) +
+                (int64_t)c * h->cfg.batch
+          : nullptr;
+  pa->dec_ordered = 0;
+  const int64_t B = h->cfg.batch;
+  int64_t items = cl.fixed_q > 0 ? B * kvc::kDecodeSplitCap
+                                 : std::max<int64_t>((cl.target + cl.hkv - 1) / cl.hkv, B);
+  return (int32_t)std::min<int64_t>(items, B * kvc::kDecodeSplitCap);
+}
+
 }  // namespace
 
 int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
                const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *stream) {
-  if (!h || !k || !v || !n_new_host) return KVC_E_ARG;
+  if (!h || !k || !v) return KVC_E_ARG;
   const int rc = begin_append(h, layer, n_new_host, C, stream);
   if (rc != KVC_OK) return rc;
   const kvc::StepArgs st = step_args(h);
@@ -416,13 +477,22 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
   const kvc::LayerArgs la = layer_args(h, layer);
   const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
   bool staged = false;
-  for (int32_t b = 0; b < B; ++b) staged |= (h->n_new[b] >= 2);
+  if (!h->step_static)
+    for (int32_t b = 0; b < B; ++b) staged |= (h->n_new[b] >= 2);
   staged = staged && la.ring && la.sk;
 
   const bool fast = h->cfg.dtype == KVC_BF16 && kvc::fast_decode_supported(D, la.rep) &&
                     kvc::fast_prefill_supported(D, la.rep);
   int err = 0;
-  if (!fast) {
+  if (fast && h->step_static) {
+    // one-token rows only; the plan is on the device
+    kvc::PartialArgs pa = partial_args(h);
+    const int32_t items = static_plan(h, layer, &pa);
+    err = kvc::launch_decode(st, la, pa, q, items, launch_on(h, KVC_K_DECODE, stream));
+    if (err) return KVC_E_HIP;
+    err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
+    if (err) return KVC_E_HIP;
+  } else if (!fast) {
     err = kvc::launch_generic(h->cfg.dtype, st, la, q, out, launch_on(h, KVC_K_GENERIC, stream));
     if (err) return KVC_E_HIP;
   } else {
@@ -483,7 +553,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
 int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, const void *v,
                       const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev, void *out,
                       void *stream) {
-  if (!h || !q || !k || !v || !out || !n_new_host) return KVC_E_ARG;
+  if (!h || !q || !k || !v || !out) return KVC_E_ARG;
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   const kvc::LayerArgs la = layer_args(h, layer);
   const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
@@ -498,21 +568,25 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   if (rc != KVC_OK) return rc;
   const kvc::StepArgs st = step_args(h);
   kvc::PartialArgs pa = partial_args(h);
-  pa.dec_split_keys = decode_split_keys(h, la, D);
-  decode_order(h, la, &pa);
   int64_t items = 0;
-  for (int32_t b = 0; b < B; ++b) {
-    if (h->n_new[b] == 1) {
-      int64_t base, hi;
-      decode_span(la, h->lens_host[b], &base, &hi);
-      items += ceil_div(hi - base, pa.dec_split_keys);
-    } else {
-      items += 1;  // idle row: its padded token and zero outputs
+  if (h->step_static) {
+    items = static_plan(h, layer, &pa);
+  } else {
+    pa.dec_split_keys = decode_split_keys(h, la, D);
+    decode_order(h, la, &pa);
+    for (int32_t b = 0; b < B; ++b) {
+      if (h->n_new[b] == 1) {
+        int64_t base, hi;
+        decode_span(la, h->lens_host[b], &base, &hi);
+        items += ceil_div(hi - base, pa.dec_split_keys);
+      } else {
+        items += 1;  // idle row: its padded token and zero outputs
+      }
     }
+    if (h->log_level >= 2 && layer == 0)
+      std::fprintf(stderr, "[kvc] fused decode plan: %d keys per split, %lld waves\n",
+                   pa.dec_split_keys, (long long)items * la.hkv);
   }
-  if (h->log_level >= 2 && layer == 0)
-    std::fprintf(stderr, "[kvc] fused decode plan: %d keys per split, %lld waves\n",
-                 pa.dec_split_keys, (long long)items * la.hkv);
   kvc::FusedArgs fa;
   fa.k = k;
   fa.v = v;
@@ -536,14 +610,84 @@ int kvc_advance(kvc_t *h, void *stream) {
   int32_t *lens = reinterpret_cast<int32_t *>(h->base + h->lay.lens_off);
   const int32_t *nn = reinterpret_cast<const int32_t *>(h->base + h->lay.nnew_off);
   if (kvc::launch_advance(lens, nn, h->cfg.batch, stream)) return KVC_E_HIP;
-  for (int32_t b = 0; b < h->cfg.batch; ++b) h->lens_host[b] += h->n_new[b];
+  if (h->step_static) {
+    h->lens_stale = true;  // the counts never reached the host
+  } else {
+    for (int32_t b = 0; b < h->cfg.batch; ++b) h->lens_host[b] += h->n_new[b];
+  }
   h->in_step = false;
+  h->step_static = false;
   return KVC_OK;
 }
 
 int kvc_lens(const kvc_t *h, int32_t *lens_host) {
   if (!h || !lens_host) return KVC_E_ARG;
+  if (h->lens_stale) return KVC_E_STATE;
   std::copy(h->lens_host.begin(), h->lens_host.end(), lens_host);
+  return KVC_OK;
+}
+
+int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream) {
+  if (!h || !n_new_dev) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  if ((int32_t)h->classes.size() > kvc::kStaticClassMax) return KVC_E_ARG;
+  if (!use_device(h)) return KVC_E_HIP;
+  kvc::StaticBeginArgs a{};
+  a.n_src = n_new_dev;
+  a.n_new = reinterpret_cast<int32_t *>(h->base + h->lay.nnew_off);
+  a.lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
+  a.flags = reinterpret_cast<int32_t *>(h->base + h->lay.flags_off);
+  a.plan_sk = reinterpret_cast<int32_t *>(h->base + h->lay.plan_off);
+  a.plan_order = h->cfg.batch <= kvc::kDecodeOrderMax
+                     ? reinterpret_cast<uint16_t *>(h->base + h->lay.plan_off + 4 * h->cfg.n_layer)
+                     : nullptr;
+  a.B = h->cfg.batch;
+  a.max_len = h->cfg.max_len;
+  a.n_class = (int32_t)h->classes.size();
+  for (int32_t c = 0; c < a.n_class; ++c) {
+    kvc::StaticClass &cl = h->classes[c];
+    kvc::LayerArgs la{};
+    la.hkv = cl.hkv;
+    la.rep = h->cfg.n_q_head / cl.hkv;
+    cl.target = (int32_t)std::min<int64_t>(decode_wave_target(h, la, h->cfg.head_dim), 1 << 30);
+    cl.min_tiles = h->dec_min_tiles;
+    cl.fixed_q = h->dec_split_fixed > 0 ? h->dec_split_fixed / kvc::kDecodeTile : 0;
+    a.cls[c] = cl;
+  }
+  if (kvc::launch_static_begin(a, stream)) return KVC_E_HIP;
+  h->C = 1;
+  h->in_step = true;
+  h->step_static = true;
+  std::fill(h->appended.begin(), h->appended.end(), 0);
+  std::fill(h->attended.begin(), h->attended.end(), 0);
+  return KVC_OK;
+}
+
+int kvc_static_status(kvc_t *h, int32_t *flags_host, void *stream) {
+  if (!h || !flags_host) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  if (!use_device(h)) return KVC_E_HIP;
+  int32_t *flags = reinterpret_cast<int32_t *>(h->base + h->lay.flags_off);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, flags, 4, hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return KVC_E_HIP;
+  const int32_t zero = 0;
+  if (kvc::launch_set_rows(flags, &zero, 1, stream)) return KVC_E_HIP;
+  *flags_host = v;
+  return KVC_OK;
+}
+
+int kvc_sync_lens(kvc_t *h, void *stream) {
+  if (!h) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  if (!use_device(h)) return KVC_E_HIP;
+  const int32_t *lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
+  if (hipMemcpyAsync(h->lens_host.data(), lens, (size_t)h->cfg.batch * 4, hipMemcpyDeviceToHost,
+                     (hipStream_t)stream) != hipSuccess ||
+      hipStreamSynchronize((hipStream_t)stream) != hipSuccess)
+    return KVC_E_HIP;
+  h->lens_stale = false;
   return KVC_OK;
 }
 

@@ -47,6 +47,8 @@ struct Layout {
   int64_t dout_off = 0;       // float [B][Hq][kDecodeSplitCap][D]
   int64_t cnt_off = 0;        // int32 [B][max Hkv]: split arrivals (fused decode), 0 between launches
   int64_t cnt_bytes = 0;
+  int64_t flags_off = 0;      // int32: sticky error bits of static steps
+  int64_t plan_off = 0;       // int32 [n_layer] split keys, then uint16 [n_layer][B] row orders
   int64_t pml_off = -1;       // float2 [B][max_chunk][Hq][kChunkSplitCap]
   int64_t pout_off = -1;      // float [B][max_chunk][Hq][kChunkSplitCap][D]
   int64_t total = 0;
@@ -85,8 +87,37 @@ struct PartialArgs {
   int32_t dec_transpose;
   int32_t dec_ordered;
   uint16_t dec_order[256];
+  // A device-planned step (static one-token steps): the split length and the
+  // row order come from device memory written by k_static_begin instead of
+  // dec_split_keys / dec_order (null: host plan).
+  const int32_t *dec_plan;
+  const uint16_t *dec_order_dev;
 };
 constexpr int kDecodeOrderMax = 256;
+
+// Static one-token steps.  Layers that plan alike (same KV heads, window and
+// layout) form a class; k_static_begin checks the step's device counts and
+// writes every class's split plan, the same one the host planner would make.
+struct StaticClass {
+  int32_t hkv, window, ring;
+  int32_t target;     // waves in one round (resident decode waves x CUs)
+  int32_t min_tiles;  // smallest split in tiles
+  int32_t fixed_q;    // > 0: fixed split length in tiles (experiment override)
+};
+constexpr int kStaticClassMax = 16;
+// Sticky error bits of static steps (the step is then run with every count 0).
+constexpr int32_t kStaticBadCount = KVC_STATIC_BAD_COUNT;  // a count outside {0, 1}
+constexpr int32_t kStaticFull = KVC_STATIC_FULL;          // a row would pass max_len
+struct StaticBeginArgs {
+  const int32_t *n_src;   // the caller's counts [B] (device)
+  int32_t *n_new;         // the step's counts [B]
+  const int32_t *lens;    // [B]
+  int32_t *flags;         // sticky error bits
+  int32_t *plan_sk;       // [n_class] keys per split
+  uint16_t *plan_order;   // [n_class][B] dispatch order, or null (B > kDecodeOrderMax)
+  int32_t B, max_len, n_class;
+  StaticClass cls[kStaticClassMax];
+};
 
 // The single-token step of one layer in one launch (append, decode, combine):
 // the new token's K (pre-RoPE) and V, the slot report, the output and the
@@ -109,6 +140,7 @@ struct Launch {
 int launch_set_rows(int32_t *dst, const int32_t *vals, int32_t n, void *stream);
 int launch_reset_rows(int32_t *lens, const int32_t *rows, int32_t n, void *stream);
 int launch_advance(int32_t *lens, const int32_t *n_new, int32_t B, void *stream);
+int launch_static_begin(const StaticBeginArgs &a, void *stream);
 int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void *k,
                   const void *v, int32_t *slot_out, const Launch &lc);
 int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc);

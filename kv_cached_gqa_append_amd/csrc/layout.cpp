@@ -100,6 +100,9 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
   // One counter per (row, KV head); Hq bounds every layer's Hkv.
   lay->cnt_bytes = B * Hq * 4;
   if (!take(&cur, lay->cnt_bytes, &lay->cnt_off)) return KVC_E_ARG;
+  // Static steps: error bits, and per layer class a split length and a row order.
+  if (!take(&cur, 4, &lay->flags_off)) return KVC_E_ARG;
+  if (!take(&cur, (int64_t)cfg->n_layer * (4 + 2 * B), &lay->plan_off)) return KVC_E_ARG;
   if (cfg->max_chunk >= 2) {
     const int64_t pq = B * (int64_t)cfg->max_chunk * Hq * kChunkSplitCap;
     if (!take(&cur, pq * 8, &lay->pml_off) || !take(&cur, pq * D * 4, &lay->pout_off))
