@@ -12,7 +12,9 @@ attention and split-combine kernels), then one kvc_advance; the decode
 attention kernel is the roofline kernel.  A second timed leg then runs the
 same steps through kvc_append_attend (one kernel per layer: RoPE + append,
 decode attention, split merge) and reports it next to the headline
-(``--fused`` makes it the headline, ``--no-other-leg`` skips it).  Warmup
+(``--fused`` makes it the headline, ``--no-other-leg`` skips it), and a
+third replays a captured static step (kvc_static_begin, kvc_append_attend
+per layer, kvc_advance) from a HIP graph, reported as ``graph``.  Warmup
 steps run first; the timed steps are bracketed by torch.cuda.synchronize().
 Kernel durations come from HIP events that each dispatch stamps at its own
 start and end on the launch stream.
