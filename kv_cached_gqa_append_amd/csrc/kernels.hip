@@ -1453,14 +1453,15 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // r = i * REP + hl (token-major), wave w holds rows w*32 .. w*32+31 as two
 // 16-row blocks.  Key tiles of 32 rows pass through a 3-stage LDS ring:
 // every thread loads 16 bytes of K and 16 bytes of V per tile with raw buffer
-// loads (hand-placed waits, two tiles in flight), writes them to LDS (K
-// row-major with padded rows, V as two transposed 16-row blocks), and one
-// barrier per tile publishes them.  Per wave and tile:
+// loads (hand-placed waits, several tiles in flight), writes them to LDS (K
+// row-major with padded rows; V transposed, each head-dim row holding the
+// keys in the order the PV operand takes them), and one barrier per tile
+// publishes them.  Per wave and tile:
 //   S^T (32 keys x 16 queries) = K . Q^T   with v_mfma_f32_16x16x32_bf16
 //   O^T (D x 16 queries)     += V^T . P^T  with the same instruction,
-// each K and V operand read from LDS once and used for both query blocks;
+// each K and V operand one 16-byte LDS read, used for both query blocks;
 // the score accumulator already has the layout P^T needs as an operand.
-// Masking (per key and query) is applied uniformly.
+// Masks apply only on tiles at the diagonal or an edge.
 // ---------------------------------------------------------------------------
 struct KeySeg {
   const char *kreg, *vreg;  // region bases
@@ -1484,7 +1485,12 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   constexpr int CP = D >= 128 ? 6 : 8;
   static_assert(KCH <= 512, "one K chunk and one V chunk per thread");
   __shared__ __align__(16) bf16 lk[NSTAGE][32 * KSTR];
-  __shared__ __align__(16) bf16 lv[NSTAGE][2 * D * kVBlock];
+  // V^T of a tile: row d holds the 32 keys in the order the PV operand of
+  // lane group q4 takes them (keys 4q4..4q4+3, then 16+4q4..16+4q4+3), so an
+  // operand is one 16-byte read; rows padded to 40 keys so that the reads of
+  // 8 consecutive d fall in distinct banks.
+  constexpr int VSTR = 40;
+  __shared__ __align__(16) bf16 lv[NSTAGE][D * VSTR];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1682,10 +1688,19 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
         x[e2] &= keep;
       }
     }
-    *reinterpret_cast<u32x4 *>(&lv[s][c * 8]) = x;
+    // chunk c: keys 8 kh .. 8 kh + 7 of the tile's 16-row block blk at
+    // head-dim element dd; its two 4-key halves go to lane groups 2 kh and
+    // 2 kh + 1, in the block's half of each group's 8 slots
+    const int blk = c / (2 * D), dd = (c % (2 * D)) / 2, kh = c % 2;
+    bf16 *row = &lv[s][dd * VSTR + blk * 4];
+    *reinterpret_cast<uint2 *>(row + (2 * kh) * 8) = make_uint2(x[0], x[1]);
+    *reinterpret_cast<uint2 *>(row + (2 * kh + 1) * 8) = make_uint2(x[2], x[3]);
   };
 
   const float scale = kLog2e * rsqrtf((float)D);
+  // Reference-max slack (log2 units): p < 2^8 keeps P well inside bf16 and
+  // l, O inside fp32.
+  constexpr float kLazyRescale = 8.f;
   // positions fit in 32 bits (max_len < 2^31)
   const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
@@ -1727,14 +1742,14 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
     bf16x8_t pf[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      float sv[2][4];
+      float sv[2][4];  // raw scores q.k (the scale enters with the exponent)
       float tmax = -INFINITY;
       if (full) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            sv[kb][jj] = sacc[blk][kb][jj] * scale;
+            sv[kb][jj] = sacc[blk][kb][jj];
             tmax = fmaxf(tmax, sv[kb][jj]);
           }
       } else {
@@ -1753,29 +1768,34 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
               pos = Li + t;
             bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp;
             if (W > 0) ok = ok && (qp - pos < W);
-            const float x = ok ? sacc[blk][kb][jj] * scale : -INFINITY;
+            const float x = ok ? sacc[blk][kb][jj] : -INFINITY;
             sv[kb][jj] = x;
             tmax = fmaxf(tmax, x);
           }
       }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mn = fmaxf(mrun[blk], tmax);
+      // the row's max over the tile: its 4 lane groups hold 8 keys each
+      tmax = swap32_max(swap16_max(tmax));
+      // Reference max, in the scaled log2 domain, moved only when the tile's
+      // max passes it by more than kLazyRescale: p = 2^(s*scale - m) then
+      // stays below 2^kLazyRescale, and the accumulators are rescaled on
+      // rare tiles instead of whenever some row's max grows.
+      const float tm = tmax * scale;
+      const bool move = tm > mrun[blk] + kLazyRescale;
+      const float mn = move ? tm : mrun[blk];
+      const float alpha = move ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
       const float mu = mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(mrun[blk] - mu);
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float pe = __builtin_amdgcn_exp2f(sv[kb][jj] - mu);
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sv[kb][jj], scale, -mu));
           ps += pe;
           pf[blk][kb * 4 + jj] = (bf16)pe;
         }
       lrun[blk] = lrun[blk] * alpha + ps;
       mrun[blk] = mn;
-      // rescale only when some query's running max moved
-      if (__ballot(alpha != 1.f) != 0) {
+      if (__ballot(move) != 0) {
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha;
       }
@@ -1784,9 +1804,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int d = db * 16 + nl;
-      const uint2 lo8 = *reinterpret_cast<const uint2 *>(&lv[s][(0 * D + d) * kVBlock + q4 * 4]);
-      const uint2 hi8 = *reinterpret_cast<const uint2 *>(&lv[s][(1 * D + d) * kVBlock + q4 * 4]);
-      const uint4 av = make_uint4(lo8.x, lo8.y, hi8.x, hi8.y);
+      const uint4 av = *reinterpret_cast<const uint4 *>(&lv[s][d * VSTR + q4 * 8]);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
         oacc[blk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
