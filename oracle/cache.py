@@ -18,6 +18,13 @@ far, plus ``lens`` (tokens per row).  One step is
    ``KVCache.update`` docstring and ``advance``; Lab 07 "Given"; tinyllm
    ``end_step``).
 
+Left padding (tinyllm ``kv_cache.py``: ``padded_causal_mask`` and
+``SlotKVCache``): a row may start with ``first[b]`` pad tokens; keys before
+``first[b]`` are hidden from every query of the row except the pad's own
+query, which sees only itself.  ``set_first`` sets it, ``reset`` clears it,
+``admit`` copies whole rows (history, length, first) from another cache, as
+the slot cache admits a finished batched prefill.
+
 Padded queries (i >= n_new[b]) and idle rows (n_new[b] == 0) produce exact
 zeros: the pages leave these outputs unspecified (tiny_agent says garbage);
 zero is this implementation's reading.  Parity status: pinned by the
@@ -98,6 +105,7 @@ class OracleCache:
         self.window = window
         self.rope_base = float(rope_base)
         self.lens = np.zeros(self.batch, dtype=np.int64)
+        self.first = np.zeros(self.batch, dtype=np.int64)
         D = self.head_dim
         self.hist_k = [[np.zeros((0, h, D)) for _ in range(self.batch)] for h in n_kv_head]
         self.hist_v = [[np.zeros((0, h, D)) for _ in range(self.batch)] for h in n_kv_head]
@@ -112,7 +120,8 @@ class OracleCache:
         blocked = _mask.offset_mask(n, pos)
         qpos = self._query_positions(b, n)[:, None]
         kpos = np.arange(pos + n)[None, :]
-        return blocked | _mask.window_blocked(qpos, kpos, self.window[layer])
+        blocked = blocked | _mask.window_blocked(qpos, kpos, self.window[layer])
+        return blocked | _mask.left_pad_blocked(qpos, kpos, int(self.first[b]))
 
     # -- the step ------------------------------------------------------------
     def check_capacity(self, n_new) -> np.ndarray:
@@ -185,12 +194,41 @@ class OracleCache:
         return outs
 
     def reset(self, rows) -> None:
-        """Empty these rows: their lengths drop to 0 and their history is gone."""
+        """Empty these rows: their lengths drop to 0, their history is gone and
+        they have no left padding."""
         for b in np.asarray(rows, dtype=np.int64).reshape(-1):
             self.lens[b] = 0
+            self.first[b] = 0
             for l in range(self.n_layer):
                 self.hist_k[l][b] = self.hist_k[l][b][:0]
                 self.hist_v[l][b] = self.hist_v[l][b][:0]
+
+    def set_first(self, rows, first) -> None:
+        """Rows ``rows`` start with ``first`` pad positions (0 = none)."""
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        first = np.asarray(first, dtype=np.int64).reshape(-1)
+        if rows.shape != first.shape or (first < 0).any():
+            raise ValueError("one first >= 0 per row")
+        self.first[rows] = first
+
+    def admit(self, rows, src: "OracleCache", src_rows) -> None:
+        """Row rows[j] becomes a copy of src's row src_rows[j]: history of every
+        layer, length and left padding."""
+        rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+        src_rows = np.asarray(src_rows, dtype=np.int64).reshape(-1)
+        if rows.shape != src_rows.shape:
+            raise ValueError("one source row per row")
+        if (src.n_kv_head != self.n_kv_head or src.window != self.window
+                or src.head_dim != self.head_dim):
+            raise ValueError("caches of different layer shapes")
+        if (src.lens[src_rows] > self.max_len).any():
+            raise CacheFull("admitted row longer than max_len")
+        for b, sb in zip(rows, src_rows):
+            self.lens[b] = src.lens[sb]
+            self.first[b] = src.first[sb]
+            for l in range(self.n_layer):
+                self.hist_k[l][b] = src.hist_k[l][sb].copy()
+                self.hist_v[l][b] = src.hist_v[l][sb].copy()
 
     def history(self, layer: int, b: int):
         """Raw (k, v) of row b, layer ``layer``: each (lens[b], Hkv, D)."""

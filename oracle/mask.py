@@ -18,6 +18,9 @@ Polarity: the functions here return True where attention is NOT allowed
   ``padded_causal_mask``: causal, keys before ``first`` hidden, the diagonal
   always kept so that no query row is empty.  Pinned by left-padding
   invariance.
+* ``left_pad_blocked(qpos, kpos, first)``: the padding term of the same mask
+  on its own (keys before ``first`` hidden except a query's own key), for
+  combining with the offset mask and the sliding clamp.
 """
 
 import numpy as np
@@ -53,3 +56,12 @@ def padded_blocked(start: int, T: int, first: int) -> np.ndarray:
     causal_blocked = j > qpos
     pad_blocked = (j < first) & (j != qpos)
     return causal_blocked | pad_blocked
+
+
+def left_pad_blocked(qpos, kpos, first: int) -> np.ndarray:
+    """True where key kpos is left padding (kpos < first) and not the
+    query's own key.  Broadcasts qpos against kpos."""
+    qpos = np.asarray(qpos)
+    kpos = np.asarray(kpos)
+    return (kpos < first) & (kpos != qpos)
+

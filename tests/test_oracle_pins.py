@@ -302,6 +302,155 @@ def test_position_shift_invariance():
 
 
 # ---------------------------------------------------------------------------
+# Left-padded rows in the incremental oracle (tinyllm kv_cache.py:
+# padded_causal_mask, and the slot cache's admit / release).
+# ---------------------------------------------------------------------------
+_PAD_WORK = wl.Workload("pin_leftpad", 2, 3, 8, (2, 4), 16, 64, (0, 6), "f32", 40)
+
+
+def _leftpad_tokens(pads, reals, seed=11):
+    """Per row: pads[b] pad tokens (large random values) then reals[b] real
+    tokens, per layer; returns q, k, v lists [layer][row] of (P+R, H, D)."""
+    g = np.random.default_rng(seed)
+    w = _PAD_WORK
+    out = []
+    for l in range(w.n_layer):
+        hk = w.n_kv_head[l]
+        rows = []
+        for P, R in zip(pads, reals):
+            mk = lambda h, scale: g.standard_normal((P + R, h, w.head_dim)) * scale
+            q, k, v = mk(w.n_q_head, 1.0), mk(hk, 1.0), mk(hk, 1.0)
+            q[:P] *= 5; k[:P] *= 5; v[:P] *= 5
+            rows.append((q, k, v))
+        out.append(rows)
+    return out
+
+
+def _feed(oc, toks, starts, counts, C):
+    """One step: row b takes tokens starts[b] .. starts[b]+counts[b]-1."""
+    layers = []
+    for l in range(oc.n_layer):
+        hq, hk, D = oc.n_q_head, oc.n_kv_head[l], oc.head_dim
+        q = np.zeros((oc.batch, C, hq, D)); k = np.zeros((oc.batch, C, hk, D)); v = np.zeros_like(k)
+        for b in range(oc.batch):
+            s, n = starts[b], counts[b]
+            tq, tk, tv = toks[l][b]
+            q[b, :n], k[b, :n], v[b, :n] = tq[s:s + n], tk[s:s + n], tv[s:s + n]
+        layers.append((q, k, v))
+    return oc.step(np.asarray(counts), layers)
+
+
+def _leftpad_run(pads, reals, prefill_chunk, decodes):
+    """Outputs per step of an unpadded and a left-padded run of the same real
+    tokens: lists of (layer outputs, starts, counts) for each run."""
+    w = _PAD_WORK
+    n_tok = [R + decodes for R in reals]
+    toks_pad = _leftpad_tokens(pads, n_tok)
+    toks_plain = [[(q[P:], k[P:], v[P:]) for (q, k, v), P in zip(rows, pads)] for rows in toks_pad]
+    runs = []
+    for toks, lead, first in ((toks_plain, [0] * len(pads), False), (toks_pad, pads, True)):
+        oc = _oracle_for(w)
+        if first:
+            oc.set_first(np.arange(w.batch), pads)
+        steps = []
+        done = [0] * w.batch
+        prompt = [L + R for L, R in zip(lead, reals)]
+        while any(d < p for d, p in zip(done, prompt)):
+            cnt = [min(prefill_chunk, p - d) for d, p in zip(done, prompt)]
+            steps.append((_feed(oc, toks, list(done), cnt, prefill_chunk), list(done), cnt))
+            done = [d + c for d, c in zip(done, cnt)]
+        for _ in range(decodes):
+            cnt = [1] * w.batch
+            steps.append((_feed(oc, toks, list(done), cnt, 1), list(done), cnt))
+            done = [d + 1 for d in done]
+        runs.append((steps, toks))
+    return runs
+
+
+def _token_outputs(steps, batch, n_layer):
+    """[layer][row] -> outputs of every token, in position order."""
+    res = [[[] for _ in range(batch)] for _ in range(n_layer)]
+    for outs, starts, counts in steps:
+        for l in range(n_layer):
+            for b in range(batch):
+                res[l][b].append(outs[l][b, :counts[b]])
+    return [[np.concatenate(r) for r in rl] for rl in res]
+
+
+@pytest.mark.parametrize("chunk", [40, 5])
+def test_oracle_left_padded_rows_equal_unpadded(chunk):
+    # tinyllm kv_cache.py module docstring: with left padding no per-row RoPE
+    # positions are needed (RoPE depends on distances only and padding shifts
+    # a row's real tokens alike); pad keys are masked.  So the real tokens'
+    # outputs of a left-padded row equal those of the same row unpadded, on a
+    # global and a sliding (W = 6) layer, for a prefill in one chunk or in
+    # chunks of 5 and for decode steps after it.
+    pads, reals, decodes = [4, 0, 9], [7, 11, 3], 8
+    (plain, _), (padded, toks) = _leftpad_run(pads, reals, chunk, decodes)
+    w = _PAD_WORK
+    a = _token_outputs(plain, w.batch, w.n_layer)
+    b = _token_outputs(padded, w.batch, w.n_layer)
+    worst = 0.0
+    for l in range(w.n_layer):
+        for r in range(w.batch):
+            P = pads[r]
+            worst = max(worst, float(np.abs(b[l][r][P:] - a[l][r]).max()))
+    assert worst <= 1e-12, worst
+
+
+def test_oracle_pad_queries_see_only_themselves():
+    # padded_causal_mask keeps the diagonal: a pad query's softmax has one
+    # key, so its output is its own value (its KV head's), exactly.
+    pads, reals = [4, 0, 9], [7, 11, 3]
+    (_, _), (padded, toks) = _leftpad_run(pads, reals, 40, 0)
+    w = _PAD_WORK
+    b = _token_outputs(padded, w.batch, w.n_layer)
+    for l in range(w.n_layer):
+        rep = w.n_q_head // w.n_kv_head[l]
+        for r in range(w.batch):
+            P = pads[r]
+            v = toks[l][r][2][:P]                              # (P, Hkv, D)
+            assert np.array_equal(b[l][r][:P], np.repeat(v, rep, axis=1))
+
+
+def test_oracle_admit_copies_rows():
+    # SlotKVCache.admit: a finished (left-padded) prefill's rows become slots;
+    # decoding the slots then equals decoding the prefill cache itself.
+    w = _PAD_WORK
+    pads, reals = [4, 0, 9], [7, 11, 3]
+    toks = _leftpad_tokens(pads, [R + 4 for R in reals], seed=12)
+    src = _oracle_for(w)
+    src.set_first(np.arange(3), pads)
+    prompt = [P + R for P, R in zip(pads, reals)]
+    _feed(src, toks, [0, 0, 0], prompt, max(prompt))
+    dst = _oracle_for(w)
+    dst.admit([2, 0, 1], src, [0, 1, 2])
+    assert list(dst.lens) == [prompt[1], prompt[2], prompt[0]]
+    assert list(dst.first) == [pads[1], pads[2], pads[0]]
+    perm = [1, 2, 0]
+    toks_dst = [[rows[i] for i in perm] for rows in toks]
+    for s in range(4):
+        a = _feed(src, toks, [p + s for p in prompt], [1, 1, 1], 1)
+        b = _feed(dst, toks_dst, [prompt[i] + s for i in perm], [1, 1, 1], 1)
+        for l in range(w.n_layer):
+            assert np.array_equal(a[l][perm], b[l])
+    dst.reset([0])
+    assert dst.lens[0] == 0 and dst.first[0] == 0
+
+
+def test_mutation_left_pad_ignored(monkeypatch):
+    monkeypatch.setattr(omask, "left_pad_blocked",
+                        lambda qpos, kpos, first: np.zeros(np.broadcast(np.asarray(qpos), np.asarray(kpos)).shape, dtype=bool))
+    assert _fails(lambda: test_oracle_left_padded_rows_equal_unpadded(40))
+
+
+def test_mutation_left_pad_hides_diagonal(monkeypatch):
+    monkeypatch.setattr(omask, "left_pad_blocked",
+                        lambda qpos, kpos, first: np.asarray(kpos) < first + 0 * np.asarray(qpos))
+    assert _fails(test_oracle_pad_queries_see_only_themselves)
+
+
+# ---------------------------------------------------------------------------
 # Sizes: Lab 07 answer 1; colibri PR "Expected memory savings".
 # ---------------------------------------------------------------------------
 def test_kv_bytes_lab07():
