@@ -106,11 +106,36 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes,
 /* Free the host handle.  The device buffer stays the caller's. */
 void kvc_destroy(kvc_t *h);
 
-/* Empty `n_rows` rows (host array of row indices): their length drops to 0.
+/* Empty `n_rows` rows (host array of row indices): their length and left
+ * padding drop to 0.
  * Nothing is zeroed: stale keys and values stay in memory and are never read
  * again (pycraft-1 reset; tiny_agent KVCache.reset).  Not allowed inside a
  * step (KVC_E_STATE). */
 int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream);
+
+/* Left padding: rows rows_host[i] start with first_host[i] pad positions
+ * (0 <= first <= max_len; 0 = none).  Keys at positions below first[b] are
+ * hidden from every query of row b, except that a pad query (position below
+ * first) sees its own key, so that no query has an empty softmax (tinyllm
+ * "kv_cache.py": padded_causal_mask and the KVCache pad_lens; a left-padded
+ * batched prefill).  RoPE positions are unchanged: pads take positions
+ * 0 .. first - 1.  kvc_reset clears it.  Not inside a step. */
+int kvc_set_first(kvc_t *h, const int32_t *rows_host, const int32_t *first_host,
+                  int32_t n_rows, void *stream);
+
+/* Admit rows of another cache (tinyllm "kv_cache.py", SlotKVCache.admit: a
+ * finished batched prefill's rows become decode slots): row dst_rows[i] of
+ * `dst` becomes a copy of row src_rows[i] of `src` (every layer's keys and
+ * values, its length and its left padding); the source rows are unchanged.
+ * The two caches must have the same layers (KV heads, windows, layouts),
+ * head_dim, Hq and dtype, live on one device, and be outside a step with
+ * fresh host mirrors (else KVC_E_ARG / KVC_E_STATE); a source row longer
+ * than dst's max_len gives KVC_E_FULL; dst rows must be distinct and, when
+ * src == dst, not among the source rows.  Device-to-device copies of the
+ * rows' stored blocks, enqueued on `stream` after any earlier work there.
+ * Release a slot with kvc_reset. */
+int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src,
+              const int32_t *src_rows, int32_t n_rows, void *stream);
 
 /* Append layer `layer`'s new keys and values.
  *   k, v          device, (B, C, Hkv_l, D) in the cache dtype; k is pre-RoPE

@@ -118,6 +118,10 @@ def lib():
         L.kvc_advance.restype = ctypes.c_int
         L.kvc_lens.argtypes = [VP, P(I32)]
         L.kvc_lens.restype = ctypes.c_int
+        L.kvc_set_first.argtypes = [VP, P(I32), P(I32), I32, VP]
+        L.kvc_set_first.restype = ctypes.c_int
+        L.kvc_admit.argtypes = [VP, P(I32), VP, P(I32), I32, VP]
+        L.kvc_admit.restype = ctypes.c_int
         L.kvc_static_begin.argtypes = [VP, VP, VP]
         L.kvc_static_begin.restype = ctypes.c_int
         L.kvc_static_status.argtypes = [VP, P(I32), VP]
@@ -245,6 +249,22 @@ def kvc_append_attend(h, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.
 
 def kvc_advance(h, stream=None) -> None:
     _check(lib().kvc_advance(h, _stream_handle(stream)), "kvc_advance")
+
+
+def kvc_set_first(h, rows, first, stream=None) -> None:
+    r, n = _rows_array(rows)
+    f, m = _rows_array(first)
+    if n != m:
+        raise ValueError("one first per row")
+    _check(lib().kvc_set_first(h, r, f, n, _stream_handle(stream)), "kvc_set_first")
+
+
+def kvc_admit(dst, dst_rows, src, src_rows, stream=None) -> None:
+    d, n = _rows_array(dst_rows)
+    r, m = _rows_array(src_rows)
+    if n != m:
+        raise ValueError("one source row per row")
+    _check(lib().kvc_admit(dst, d, src, r, n, _stream_handle(stream)), "kvc_admit")
 
 
 def kvc_static_begin(h, n_new_dev: torch.Tensor, stream=None) -> None:
@@ -408,7 +428,16 @@ class Cache:
         kvc_sync_lens(self.handle, stream)
 
     def reset(self, rows, stream=None):
+        """Empty rows (release slots): length and left padding 0."""
         kvc_reset(self.handle, rows, stream)
+
+    def set_first(self, rows, first, stream=None):
+        """Rows start with ``first`` left-pad positions (hidden keys)."""
+        kvc_set_first(self.handle, rows, first, stream)
+
+    def admit(self, rows, src: "Cache", src_rows, stream=None):
+        """Rows ``rows`` become copies of ``src``'s rows ``src_rows``."""
+        kvc_admit(self.handle, rows, src.handle, src_rows, stream)
 
     def lens(self):
         return kvc_lens(self.handle, self.batch)

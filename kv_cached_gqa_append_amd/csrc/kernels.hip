@@ -142,21 +142,46 @@ __device__ __forceinline__ int64_t ring_slot_pos(int64_t s, int64_t L, int W) {
   return s < r ? (L - r + s) : (L - r - W + s);
 }
 
-// Decode key span in storage rows (identical to the host planner).
-__device__ __forceinline__ void decode_span_dev(const LayerArgs &la, int64_t p, int64_t *base,
-                                                int64_t *lo, int64_t *hi) {
+// Keys of a one-token query at position p on this layer, for a row whose
+// first `first` positions are left padding (identical spans to the host
+// planner).  The first visible position is the window's (W > 0) or 0,
+// raised to `first`; a pad query (p < first) sees only itself.  Storage rows
+// [base, hi) are visited; row r there is visible iff r < hi and r - va,
+// taken mod vwrap on a ring (vwrap = W; 0 on a full layer), lies in [0, vn).
+// On a ring the visible positions fill slots [0, min(p + 1, W)) and the
+// padding visible in the window is a run of consecutive slots mod W.
+struct DecodeSpan {
+  int64_t base, hi, va, vn;
+  int32_t vwrap;
+};
+__device__ __forceinline__ DecodeSpan decode_span_dev(const LayerArgs &la, int64_t p,
+                                                      int64_t first) {
+  int64_t start = la.window > 0 ? (p - la.window + 1 > 0 ? p - la.window + 1 : 0) : 0;
+  start = p < first ? p : (start > first ? start : first);
+  DecodeSpan s;
+  s.vn = p + 1 - start;
   if (la.ring) {
-    *lo = 0;
-    *hi = p + 1 < la.window ? p + 1 : la.window;
+    s.base = 0;
+    s.hi = p + 1 < la.window ? p + 1 : la.window;
+    s.va = start % la.window;
+    s.vwrap = la.window;
   } else {
-    *lo = la.window > 0 ? (p - la.window + 1 > 0 ? p - la.window + 1 : 0) : 0;
-    *hi = p + 1;
+    s.base = start / kRowAlign * kRowAlign;
+    s.hi = p + 1;
+    s.va = start;
+    s.vwrap = 0;
   }
-  *base = *lo / kRowAlign * kRowAlign;
+  return s;
 }
+// Key span of a chunk of n tokens from position L on a full layer: rows
+// [lo, hi), visited from base.  Left padding raises lo to `first` unless the
+// chunk holds pad queries (L < first), which see their own rows (>= L).
 __device__ __forceinline__ void chunk_span_dev(const LayerArgs &la, int64_t L, int64_t n,
-                                               int64_t *base, int64_t *lo, int64_t *hi) {
+                                               int64_t first, int64_t *base, int64_t *lo,
+                                               int64_t *hi) {
   *lo = la.window > 0 ? (L - la.window + 1 > 0 ? L - la.window + 1 : 0) : 0;
+  const int64_t f = first < L ? first : L;
+  if (f > *lo) *lo = f;
   *hi = L + n;
   *base = *lo / kRowAlign * kRowAlign;
 }
@@ -173,9 +198,43 @@ __global__ void k_set_rows(int32_t *dst, I32Chunk c, int32_t n) {
   if (i < n) dst[i] = c.v[i];
 }
 
-__global__ void k_reset_rows(int32_t *lens, I32Chunk rows, int32_t n) {
+__global__ void k_reset_rows(int32_t *lens, int32_t *first, I32Chunk rows, int32_t n) {
   const int i = threadIdx.x;
-  if (i < n) lens[rows.v[i]] = 0;
+  if (i < n) {
+    lens[rows.v[i]] = 0;
+    first[rows.v[i]] = 0;
+  }
+}
+
+__global__ void k_set_first(int32_t *first, I32Chunk rows, I32Chunk vals, int32_t n) {
+  const int i = threadIdx.x;
+  if (i < n) first[rows.v[i]] = vals.v[i];
+}
+
+// Grid (pairs x KV heads, 2 (K, V), z): each block copies a strided share of
+// the first rows[j] storage rows of one head's K (y = 0) or V (y = 1) region;
+// both regions keep a head's rows contiguous from row 0 (V in whole 16-row
+// blocks), so the copy is a flat run of 16-byte units.
+__global__ __launch_bounds__(256) void k_copy_rows(LayerArgs dst, LayerArgs src, int32_t row_bytes,
+                                                   CopyPairs pr) {
+  const int j = blockIdx.x / src.hkv, g = blockIdx.x % src.hkv;
+  const char *sb = (blockIdx.y ? src.v : src.k) +
+                   ((int64_t)pr.src_row[j] * src.hkv + g) * src.rows_alloc * row_bytes;
+  char *db = (blockIdx.y ? dst.v : dst.k) +
+             ((int64_t)pr.dst_row[j] * dst.hkv + g) * dst.rows_alloc * row_bytes;
+  const int64_t units = (int64_t)pr.rows[j] * row_bytes / 16;
+  for (int64_t u = (int64_t)blockIdx.z * blockDim.x + threadIdx.x; u < units;
+       u += (int64_t)gridDim.z * blockDim.x)
+    reinterpret_cast<uint4 *>(db)[u] = reinterpret_cast<const uint4 *>(sb)[u];
+}
+
+__global__ void k_copy_state(int32_t *dst_lens, int32_t *dst_first, const int32_t *src_lens,
+                             const int32_t *src_first, CopyPairs pr, int32_t n) {
+  const int j = threadIdx.x;
+  if (j < n) {
+    dst_lens[pr.dst_row[j]] = src_lens[pr.src_row[j]];
+    dst_first[pr.dst_row[j]] = src_first[pr.src_row[j]];
+  }
 }
 
 __global__ void k_advance(int32_t *lens, const int32_t *n_new, int32_t B) {
@@ -194,14 +253,56 @@ int launch_set_rows(int32_t *dst, const int32_t *vals, int32_t n, void *stream) 
   return (int)hipGetLastError();
 }
 
-int launch_reset_rows(int32_t *lens, const int32_t *rows, int32_t n, void *stream) {
+int launch_reset_rows(int32_t *lens, int32_t *first, const int32_t *rows, int32_t n,
+                      void *stream) {
   for (int32_t off = 0; off < n; off += 256) {
     I32Chunk c;
     const int32_t m = n - off < 256 ? n - off : 256;
     std::memset(&c, 0, sizeof(c));
     std::memcpy(c.v, rows + off, sizeof(int32_t) * m);
-    hipLaunchKernelGGL(k_reset_rows, dim3(1), dim3(256), 0, (hipStream_t)stream, lens, c, m);
+    hipLaunchKernelGGL(k_reset_rows, dim3(1), dim3(256), 0, (hipStream_t)stream, lens, first, c,
+                       m);
   }
+  return (int)hipGetLastError();
+}
+
+int launch_set_first(int32_t *first, const int32_t *rows, const int32_t *vals, int32_t n,
+                     void *stream) {
+  for (int32_t off = 0; off < n; off += 256) {
+    I32Chunk r, v;
+    const int32_t m = n - off < 256 ? n - off : 256;
+    std::memset(&r, 0, sizeof(r));
+    std::memset(&v, 0, sizeof(v));
+    std::memcpy(r.v, rows + off, sizeof(int32_t) * m);
+    std::memcpy(v.v, vals + off, sizeof(int32_t) * m);
+    hipLaunchKernelGGL(k_set_first, dim3(1), dim3(256), 0, (hipStream_t)stream, first, r, v, m);
+  }
+  return (int)hipGetLastError();
+}
+
+int launch_copy_rows(const LayerArgs &dst, const LayerArgs &src, int D, int dtype_bytes,
+                     const CopyPairs &pairs, int32_t n_pairs, void *stream) {
+  if (n_pairs < 1 || n_pairs > 64 || dst.hkv != src.hkv) return (int)hipErrorInvalidValue;
+  const int32_t row_bytes = D * dtype_bytes;
+  int32_t most = 0;
+  for (int32_t j = 0; j < n_pairs; ++j) {
+    if (pairs.rows[j] > src.rows_alloc || pairs.rows[j] > dst.rows_alloc || pairs.rows[j] < 0)
+      return (int)hipErrorInvalidValue;
+    most = pairs.rows[j] > most ? pairs.rows[j] : most;
+  }
+  const int64_t units = (int64_t)most * row_bytes / 16;
+  const unsigned z = (unsigned)(units / 2048 < 1 ? 1 : (units / 2048 > 64 ? 64 : units / 2048));
+  hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)(n_pairs * src.hkv), 2, z), dim3(256), 0,
+                     (hipStream_t)stream, dst, src, row_bytes, pairs);
+  return (int)hipGetLastError();
+}
+
+int launch_copy_state(int32_t *dst_lens, int32_t *dst_first, const int32_t *src_lens,
+                      const int32_t *src_first, const CopyPairs &pairs, int32_t n_pairs,
+                      void *stream) {
+  if (n_pairs < 1 || n_pairs > 64) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_copy_state, dim3(1), dim3(64), 0, (hipStream_t)stream, dst_lens, dst_first,
+                     src_lens, src_first, pairs, n_pairs);
   return (int)hipGetLastError();
 }
 
@@ -261,9 +362,8 @@ __global__ __launch_bounds__(64) void k_static_begin(StaticBeginArgs a) {
   la.ring = cl.ring;
   auto tiles = [&](int b) -> int {  // tiles of a decoding row, 0 for an idle one
     if (bad || a.n_src[b] != 1) return 0;
-    int64_t base, lo, hi;
-    decode_span_dev(la, a.lens[b], &base, &lo, &hi);
-    return (int)cdiv(hi - base, kDecodeTile);
+    const DecodeSpan sp = decode_span_dev(la, a.lens[b], a.first[b]);
+    return (int)cdiv(sp.hi - sp.base, kDecodeTile);
   };
   int max_t = 0, idle = 0;
   for (int b = lane; b < a.B; b += 64) {
@@ -534,32 +634,40 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
   S.l = 0.f;
   const float scale = rsqrtf((float)D);
   const int W = la.window;
+  // left padding: keys before `first` are hidden, except the query's own
+  const int64_t first = st.first[b];
+  auto hidden = [&](int64_t pos) { return pos < first && pos != p; };
   if (la.ring && n >= 2 && la.sk) {
     // history from the ring (slots holding positions within the window) ...
     const int64_t nh = L < W ? L : W;
     for (int64_t s = 0; s < nh; ++s) {
       const int64_t pos = ring_slot_pos(s, L, W);
-      if (pos < 0 || p - pos >= W) continue;
+      if (pos < 0 || p - pos >= W || hidden(pos)) continue;
       generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, s, D),
                   v_elem<T>(la.v, bg, la.rows_alloc, s, 0, D), D, scale);
     }
     // ... and the chunk's own rows from staging
     for (int j = 0; j <= i; ++j) {
-      if (i - j >= W) continue;
+      if (i - j >= W || hidden(L + j)) continue;
       generic_key(S, k_row<T>(la.sk, bg, la.stage_rows_alloc, j, D),
                   v_elem<T>(la.sv, bg, la.stage_rows_alloc, j, 0, D), D, scale);
     }
   } else if (la.ring) {
-    // one-token step: the visible positions fill slots [0, min(p + 1, W))
+    // one-token step: the visible positions fill slots [0, min(p + 1, W));
+    // slot s holds the latest position <= p congruent to s mod W
     const int64_t hi = p + 1 < W ? p + 1 : W;
-    for (int64_t s = 0; s < hi; ++s)
+    for (int64_t s = 0; s < hi; ++s) {
+      if (hidden(p - (p - s) % W)) continue;
       generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, s, D),
                   v_elem<T>(la.v, bg, la.rows_alloc, s, 0, D), D, scale);
+    }
   } else {
     const int64_t lo = W > 0 ? (p - W + 1 > 0 ? p - W + 1 : 0) : 0;
-    for (int64_t t = lo; t <= p; ++t)
+    for (int64_t t = lo; t <= p; ++t) {
+      if (hidden(t)) continue;
       generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, t, D),
                   v_elem<T>(la.v, bg, la.rows_alloc, t, 0, D), D, scale);
+    }
   }
   const float inv = 1.f / S.l;
 #pragma unroll
@@ -1023,9 +1131,8 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
         const int r = row_at(r0);
         const int nr = st.n_new[r];
         if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
-        int64_t base, lo, hi;
-        decode_span_dev(la, st.lens[r], &base, &lo, &hi);
-        return (int)cdiv(hi - base, SK);
+        const DecodeSpan sp = decode_span_dev(la, st.lens[r], st.first[r]);
+        return (int)cdiv(sp.hi - sp.base, SK);
       },
       &b, &split64);
   if (b < 0) return;
@@ -1041,10 +1148,10 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const int split = (int)split64;
   const int h0 = g * REP;
   const int64_t p = st.lens[b];
-  int64_t base64, lo64, hi64;
-  decode_span_dev(la, p, &base64, &lo64, &hi64);
+  const DecodeSpan span = decode_span_dev(la, p, st.first[b]);
+  const int64_t base64 = span.base, hi64 = span.hi;
   // Row indices fit in 32 bits (rows <= max_len < 2^31).
-  const int lo = (int)lo64, hi = (int)hi64;
+  const int hi = (int)hi64, va = (int)span.va, vn = (int)span.vn, vwrap = span.vwrap;
   // The row's 16-key tiles are dealt round-robin to its splits: split s
   // takes tiles s, s + nsplit, s + 2 nsplit, ... (counts differ by at most
   // one).  The splits of a row then sweep its K and V regions side by side,
@@ -1181,9 +1288,10 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   int hbase = 0;     // first head this lane owns (set by the reduce-scatter)
   bool writer = true;  // one lane per (key, head) publishes p
 
-  // One tile: QK, online softmax, P.V.  Rows of the tile outside [lo, hi)
-  // are masked in the scores; their V is finite (rows past a row's end are
-  // zeroed when the append enters a new 32-row tile), so p = 0 cancels them.
+  // One tile: QK, online softmax, P.V.  Rows of the tile that are not
+  // visible (outside the span, left padding) are masked in the scores; their
+  // V is finite (rows past a row's end are zeroed when the append enters a
+  // new 32-row tile), so p = 0 cancels them.
   auto step = [&](int it, Tile &T) {
     const int t0 = t_begin + it * t_stride;
     const int par = it & 1;
@@ -1207,7 +1315,8 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     for (int r = 0; r < NR; ++r) {
       key_reduce_scatter<LK, REP, HPL>(a[r], lane, s[r]);
       const int key = t0 + r * KR + kr;
-      const bool ok = key >= lo && key < hi;
+      const int d = key - va + (key < va ? vwrap : 0);
+      const bool ok = key < hi && (unsigned)d < (unsigned)vn;
 #pragma unroll
       for (int u = 0; u < HPL; ++u) s[r][u] = ok ? s[r][u] : -INFINITY;
     }
@@ -1508,7 +1617,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
         const int nqt = (int)cdiv((int64_t)n * REP, kChunkQTile);
         if (la.ring) return nqt;
         int64_t base, lo, hi;
-        chunk_span_dev(la, st.lens[r], n, &base, &lo, &hi);
+        chunk_span_dev(la, st.lens[r], n, st.first[r], &base, &lo, &hi);
         return nqt * (int)cdiv(hi - base, SKP);
       },
       &b, &local);
@@ -1518,7 +1627,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   int nks = 1;
   int64_t cbase = 0, clo = 0, chi = 0;
   if (!la.ring) {
-    chunk_span_dev(la, L, n, &cbase, &clo, &chi);
+    chunk_span_dev(la, L, n, st.first[b], &cbase, &clo, &chi);
     nks = (int)cdiv(chi - cbase, SKP);
   }
   const int qt = (int)(local / nks), ks = (int)(local % nks);
@@ -1703,6 +1812,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   constexpr float kLazyRescale = 8.f;
   // positions fit in 32 bits (max_len < 2^31)
   const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
+  const int first_i = st.first[b];  // left padding: keys before it are hidden
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   floatx4 oacc[2][NDB];
 #pragma unroll
@@ -1738,7 +1848,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
     // only the tiles at the diagonal and the edges do.
     const int t0i = (int)t0, vloi = (int)vlo, vhii = (int)vhi;
     const bool full = kind == 0 && t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
-                      (W == 0 || pmax_i - t0i < W);
+                      (W == 0 || pmax_i - t0i < W) && t0i >= first_i;
     bf16x8_t pf[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
@@ -1766,7 +1876,8 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
               pos = (int)ring_slot_pos(t, L, W);
             else
               pos = Li + t;
-            bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp;
+            bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp &&
+                      (pos >= first_i || pos == qp);
             if (W > 0) ok = ok && (qp - pos < W);
             const float x = ok ? sacc[blk][kb][jj] : -INFINITY;
             sv[kb][jj] = x;
@@ -1920,9 +2031,8 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
   const float *os;
   int ns;
   if (n == 1) {
-    int64_t base, lo, hi;
-    decode_span_dev(la, L, &base, &lo, &hi);
-    ns = (int)cdiv(hi - base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
+    const DecodeSpan sp = decode_span_dev(la, L, st.first[b]);
+    ns = (int)cdiv(sp.hi - sp.base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
     const int64_t s0 = ((int64_t)b * st.Hq + h) * kDecodeSplitCap;
     ml = pa.dml + s0 * 2;
     os = pa.dout + s0 * D;
@@ -1930,7 +2040,7 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
     ns = 1;
     if (!la.ring) {
       int64_t base, lo, hi;
-      chunk_span_dev(la, L, n, &base, &lo, &hi);
+      chunk_span_dev(la, L, n, st.first[b], &base, &lo, &hi);
       ns = (int)cdiv(hi - base, pa.pre_split_keys);
     }
     const int64_t s0 = (((int64_t)b * pa.max_chunk + i) * st.Hq + h) * kChunkSplitCap;

@@ -31,6 +31,7 @@ struct kvc_cache {
   size_t bytes = 0;
   int device = 0;
   std::vector<int32_t> lens_host;
+  std::vector<int32_t> first_host;  // left padding per row (mirror of the device copy)
   // step state
   bool in_step = false;
   std::vector<int32_t> n_new;
@@ -76,6 +77,7 @@ kvc::StepArgs step_args(const kvc_t *h) {
   kvc::StepArgs st{};
   st.lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
   st.n_new = reinterpret_cast<const int32_t *>(h->base + h->lay.nnew_off);
+  st.first = reinterpret_cast<const int32_t *>(h->base + h->lay.first_off);
   st.rope = h->lay.rope_off >= 0 ? reinterpret_cast<const float *>(h->base + h->lay.rope_off)
                                   : nullptr;
   st.B = h->cfg.batch;
@@ -118,7 +120,7 @@ kvc::Launch launch_on(kvc_t *h, int kind, void *stream) {
   return lc;
 }
 
-void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi);
+void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t first, int64_t *base, int64_t *hi);
 
 // Keys per decode split for this layer and step.  The decode launch should be
 // one round of equally long waves: the smallest split (in 16-key tiles) whose
@@ -136,7 +138,7 @@ int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
     extra += h->n_new[b] == 0 ? la.hkv : 0;
     if (h->n_new[b] != 1) continue;
     int64_t base, hi;
-    decode_span(la, h->lens_host[b], &base, &hi);
+    decode_span(la, h->lens_host[b], h->first_host[b], &base, &hi);
     tiles.push_back((hi - base + TK - 1) / TK);
     max_t = std::max(max_t, tiles.back());
   }
@@ -183,7 +185,7 @@ void decode_order(const kvc_t *h, const kvc::LayerArgs &la, kvc::PartialArgs *pa
     double per = 0.0;
     if (h->n_new[b] == 1) {
       int64_t base, hi;
-      decode_span(la, h->lens_host[b], &base, &hi);
+      decode_span(la, h->lens_host[b], h->first_host[b], &base, &hi);
       const int64_t t = (hi - base + kvc::kDecodeTile - 1) / kvc::kDecodeTile;
       const int64_t ns = (hi - base + pa->dec_split_keys - 1) / pa->dec_split_keys;
       per = (double)t / (double)ns;
@@ -195,24 +197,29 @@ void decode_order(const kvc_t *h, const kvc::LayerArgs &la, kvc::PartialArgs *pa
   pa->dec_ordered = 1;
 }
 
-// Key span of a one-token query at p on this layer, in storage rows.
-// Global layer: rows [lo, p] (lo = p - W + 1 when a window clamps).
-// Ring layer: the visible positions occupy slots [0, min(p + 1, W)).
-void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t *base, int64_t *hi) {
-  int64_t lo;
+// Key span of a one-token query at p on this layer, in storage rows (the
+// rows a decode visits; masking of the rest is the kernel's).  Global layer:
+// from the first visible position (the window's, raised to the row's left
+// padding `first`; a pad query sees only itself) to p.  Ring layer: the
+// visible positions occupy slots [0, min(p + 1, W)).
+void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t first, int64_t *base, int64_t *hi) {
   if (la.ring) {
-    lo = 0;
+    *base = 0;
     *hi = std::min<int64_t>(p + 1, la.window);
-  } else {
-    lo = la.window > 0 ? std::max<int64_t>(0, p - la.window + 1) : 0;
-    *hi = p + 1;
+    return;
   }
-  *base = lo / kvc::kRowAlign * kvc::kRowAlign;
+  int64_t start = la.window > 0 ? std::max<int64_t>(0, p - la.window + 1) : 0;
+  start = p < first ? p : std::max(start, first);
+  *hi = p + 1;
+  *base = start / kvc::kRowAlign * kvc::kRowAlign;
 }
 
-// Key span of a chunk of n tokens starting at L on a non-ring layer.
-void chunk_span(const kvc::LayerArgs &la, int64_t L, int64_t n, int64_t *base, int64_t *hi) {
-  const int64_t lo = la.window > 0 ? std::max<int64_t>(0, L - la.window + 1) : 0;
+// Key span of a chunk of n tokens starting at L on a non-ring layer; left
+// padding raises the start to `first` unless the chunk holds pad queries.
+void chunk_span(const kvc::LayerArgs &la, int64_t L, int64_t n, int64_t first, int64_t *base,
+                int64_t *hi) {
+  int64_t lo = la.window > 0 ? std::max<int64_t>(0, L - la.window + 1) : 0;
+  lo = std::max(lo, std::min(first, L));
   *hi = L + n;
   *base = lo / kvc::kRowAlign * kvc::kRowAlign;
 }
@@ -262,6 +269,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   h->base = static_cast<char *>(dev_buf);
   h->bytes = buf_bytes;
   h->lens_host.assign(cfg->batch, 0);
+  h->first_host.assign(cfg->batch, 0);
   h->n_new.assign(cfg->batch, 0);
   h->appended.assign(cfg->n_layer, 0);
   h->attended.assign(cfg->n_layer, 0);
@@ -296,6 +304,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   // at zero (the counters return to zero at the end of every fused launch).
   if (hipMemsetAsync(h->base + h->lay.lens_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.nnew_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
+      hipMemsetAsync(h->base + h->lay.first_off, 0, (size_t)cfg->batch * 4, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.cnt_off, 0, h->lay.cnt_bytes, s) != hipSuccess ||
       hipMemsetAsync(h->base + h->lay.flags_off, 0, 4, s) != hipSuccess ||
       hipStreamSynchronize(s) != hipSuccess) {
@@ -365,9 +374,81 @@ int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream) 
   if (n_rows == 0) return KVC_OK;
   if (!use_device(h)) return KVC_E_HIP;
   int32_t *lens = reinterpret_cast<int32_t *>(h->base + h->lay.lens_off);
-  int err = kvc::launch_reset_rows(lens, rows_host, n_rows, stream);
+  int32_t *first = reinterpret_cast<int32_t *>(h->base + h->lay.first_off);
+  int err = kvc::launch_reset_rows(lens, first, rows_host, n_rows, stream);
   if (err) return KVC_E_HIP;
-  for (int32_t i = 0; i < n_rows; ++i) h->lens_host[rows_host[i]] = 0;
+  for (int32_t i = 0; i < n_rows; ++i) {
+    h->lens_host[rows_host[i]] = 0;
+    h->first_host[rows_host[i]] = 0;
+  }
+  return KVC_OK;
+}
+
+int kvc_set_first(kvc_t *h, const int32_t *rows_host, const int32_t *first_host, int32_t n_rows,
+                  void *stream) {
+  if (!h || n_rows < 0 || (n_rows > 0 && (!rows_host || !first_host))) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (rows_host[i] < 0 || rows_host[i] >= h->cfg.batch || first_host[i] < 0 ||
+        first_host[i] > h->cfg.max_len)
+      return KVC_E_ARG;
+  if (n_rows == 0) return KVC_OK;
+  if (!use_device(h)) return KVC_E_HIP;
+  int32_t *first = reinterpret_cast<int32_t *>(h->base + h->lay.first_off);
+  if (kvc::launch_set_first(first, rows_host, first_host, n_rows, stream)) return KVC_E_HIP;
+  for (int32_t i = 0; i < n_rows; ++i) h->first_host[rows_host[i]] = first_host[i];
+  return KVC_OK;
+}
+
+int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src, const int32_t *src_rows,
+              int32_t n_rows, void *stream) {
+  if (!dst || !src || n_rows < 0 || (n_rows > 0 && (!dst_rows || !src_rows))) return KVC_E_ARG;
+  if (dst->in_step || src->in_step || dst->lens_stale || src->lens_stale) return KVC_E_STATE;
+  const kvc_config &a = dst->cfg, &b = src->cfg;
+  if (a.n_layer != b.n_layer || a.head_dim != b.head_dim || a.dtype != b.dtype ||
+      a.n_q_head != b.n_q_head || dst->device != src->device)
+    return KVC_E_ARG;
+  for (int32_t l = 0; l < a.n_layer; ++l) {
+    const LayerLayout &x = dst->lay.layers[l], &y = src->lay.layers[l];
+    if (x.hkv != y.hkv || x.window != y.window || x.ring != y.ring) return KVC_E_ARG;
+  }
+  std::vector<uint8_t> seen(a.batch, 0);
+  for (int32_t i = 0; i < n_rows; ++i) {
+    const int32_t d = dst_rows[i], r = src_rows[i];
+    if (d < 0 || d >= a.batch || r < 0 || r >= b.batch || seen[d]) return KVC_E_ARG;
+    seen[d] = 1;
+    if (src->lens_host[r] > a.max_len) return KVC_E_FULL;
+  }
+  if (dst == src)  // a row must not be both read and written
+    for (int32_t i = 0; i < n_rows; ++i)
+      if (seen[src_rows[i]]) return KVC_E_ARG;
+  if (n_rows == 0) return KVC_OK;
+  if (!use_device(dst)) return KVC_E_HIP;
+  const int s = kvc::dtype_bytes(a.dtype);
+  for (int32_t off = 0; off < n_rows; off += 64) {
+    kvc::CopyPairs pairs{};
+    const int32_t m = std::min<int32_t>(64, n_rows - off);
+    for (int32_t l = 0; l < a.n_layer; ++l) {
+      const kvc::LayerArgs dl = layer_args(dst, l), sl = layer_args(src, l);
+      for (int32_t j = 0; j < m; ++j) {
+        pairs.src_row[j] = src_rows[off + j];
+        pairs.dst_row[j] = dst_rows[off + j];
+        const int64_t top = std::min<int64_t>(src->lens_host[src_rows[off + j]], sl.rows);
+        pairs.rows[j] = (int32_t)round_up(top, kvc::kRowAlign);
+      }
+      if (kvc::launch_copy_rows(dl, sl, a.head_dim, s, pairs, m, stream)) return KVC_E_HIP;
+    }
+    if (kvc::launch_copy_state(reinterpret_cast<int32_t *>(dst->base + dst->lay.lens_off),
+                               reinterpret_cast<int32_t *>(dst->base + dst->lay.first_off),
+                               reinterpret_cast<const int32_t *>(src->base + src->lay.lens_off),
+                               reinterpret_cast<const int32_t *>(src->base + src->lay.first_off),
+                               pairs, m, stream))
+      return KVC_E_HIP;
+  }
+  for (int32_t i = 0; i < n_rows; ++i) {
+    dst->lens_host[dst_rows[i]] = src->lens_host[src_rows[i]];
+    dst->first_host[dst_rows[i]] = src->first_host[src_rows[i]];
+  }
   return KVC_OK;
 }
 
@@ -502,7 +583,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       const int64_t L = h->lens_host[b], n = h->n_new[b];
       int64_t base, hi;
       if (n >= 2 && !la.ring) {
-        chunk_span(la, L, n, &base, &hi);
+        chunk_span(la, L, n, h->first_host[b], &base, &hi);
         max_chunk_span = std::max(max_chunk_span, hi - base);
       }
     }
@@ -516,13 +597,13 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       const int64_t L = h->lens_host[b], n = h->n_new[b];
       int64_t base, hi;
       if (n == 1) {
-        decode_span(la, L, &base, &hi);
+        decode_span(la, L, h->first_host[b], &base, &hi);
         dec_items += ceil_div(hi - base, pa.dec_split_keys);
       } else if (n >= 2) {
         const int64_t nqt = ceil_div(n * la.rep, kvc::kChunkQTile);
         int64_t nks = 1;
         if (!la.ring) {
-          chunk_span(la, L, n, &base, &hi);
+          chunk_span(la, L, n, h->first_host[b], &base, &hi);
           nks = ceil_div(hi - base, pa.pre_split_keys);
         }
         pre_items += nqt * nks;
@@ -577,7 +658,7 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
     for (int32_t b = 0; b < B; ++b) {
       if (h->n_new[b] == 1) {
         int64_t base, hi;
-        decode_span(la, h->lens_host[b], &base, &hi);
+        decode_span(la, h->lens_host[b], h->first_host[b], &base, &hi);
         items += ceil_div(hi - base, pa.dec_split_keys);
       } else {
         items += 1;  // idle row: its padded token and zero outputs
@@ -636,6 +717,7 @@ int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream) {
   a.n_src = n_new_dev;
   a.n_new = reinterpret_cast<int32_t *>(h->base + h->lay.nnew_off);
   a.lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
+  a.first = reinterpret_cast<const int32_t *>(h->base + h->lay.first_off);
   a.flags = reinterpret_cast<int32_t *>(h->base + h->lay.flags_off);
   a.plan_sk = reinterpret_cast<int32_t *>(h->base + h->lay.plan_off);
   a.plan_order = h->cfg.batch <= kvc::kDecodeOrderMax

@@ -43,6 +43,7 @@ struct Layout {
   int64_t rope_off = -1;      // float2 (cos, sin) [max_len][D/2], fp32
   int64_t lens_off = 0;       // int32 [B]
   int64_t nnew_off = 0;       // int32 [B]
+  int64_t first_off = 0;      // int32 [B]: left padding per row
   int64_t dml_off = 0;        // float2 (m, l) [B][Hq][kDecodeSplitCap]
   int64_t dout_off = 0;       // float [B][Hq][kDecodeSplitCap][D]
   int64_t cnt_off = 0;        // int32 [B][max Hkv]: split arrivals (fused decode), 0 between launches
@@ -71,6 +72,7 @@ struct LayerArgs {
 struct StepArgs {
   const int32_t *lens;    // device [B]
   const int32_t *n_new;   // device [B]
+  const int32_t *first;   // device [B]: left padding (keys before it hidden)
   const float *rope;      // device float2 table or nullptr (no rotation)
   int32_t B, C, Hq, D, max_len;
 };
@@ -112,6 +114,7 @@ struct StaticBeginArgs {
   const int32_t *n_src;   // the caller's counts [B] (device)
   int32_t *n_new;         // the step's counts [B]
   const int32_t *lens;    // [B]
+  const int32_t *first;   // [B]
   int32_t *flags;         // sticky error bits
   int32_t *plan_sk;       // [n_class] keys per split
   uint16_t *plan_order;   // [n_class][B] dispatch order, or null (B > kDecodeOrderMax)
@@ -138,7 +141,23 @@ struct Launch {
 
 // Launchers (kernels.hip).  Return hipError_t as int (0 = success).
 int launch_set_rows(int32_t *dst, const int32_t *vals, int32_t n, void *stream);
-int launch_reset_rows(int32_t *lens, const int32_t *rows, int32_t n, void *stream);
+// Empties rows: length and left padding 0.
+int launch_reset_rows(int32_t *lens, int32_t *first, const int32_t *rows, int32_t n, void *stream);
+// first[rows[i]] = vals[i].
+int launch_set_first(int32_t *first, const int32_t *rows, const int32_t *vals, int32_t n,
+                     void *stream);
+// Row copies between two caches of the same layer shapes: per pair j, the
+// first `rows[j]` storage rows (a multiple of 32) of every KV head of row
+// src_row[j] (K rows and V blocks), into row dst_row[j].
+struct CopyPairs {
+  int32_t src_row[64], dst_row[64], rows[64];
+};
+int launch_copy_rows(const LayerArgs &dst, const LayerArgs &src, int D, int dtype_bytes,
+                     const CopyPairs &pairs, int32_t n_pairs, void *stream);
+// lens / first of dst_row[j] = those of src_row[j] (device arrays).
+int launch_copy_state(int32_t *dst_lens, int32_t *dst_first, const int32_t *src_lens,
+                      const int32_t *src_first, const CopyPairs &pairs, int32_t n_pairs,
+                      void *stream);
 int launch_advance(int32_t *lens, const int32_t *n_new, int32_t B, void *stream);
 int launch_static_begin(const StaticBeginArgs &a, void *stream);
 int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void *k,

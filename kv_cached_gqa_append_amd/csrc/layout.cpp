@@ -92,7 +92,8 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
   } else {
     lay->rope_off = -1;
   }
-  if (!take(&cur, B * 4, &lay->lens_off) || !take(&cur, B * 4, &lay->nnew_off))
+  if (!take(&cur, B * 4, &lay->lens_off) || !take(&cur, B * 4, &lay->nnew_off) ||
+      !take(&cur, B * 4, &lay->first_off))
     return KVC_E_ARG;
   const int64_t dq = B * Hq * kDecodeSplitCap;
   if (!take(&cur, dq * 8, &lay->dml_off) || !take(&cur, dq * D * 4, &lay->dout_off))

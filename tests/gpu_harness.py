@@ -111,6 +111,14 @@ class Pair:
         self.cache.reset(rows)
         self.ref.reset(rows)
 
+    def set_first(self, rows, first):
+        self.cache.set_first(rows, first)
+        self.ref.set_first(rows, first)
+
+    def admit(self, rows, src: "Pair", src_rows):
+        self.cache.admit(rows, src.cache, src_rows)
+        self.ref.admit(rows, src.ref, src_rows)
+
     def check_cache_rows(self, layer):
         """Stored K (rotated) and V of every live row against the oracle's raw
         history: V bit-exact; K is the rotation computed in float32 and
