@@ -561,6 +561,64 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
             "kv_nbytes": {"rings": nb_ring, "full": nb_full},
             "entries": legs}
 
+def paged_leg(dev, steps, warmup):
+    """The headline decode workload on a paged cache (a pool of B * max_len / 16
+    pages, the contiguous cache's bytes; rows fill in turns, so their pages
+    interleave in the pool), one-token steps through kvc_append +
+    kvc_attend: the decode kernel's rate with a block-table lookup per tile."""
+    base = wl.DECODE_B64
+    work = base.replace(n_pages=base.batch * base.max_len // 16)
+    lens0, sched = plan_lens(work, steps, warmup, 3)
+    cache = K.Cache(K.config_from_workload(work), dev)
+    fill_history(cache, work, lens0, dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(wl.seed_of(work.name, "paged"))
+    B, D, L = work.batch, work.head_dim, work.n_layer
+    mk = lambda h: torch.randn(B, 1, h, D, generator=g, device=dev).to(work.torch_dtype)
+    qs = [mk(work.n_q_head) for _ in range(L)]
+    ks = [mk(8) for _ in range(L)]
+    vs = [mk(8) for _ in range(L)]
+    outs = [torch.empty_like(x) for x in qs]
+
+    def run_step(n):
+        for l in range(L):
+            cache.append(l, ks[l], vs[l], n)
+            cache.attend(l, qs[l], outs[l])
+        cache.advance()
+
+    for n in sched[:warmup]:
+        run_step(n)
+    torch.cuda.synchronize()
+    lens = np.asarray(cache.lens(), dtype=np.int64)
+    kbytes = sbytes = tokens = 0
+    for n in sched[warmup:warmup + steps]:
+        kbytes += decode_kernel_bytes(lens, n, work) * L
+        sbytes += step_bytes(lens, n, work)
+        tokens += int(n.sum())
+        lens = lens + n
+    K.kvc_timing_begin(cache.handle, steps * L * 4 + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for n in sched[warmup:warmup + steps]:
+        run_step(n)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    kt = K.kvc_timing_end(cache.handle)
+    stats = cache.page_stats()
+    cache.close()
+    dec_ms, dec_n = kt["decode"]
+    gbs = kbytes / (dec_ms / 1e3) / 1e9
+    log(f"[bench] paged decode_b64: {steps} steps, {dt * 1e3 / steps:.3f} ms/step, "
+        f"{tokens / dt:.0f} tok/s, decode kernel {dec_ms * 1e3 / dec_n:.1f} us "
+        f"({gbs:.0f} GB/s); pages {stats}")
+    return {"workload": f"decode_b64 on a paged cache of {work.n_pages} 16-row pages",
+            "entry": "kvc_append+kvc_attend", "steps": steps, "warmup": warmup,
+            "ms_per_step": round(dt * 1e3 / steps, 4), "tokens_per_s": round(tokens / dt, 1),
+            "value": round(sbytes / dt / 1e9, 1), "unit": "GB/s",
+            "kernel": "k_decode<128,4,paged>", "kernel_achieved": round(gbs, 1),
+            "kernel_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "avg_launch_us": round(dec_ms * 1e3 / dec_n, 2), "page_stats": stats}
+
 def graph_leg(cache, work, qs, ks, vs, sched, warmup, steps, step_bytes_fn):
     """One-token steps replayed from a captured HIP graph (kvc_static_begin,
     kvc_append_attend per layer, kvc_advance; counts copied into the graph's
@@ -665,7 +723,9 @@ def main():
                     help="layers of the mixed leg")
     ap.add_argument("--long-decode-steps", type=int, default=32,
                     help="timed steps of the long-context decode leg (0 skips it)")
-    ap.add_argument("--only", choices=("mixed", "long_decode"),
+    ap.add_argument("--paged-steps", type=int, default=24,
+                    help="timed steps of the paged decode leg (0 skips it)")
+    ap.add_argument("--only", choices=("mixed", "long_decode", "paged"),
                     help="run only that leg and print its object")
     ap.add_argument("--fused", action="store_true",
                     help="headline leg through kvc_append_attend (one kernel per layer) instead "
@@ -710,6 +770,9 @@ def main():
     if args.only == "mixed":
         print(json.dumps({"mixed": mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)}),
               flush=True)
+        return
+    if args.only == "paged":
+        print(json.dumps({"paged": paged_leg(dev, args.paged_steps, args.warmup)}), flush=True)
         return
     if args.only == "long_decode":
         print(json.dumps({"long_decode": long_decode_leg(dev, args.long_decode_steps, 4)}),
@@ -826,6 +889,10 @@ def main():
     if args.prefill_chunks > 0:
         prefill = prefill_leg(dev, args.prefill_chunks)
         torch.cuda.empty_cache()
+    paged = None
+    if args.paged_steps > 0:
+        paged = paged_leg(dev, args.paged_steps, args.warmup)
+        torch.cuda.empty_cache()
     mixed = None
     if args.mixed_steps > 0:
         mixed = mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)
@@ -875,6 +942,7 @@ def main():
         "other_entry_point": other,
         "graph": graph,
         "prefill": prefill,
+        "paged": paged,
         "mixed": mixed,
         "long_decode": long_decode,
         "cpu_baseline": cpu,

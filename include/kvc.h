@@ -89,7 +89,18 @@ typedef struct {
                                the window is applied as a mask only           */
   double rope_base;         /* > 0: RoPE with theta_d = base^(-2d/D), half-split
                                pairs (d, d+D/2); 0: q and k arrive rotated      */
+  int32_t n_pages;          /* 0: every row keeps max_len rows per full layer.
+                               > 0: paged cache ("Lab 07 - KV cache and
+                               sampling", Stretch: fixed 16-token blocks and a
+                               per-sequence block table): the full-layout
+                               layers (all but rings) share a pool of n_pages
+                               16-row pages, handed to rows as they grow and
+                               returned by kvc_reset; one block table per row
+                               serves every such layer                          */
 } kvc_config;
+
+/* Rows per page of a paged cache. */
+enum { KVC_PAGE_ROWS = 16 };
 
 /* Size in bytes for `what` (KVC_NB_KV or KVC_NB_ALLOC); 0 if cfg is invalid.
  * Pure host computation. */
@@ -147,7 +158,9 @@ int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src,
  *                 in (full layer: pos or max_len for padding; ring layer:
  *                 pos % W for the last W real tokens, else W).
  * The first append of a step checks capacity (lens[b] + n_new[b] <= max_len
- * for every row, else KVC_E_FULL) and latches n_new and C; every other append
+ * for every row, and on a paged cache enough free pages for the rows' new
+ * positions, else KVC_E_FULL with nothing taken) and latches n_new and C
+ * (and takes the pages); every other append
  * of the step must pass the same values (else KVC_E_STATE).  Each layer is
  * appended once per step. */
 int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
@@ -183,6 +196,22 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k,
 /* End the step: lens[b] += n_new[b] on the device and in the host mirror.
  * Every layer must have been appended and attended (else KVC_E_STATE). */
 int kvc_advance(kvc_t *h, void *stream);
+
+/* Paged caches: page use in tokens (tinyllm "kv_cache.py" SlotKVCache:
+ * used_tokens / allocated_tokens / reserved_tokens).  used = sum of the row
+ * lengths; allocated = pages held by rows x 16; reserved = n_pages x 16 (an
+ * unpaged cache reports B x max_len for both allocated and reserved).
+ * Host mirrors only (KVC_E_STATE while the lengths mirror is stale). */
+int kvc_page_stats(const kvc_t *h, int64_t *used, int64_t *allocated, int64_t *reserved);
+
+/* Paged caches: give rows rows_host[i] pages for at least tokens_host[i]
+ * positions (pages are otherwise taken by the appends that need them), so
+ * that later static steps, which cannot take pages, have room; a static step
+ * rejects a row without a page for its token (KVC_STATIC_FULL).  KVC_E_FULL
+ * (nothing taken) if the pool runs short or a count passes max_len.  Not
+ * inside a step; a no-op on an unpaged cache. */
+int kvc_reserve(kvc_t *h, const int32_t *rows_host, const int32_t *tokens_host, int32_t n_rows,
+                void *stream);
 
 /* Copy the host mirror of the row lengths into lens_host[B].  KVC_E_STATE
  * while the mirror is behind the device (after a static step, until

@@ -59,6 +59,7 @@ class KvcConfig(ctypes.Structure):
         ("window", ctypes.POINTER(ctypes.c_int32)),
         ("use_ring", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
+        ("n_pages", ctypes.c_int32),
     ]
 
 
@@ -122,6 +123,10 @@ def lib():
         L.kvc_set_first.restype = ctypes.c_int
         L.kvc_admit.argtypes = [VP, P(I32), VP, P(I32), I32, VP]
         L.kvc_admit.restype = ctypes.c_int
+        L.kvc_page_stats.argtypes = [VP, P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]
+        L.kvc_page_stats.restype = ctypes.c_int
+        L.kvc_reserve.argtypes = [VP, P(I32), P(I32), I32, VP]
+        L.kvc_reserve.restype = ctypes.c_int
         L.kvc_static_begin.argtypes = [VP, VP, VP]
         L.kvc_static_begin.restype = ctypes.c_int
         L.kvc_static_status.argtypes = [VP, P(I32), VP]
@@ -162,7 +167,7 @@ def _check(code: int, what: str) -> None:
 
 
 def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
-                n_kv_head, window, use_ring=True, rope_base=10000.0) -> KvcConfig:
+                n_kv_head, window, use_ring=True, rope_base=10000.0, n_pages=0) -> KvcConfig:
     """A ``KvcConfig`` that keeps its per-layer arrays alive."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
@@ -175,7 +180,8 @@ def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
     hk = (ctypes.c_int32 * len(n_kv_head))(*[int(x) for x in n_kv_head])
     wn = (ctypes.c_int32 * len(window))(*[int(x) for x in window])
     cfg = KvcConfig(int(n_layer), int(batch), int(n_q_head), int(head_dim), int(max_len),
-                    int(max_chunk), int(dtype), hk, wn, int(bool(use_ring)), float(rope_base))
+                    int(max_chunk), int(dtype), hk, wn, int(bool(use_ring)), float(rope_base),
+                    int(n_pages))
     cfg._keep = (hk, wn)
     return cfg
 
@@ -183,7 +189,8 @@ def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
 def config_from_workload(w) -> KvcConfig:
     """Config for a ``workloads.Workload``."""
     return make_config(w.n_layer, w.batch, w.n_q_head, w.head_dim, w.max_len, w.max_chunk,
-                       w.dtype, list(w.n_kv_head), list(w.window), w.use_ring, w.rope_base)
+                       w.dtype, list(w.n_kv_head), list(w.window), w.use_ring, w.rope_base,
+                       getattr(w, "n_pages", 0))
 
 
 def kvc_nbytes(cfg: KvcConfig, what: int = KVC_NB_KV) -> int:
@@ -265,6 +272,21 @@ def kvc_admit(dst, dst_rows, src, src_rows, stream=None) -> None:
     if n != m:
         raise ValueError("one source row per row")
     _check(lib().kvc_admit(dst, d, src, r, n, _stream_handle(stream)), "kvc_admit")
+
+
+def kvc_page_stats(h):
+    u, a, r = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().kvc_page_stats(h, ctypes.byref(u), ctypes.byref(a), ctypes.byref(r)),
+           "kvc_page_stats")
+    return {"used": int(u.value), "allocated": int(a.value), "reserved": int(r.value)}
+
+
+def kvc_reserve(h, rows, tokens, stream=None) -> None:
+    r, n = _rows_array(rows)
+    t, m = _rows_array(tokens)
+    if n != m:
+        raise ValueError("one token count per row")
+    _check(lib().kvc_reserve(h, r, t, n, _stream_handle(stream)), "kvc_reserve")
 
 
 def kvc_static_begin(h, n_new_dev: torch.Tensor, stream=None) -> None:
@@ -430,6 +452,14 @@ class Cache:
     def reset(self, rows, stream=None):
         """Empty rows (release slots): length and left padding 0."""
         kvc_reset(self.handle, rows, stream)
+
+    def page_stats(self):
+        """Token counts: used (row lengths), allocated (pages held), reserved (pool)."""
+        return kvc_page_stats(self.handle)
+
+    def reserve(self, rows, tokens, stream=None):
+        """Paged cache: pages for at least ``tokens`` positions of each row."""
+        kvc_reserve(self.handle, rows, tokens, stream)
 
     def set_first(self, rows, first, stream=None):
         """Rows start with ``first`` left-pad positions (hidden keys)."""

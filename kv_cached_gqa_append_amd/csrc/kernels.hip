@@ -135,6 +135,30 @@ __device__ __forceinline__ T *v_elem(char *base, int64_t bg, int rows_alloc, int
   return v_block<T>(base, bg, rows_alloc, r / kVBlock, D) + d * kVBlock + (r % kVBlock);
 }
 
+// Element offset of the 16-row block holding storage row r of KV head g of
+// row b in a layer's K or V region (r == rows: the scratch row).  Both
+// layouts keep a block's 16 K rows, and its V block, contiguous; a paged
+// layer finds the block's page in the block table (the scratch row in the
+// scratch page), a full one at its place in the head's region.
+__device__ __forceinline__ int64_t row_block_elem(const LayerArgs &la, int b, int g, int64_t r,
+                                                  int D) {
+  if (la.paged) {
+    const int64_t pg = r < la.rows ? la.table[(int64_t)b * la.ppr + r / kPageRows]
+                                   : (int64_t)la.scratch_page;
+    return (pg * la.hkv + g) * kPageRows * D;
+  }
+  return (((int64_t)b * la.hkv + g) * la.rows_alloc + r / kPageRows * kPageRows) * D;
+}
+template <typename T>
+__device__ __forceinline__ T *krow_ptr(const LayerArgs &la, int b, int g, int64_t r, int D) {
+  return reinterpret_cast<T *>(la.k) + row_block_elem(la, b, g, r, D) + (r % kPageRows) * D;
+}
+// V element (r, d) of the head is at vcol_ptr(...)[d * kVBlock].
+template <typename T>
+__device__ __forceinline__ T *vcol_ptr(const LayerArgs &la, int b, int g, int64_t r, int D) {
+  return reinterpret_cast<T *>(la.v) + row_block_elem(la, b, g, r, D) + (r % kPageRows);
+}
+
 // Position held by ring slot s before this step's commit, L = tokens so far:
 // the latest t < L with t % W == s (negative: the slot is empty).
 __device__ __forceinline__ int64_t ring_slot_pos(int64_t s, int64_t L, int W) {
@@ -211,21 +235,41 @@ __global__ void k_set_first(int32_t *first, I32Chunk rows, I32Chunk vals, int32_
   if (i < n) first[rows.v[i]] = vals.v[i];
 }
 
-// Grid (pairs x KV heads, 2 (K, V), z): each block copies a strided share of
-// the first rows[j] storage rows of one head's K (y = 0) or V (y = 1) region;
-// both regions keep a head's rows contiguous from row 0 (V in whole 16-row
-// blocks), so the copy is a flat run of 16-byte units.
-__global__ __launch_bounds__(256) void k_copy_rows(LayerArgs dst, LayerArgs src, int32_t row_bytes,
-                                                   CopyPairs pr) {
+// Grid (pairs x KV heads, 2 (K, V), blocks): one 16-row block (K rows or V
+// block, contiguous in either layout) of one head of one pair per workgroup.
+__global__ __launch_bounds__(256) void k_copy_rows(LayerArgs dst, LayerArgs src, int32_t D,
+                                                   int32_t row_bytes, CopyPairs pr) {
   const int j = blockIdx.x / src.hkv, g = blockIdx.x % src.hkv;
-  const char *sb = (blockIdx.y ? src.v : src.k) +
-                   ((int64_t)pr.src_row[j] * src.hkv + g) * src.rows_alloc * row_bytes;
-  char *db = (blockIdx.y ? dst.v : dst.k) +
-             ((int64_t)pr.dst_row[j] * dst.hkv + g) * dst.rows_alloc * row_bytes;
-  const int64_t units = (int64_t)pr.rows[j] * row_bytes / 16;
-  for (int64_t u = (int64_t)blockIdx.z * blockDim.x + threadIdx.x; u < units;
-       u += (int64_t)gridDim.z * blockDim.x)
+  const int64_t blk = blockIdx.z;
+  if (blk >= pr.blocks[j]) return;
+  const int64_t r = blk * kPageRows;
+  const int es = row_bytes / D;  // element size
+  const char *sb = (blockIdx.y ? src.v : src.k) + row_block_elem(src, pr.src_row[j], g, r, D) * es;
+  char *db = (blockIdx.y ? dst.v : dst.k) + row_block_elem(dst, pr.dst_row[j], g, r, D) * es;
+  const int units = kPageRows * row_bytes / 16;
+  for (int u = threadIdx.x; u < units; u += blockDim.x)
     reinterpret_cast<uint4 *>(db)[u] = reinterpret_cast<const uint4 *>(sb)[u];
+}
+
+// Block-table and capacity updates (workgroup 0) and the zeroing of V of
+// newly taken pages, one page per further workgroup, in every paged layer.
+__global__ __launch_bounds__(256) void k_page_update(int32_t *table, int32_t *cap, I32Chunk cap_rows,
+                                                     I32Chunk cap_vals, int32_t n_cap, PageUpdate u,
+                                                     int32_t n_upd, PagedPools pools,
+                                                     int64_t page_bytes) {
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < n_upd; i += blockDim.x) table[u.idx[i]] = u.page[i];
+    for (int i = threadIdx.x; i < n_cap; i += blockDim.x) cap[cap_rows.v[i]] = cap_vals.v[i];
+    return;
+  }
+  const int k = blockIdx.x - 1;
+  if (k >= n_upd || u.zero[k] < 0) return;
+  const int64_t pg = u.zero[k];
+  for (int l = 0; l < pools.n; ++l) {
+    const int64_t bytes = page_bytes * pools.hkv[l];
+    uint4 *dst = reinterpret_cast<uint4 *>(pools.v[l] + pg * bytes);
+    for (int64_t e = threadIdx.x; e < bytes / 16; e += blockDim.x) dst[e] = make_uint4(0, 0, 0, 0);
+  }
 }
 
 __global__ void k_copy_state(int32_t *dst_lens, int32_t *dst_first, const int32_t *src_lens,
@@ -283,17 +327,34 @@ int launch_set_first(int32_t *first, const int32_t *rows, const int32_t *vals, i
 int launch_copy_rows(const LayerArgs &dst, const LayerArgs &src, int D, int dtype_bytes,
                      const CopyPairs &pairs, int32_t n_pairs, void *stream) {
   if (n_pairs < 1 || n_pairs > 64 || dst.hkv != src.hkv) return (int)hipErrorInvalidValue;
-  const int32_t row_bytes = D * dtype_bytes;
   int32_t most = 0;
   for (int32_t j = 0; j < n_pairs; ++j) {
-    if (pairs.rows[j] > src.rows_alloc || pairs.rows[j] > dst.rows_alloc || pairs.rows[j] < 0)
+    const int64_t rows = (int64_t)pairs.blocks[j] * kPageRows;
+    if (pairs.blocks[j] < 0 || (!src.paged && rows > src.rows_alloc) ||
+        (!dst.paged && rows > dst.rows_alloc) || (src.paged && rows > (int64_t)src.ppr * kPageRows) ||
+        (dst.paged && rows > (int64_t)dst.ppr * kPageRows))
       return (int)hipErrorInvalidValue;
-    most = pairs.rows[j] > most ? pairs.rows[j] : most;
+    most = pairs.blocks[j] > most ? pairs.blocks[j] : most;
   }
-  const int64_t units = (int64_t)most * row_bytes / 16;
-  const unsigned z = (unsigned)(units / 2048 < 1 ? 1 : (units / 2048 > 64 ? 64 : units / 2048));
-  hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)(n_pairs * src.hkv), 2, z), dim3(256), 0,
-                     (hipStream_t)stream, dst, src, row_bytes, pairs);
+  if (most == 0) return 0;
+  hipLaunchKernelGGL(k_copy_rows, dim3((unsigned)(n_pairs * src.hkv), 2, (unsigned)most), dim3(256),
+                     0, (hipStream_t)stream, dst, src, (int32_t)D, (int32_t)(D * dtype_bytes), pairs);
+  return (int)hipGetLastError();
+}
+
+int launch_page_update(int32_t *table, int32_t *cap, const int32_t *cap_rows, const int32_t *cap_vals,
+                       int32_t n_cap, const PageUpdate &u, int32_t n_upd, const PagedPools &pools,
+                       int64_t page_bytes, void *stream) {
+  if (n_cap < 0 || n_cap > 256 || n_upd < 0 || n_upd > 64) return (int)hipErrorInvalidValue;
+  I32Chunk cr, cv;
+  std::memset(&cr, 0, sizeof(cr));
+  std::memset(&cv, 0, sizeof(cv));
+  if (n_cap) {
+    std::memcpy(cr.v, cap_rows, sizeof(int32_t) * n_cap);
+    std::memcpy(cv.v, cap_vals, sizeof(int32_t) * n_cap);
+  }
+  hipLaunchKernelGGL(k_page_update, dim3((unsigned)(1 + n_upd)), dim3(256), 0, (hipStream_t)stream,
+                     table, cap, cr, cv, n_cap, u, n_upd, pools, page_bytes);
   return (int)hipGetLastError();
 }
 
@@ -349,7 +410,7 @@ __global__ __launch_bounds__(64) void k_static_begin(StaticBeginArgs a) {
     const int n = a.n_src[b];
     if (n < 0 || n > 1)
       bad |= kStaticBadCount;
-    else if ((int64_t)a.lens[b] + n > a.max_len)
+    else if ((int64_t)a.lens[b] + n > a.max_len || (a.cap && a.lens[b] + n > a.cap[b]))
       bad |= kStaticFull;
   }
   bad = __builtin_amdgcn_readfirstlane(wave_or_i(bad));
@@ -456,7 +517,8 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
   // a new tile, zero V in the rest of that tile.  The rows zeroed here are
   // beyond every row this append writes (only the scratch row may coincide,
   // and both writes are finite).
-  if (i == 0 && n >= 1) {
+  // (A paged layer's pages have V zeroed when a row takes them.)
+  if (i == 0 && n >= 1 && !la.paged) {
     const int64_t W = la.window;
     const int64_t old_top = la.ring ? (L < W ? L : W) : L;
     const int64_t new_top = la.ring ? (L + n < W ? L + n : W) : L + n;
@@ -469,27 +531,21 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
           *v_elem<T>(la.v, bgz, la.rows_alloc, rz, d, st.D) = from_f<T>(0.f);
     }
   }
-  int64_t r;
-  char *kreg, *vreg;
-  int ralloc;
+  const int64_t bg = (int64_t)b * la.hkv + g;
+  T *kd, *vd;
   if (staged) {
     if (!valid) return;  // staging rows of padding are never read
-    r = i;
-    kreg = la.sk;
-    vreg = la.sv;
-    ralloc = la.stage_rows_alloc;
+    kd = k_row<T>(la.sk, bg, la.stage_rows_alloc, i, D);
+    vd = v_elem<T>(la.sv, bg, la.stage_rows_alloc, i, 0, D);
   } else {
+    int64_t r;
     if (la.ring)
       r = valid ? p % la.window : la.window;
     else
       r = valid ? p : la.rows;
-    kreg = la.k;
-    vreg = la.v;
-    ralloc = la.rows_alloc;
+    kd = krow_ptr<T>(la, b, g, r, D);
+    vd = vcol_ptr<T>(la, b, g, r, D);
   }
-  const int64_t bg = (int64_t)b * la.hkv + g;
-  T *kd = k_row<T>(kreg, bg, ralloc, r, D);
-  T *vd = v_elem<T>(vreg, bg, ralloc, r, 0, D);
   const T *ks = k + row * D;
   const T *vs = v + row * D;
   const bool rot = st.rope != nullptr && valid;
@@ -643,8 +699,7 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
     for (int64_t s = 0; s < nh; ++s) {
       const int64_t pos = ring_slot_pos(s, L, W);
       if (pos < 0 || p - pos >= W || hidden(pos)) continue;
-      generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, s, D),
-                  v_elem<T>(la.v, bg, la.rows_alloc, s, 0, D), D, scale);
+      generic_key(S, krow_ptr<T>(la, b, g, s, D), vcol_ptr<T>(la, b, g, s, D), D, scale);
     }
     // ... and the chunk's own rows from staging
     for (int j = 0; j <= i; ++j) {
@@ -658,15 +713,13 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
     const int64_t hi = p + 1 < W ? p + 1 : W;
     for (int64_t s = 0; s < hi; ++s) {
       if (hidden(p - (p - s) % W)) continue;
-      generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, s, D),
-                  v_elem<T>(la.v, bg, la.rows_alloc, s, 0, D), D, scale);
+      generic_key(S, krow_ptr<T>(la, b, g, s, D), vcol_ptr<T>(la, b, g, s, D), D, scale);
     }
   } else {
     const int64_t lo = W > 0 ? (p - W + 1 > 0 ? p - W + 1 : 0) : 0;
     for (int64_t t = lo; t <= p; ++t) {
       if (hidden(t)) continue;
-      generic_key(S, k_row<T>(la.k, bg, la.rows_alloc, t, D),
-                  v_elem<T>(la.v, bg, la.rows_alloc, t, 0, D), D, scale);
+      generic_key(S, krow_ptr<T>(la, b, g, t, D), vcol_ptr<T>(la, b, g, t, D), D, scale);
     }
   }
   const float inv = 1.f / S.l;
@@ -947,15 +1000,15 @@ __device__ __forceinline__ void store_token_row(const LayerArgs &la, const Fused
                             : (valid ? p : (int64_t)la.rows);
   constexpr int half = D / 2;
   if (lane < half) {
-    bf16 *kd = k_row<bf16>(la.k, bg, la.rows_alloc, r, D);
-    bf16 *vd = v_elem<bf16>(la.v, bg, la.rows_alloc, r, 0, D);
+    bf16 *kd = krow_ptr<bf16>(la, b, g, r, D);
+    bf16 *vd = vcol_ptr<bf16>(la, b, g, r, D);
     kd[lane] = (bf16)y1;
     kd[lane + half] = (bf16)y2;
     vd[lane * kVBlock] = valid ? v1 : (bf16)0.f;
     vd[(lane + half) * kVBlock] = valid ? v2 : (bf16)0.f;
   }
   if (fa.slot_out && g == 0 && lane == 0) fa.slot_out[b] = (int32_t)r;
-  if (valid) {
+  if (valid && !la.paged) {  // (pages have V zeroed when taken)
     const int64_t W = la.window;
     const int64_t old_top = la.ring ? (p < W ? p : W) : p;
     const int64_t new_top = la.ring ? (p + 1 < W ? p + 1 : W) : p + 1;
@@ -1105,11 +1158,13 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
 // column, slot report); rows with n_new == 0 get one item that writes their
 // padded token to the scratch row and zero outputs; and the last split of a
 // (row, KV head) to finish combines the splits into the output.
-template <int D, int REP, bool FUSED = false, int NBUF = DecodeShape<D, REP>::NBUF,
-          int WAVES = DecodeShape<D, REP>::WAVES>
+// PAGED: a paged full layer; each 16-row tile is one page, found in the
+// block table when the tile's loads are issued.
+template <int D, int REP, bool FUSED = false, bool PAGED = false,
+          int NBUF = DecodeShape<D, REP>::NBUF, int WAVES = DecodeShape<D, REP>::WAVES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
-              FusedArgs fa) {
+              FusedArgs fa, const int32_t *__restrict__ ptab) {
   using S = DecodeShape<D, REP>;
   constexpr int LK = S::LK, KR = S::KR, TK = S::TK, NR = S::NR, NCH = S::NCH, VT = S::VT;
   constexpr int HPL = S::HPL;
@@ -1247,12 +1302,26 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     u32x4 v[VT];
   };
   constexpr int LPT = NR * NCH + VT;  // loads per tile
+  constexpr int page_b = kPageRows * D * 2;  // bytes of one head's page (K or V)
   auto load = [&](int it, Tile &T) {
     const bool live = it < n_iter;
     const int t0 = t_begin + (live ? it : 0) * t_stride;
-    const i32x4 ka = live ? rk : rk_none, va = live ? rv : rv_none;
-    // K rows and V blocks advance by the same bytes per row
-    const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
+    i32x4 ka, va;
+    int so;
+    if constexpr (PAGED) {
+      // the tile's page (a scalar load: the table is read-only here); its K
+      // rows and V block start the page's head slice
+      const int pg = ptab[(int64_t)b * la.ppr + t0 / kPageRows];
+      const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
+      ka = live ? sgpr_rsrc(la.k + off, page_b) : rk_none;
+      va = live ? sgpr_rsrc(la.v + off, page_b) : rv_none;
+      so = 0;
+    } else {
+      ka = live ? rk : rk_none;
+      va = live ? rv : rv_none;
+      // K rows and V blocks advance by the same bytes per row
+      so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
+    }
     static_for<0, NR>([&](auto r) {
       static_for<0, NCH>([&](auto t) {
         constexpr int off = decltype(r)::value * KR * D * 2 + decltype(t)::value * LK * 16;
@@ -1499,7 +1568,12 @@ static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const Parti
                             const void *q, int32_t n_items, const Launch &lc) {
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
                                      : dim3((unsigned)n_items, (unsigned)la.hkv);
-  launch_kernel((k_decode<D, REP>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, FusedArgs{});
+  if (la.paged)
+    launch_kernel((k_decode<D, REP, false, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q,
+                  FusedArgs{}, la.table);
+  else
+    launch_kernel((k_decode<D, REP>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, FusedArgs{},
+                  la.table);
 }
 
 template <int D, int REP>
@@ -1508,7 +1582,12 @@ static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const
                                   const Launch &lc) {
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
                                      : dim3((unsigned)n_items, (unsigned)la.hkv);
-  launch_kernel((k_decode<D, REP, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, fa);
+  if (la.paged)
+    launch_kernel((k_decode<D, REP, true, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q,
+                  fa, la.table);
+  else
+    launch_kernel((k_decode<D, REP, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, fa,
+                  la.table);
 }
 
 template <int D, int REP>
@@ -1580,9 +1659,12 @@ struct KeySeg {
   int kind;                 // 0: position = row; 1: ring history; 2: staging (pos = L + row)
 };
 
-template <int D, int REP>
+// PAGED: a paged full layer; a 32-row tile spans two pages, and the chunks
+// each wave loads lie in one of them.
+template <int D, int REP, bool PAGED = false>
 __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
-                                               const bf16 *__restrict__ q) {
+                                               const bf16 *__restrict__ q,
+                                               const int32_t *__restrict__ ptab) {
   constexpr int NDS = D / 32;              // 32-wide d steps (QK contraction)
   constexpr int NDB = D / 16;              // 16-wide d blocks (PV output)
   constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
@@ -1742,6 +1824,12 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   // Threads past a tile's chunk count (D < 128: whole waves) load nothing.
   const bool loader = wave * 64 < KCH;
   const int voffs = tid * 16;
+  // paged: bytes of one head's page, the page of the tile this wave's chunks
+  // fall in (K row tid / (D / 8) and V block tid / (2 D) agree), and the
+  // chunk's offset inside it
+  constexpr int page_b = kPageRows * D * 2;
+  const int phalf = __builtin_amdgcn_readfirstlane(wave * 32 / D);
+  const int poffs = voffs % page_b;
 
   // Tile i: its segment, first storage row and bounds (uniform scalars).
   struct TileInfo {
@@ -1768,12 +1856,23 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
     const bool second = i >= n0;
     const TileInfo ti = tile_of(live ? i : 0);
     const int64_t t0 = ti.t0;
-    const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
-    const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
-    // K rows and V blocks advance by the same bytes per row
-    const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
-    tile_load<0>(rk, ka, voffs, so);
-    tile_load<0>(rv, va, voffs, so);
+    if constexpr (PAGED) {
+      // this wave's K rows and V block of the tile lie in its page `phalf`
+      const int idx = live ? (int)(t0 / kPageRows) + phalf : 0;
+      const int pg = ptab[(int64_t)b * la.ppr + idx];
+      const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
+      const i32x4 ka = rsrc_sel(live, sgpr_rsrc(la.k + off, page_b), dnone);
+      const i32x4 va = rsrc_sel(live, sgpr_rsrc(la.v + off, page_b), dnone);
+      tile_load<0>(rk, ka, poffs, 0);
+      tile_load<0>(rv, va, poffs, 0);
+    } else {
+      const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
+      const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
+      // K rows and V blocks advance by the same bytes per row
+      const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
+      tile_load<0>(rk, ka, voffs, so);
+      tile_load<0>(rv, va, voffs, so);
+    }
   };
   // Write tile i's chunks (already waited for) to LDS stage s; V rows outside
   // the segment's data are zeroed (their p is 0, and 0 times garbage could be
@@ -1989,7 +2088,12 @@ bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && re
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, const Launch &lc) {
-  launch_kernel((k_chunk<D, REP>), dim3((unsigned)n_items, (unsigned)la.hkv), dim3(512), lc, st, la, pa, (const bf16 *)q);
+  const dim3 grid((unsigned)n_items, (unsigned)la.hkv);
+  if (la.paged)
+    launch_kernel((k_chunk<D, REP, true>), grid, dim3(512), lc, st, la, pa, (const bf16 *)q,
+                  la.table);
+  else
+    launch_kernel((k_chunk<D, REP>), grid, dim3(512), lc, st, la, pa, (const bf16 *)q, la.table);
 }
 
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,

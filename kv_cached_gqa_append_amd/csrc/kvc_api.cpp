@@ -32,6 +32,9 @@ struct kvc_cache {
   int device = 0;
   std::vector<int32_t> lens_host;
   std::vector<int32_t> first_host;  // left padding per row (mirror of the device copy)
+  // paged caches: free pages and the pages each row holds, in block order
+  std::vector<int32_t> free_pages;
+  std::vector<std::vector<int32_t>> row_pages;
   // step state
   bool in_step = false;
   std::vector<int32_t> n_new;
@@ -102,7 +105,114 @@ kvc::LayerArgs layer_args(const kvc_t *h, int layer) {
   la.rows = L.rows;
   la.rows_alloc = L.rows_alloc;
   la.stage_rows_alloc = L.stage_rows_alloc;
+  if (L.paged) {
+    la.paged = 1;
+    la.table = reinterpret_cast<const int32_t *>(h->base + h->lay.table_off);
+    la.ppr = h->lay.pages_per_row;
+    la.scratch_page = h->lay.n_pages + 1;
+  }
   return la;
+}
+
+// -- paged caches: the host page allocator ----------------------------------
+// Pages not held by a row sit in a free list; row b holds row_pages[b] in
+// block order.  Unassigned block-table entries name the zero page (n_pages),
+// so a 32-row tile may read past a row's last page.  A page taken by a row
+// gets V zeroed in every paged layer first (the decode tiles read rows past
+// a row's end, masked, and need them finite).
+
+int32_t zero_page(const kvc_t *h) { return h->lay.n_pages; }
+
+// Enqueue block-table entries (table index -> page; zero: page to clear or
+// -1) and row capacities, in launches of at most 64 entries and 256 rows,
+// once per group of up to 64 paged layers.
+int push_page_updates(kvc_t *h, const std::vector<int32_t> &idx, const std::vector<int32_t> &page,
+                      const std::vector<int32_t> &zero, const std::vector<int32_t> &cap_rows,
+                      const std::vector<int32_t> &cap_vals, void *stream) {
+  int32_t *table = reinterpret_cast<int32_t *>(h->base + h->lay.table_off);
+  int32_t *cap = reinterpret_cast<int32_t *>(h->base + h->lay.cap_off);
+  std::vector<kvc::PagedPools> groups(1);
+  groups[0].n = 0;
+  for (const LayerLayout &L : h->lay.layers) {
+    if (!L.paged) continue;
+    if (groups.back().n == 64) {
+      groups.emplace_back();
+      groups.back().n = 0;
+    }
+    kvc::PagedPools &g = groups.back();
+    g.v[g.n] = h->base + L.v_off;
+    g.hkv[g.n] = L.hkv;
+    ++g.n;
+  }
+  const size_t nu = idx.size(), nc = cap_rows.size();
+  size_t u0 = 0, c0 = 0;
+  while (u0 < nu || c0 < nc) {
+    kvc::PageUpdate u{};
+    const int32_t mu = (int32_t)std::min<size_t>(64, nu - u0);
+    const int32_t mc = (int32_t)std::min<size_t>(256, nc - c0);
+    for (int32_t i = 0; i < mu; ++i) {
+      u.idx[i] = idx[u0 + i];
+      u.page[i] = page[u0 + i];
+      u.zero[i] = zero[u0 + i];
+    }
+    // (every group's launch repeats the table writes: the same values)
+    for (const kvc::PagedPools &g : groups)
+      if (kvc::launch_page_update(table, cap, cap_rows.data() + c0, cap_vals.data() + c0, mc, u, mu,
+                                  g, h->lay.page_bytes, stream))
+        return KVC_E_HIP;
+    u0 += mu;
+    c0 += mc;
+  }
+  return KVC_OK;
+}
+
+// Give each row `rows[i]` pages for at least `tokens[i]` positions; all or
+// nothing (KVC_E_FULL if the free list is short).
+int take_pages(kvc_t *h, const std::vector<int32_t> &rows, const std::vector<int64_t> &tokens,
+               void *stream) {
+  int64_t want = 0;
+  for (size_t i = 0; i < rows.size(); ++i) {
+    const int64_t need = (tokens[i] + kvc::kPageRows - 1) / kvc::kPageRows;
+    want += std::max<int64_t>(0, need - (int64_t)h->row_pages[rows[i]].size());
+  }
+  if (want == 0) return KVC_OK;
+  if (want > (int64_t)h->free_pages.size()) return KVC_E_FULL;
+  std::vector<int32_t> idx, page, zero, cap_rows, cap_vals;
+  for (size_t i = 0; i < rows.size(); ++i) {
+    const int32_t b = rows[i];
+    const int64_t need = (tokens[i] + kvc::kPageRows - 1) / kvc::kPageRows;
+    std::vector<int32_t> &held = h->row_pages[b];
+    if ((int64_t)held.size() >= need) continue;
+    while ((int64_t)held.size() < need) {
+      const int32_t pg = h->free_pages.back();
+      h->free_pages.pop_back();
+      idx.push_back(b * h->lay.pages_per_row + (int32_t)held.size());
+      page.push_back(pg);
+      zero.push_back(pg);
+      held.push_back(pg);
+    }
+    cap_rows.push_back(b);
+    cap_vals.push_back((int32_t)held.size() * kvc::kPageRows);
+  }
+  return push_page_updates(h, idx, page, zero, cap_rows, cap_vals, stream);
+}
+
+// Return rows' pages to the free list; their table entries name the zero page.
+int release_pages(kvc_t *h, const int32_t *rows, int32_t n, void *stream) {
+  std::vector<int32_t> idx, page, zero, cap_rows, cap_vals;
+  for (int32_t i = 0; i < n; ++i) {
+    std::vector<int32_t> &held = h->row_pages[rows[i]];
+    for (size_t k = 0; k < held.size(); ++k) {
+      idx.push_back(rows[i] * h->lay.pages_per_row + (int32_t)k);
+      page.push_back(zero_page(h));
+      zero.push_back(-1);
+      h->free_pages.push_back(held[k]);
+    }
+    held.clear();
+    cap_rows.push_back(rows[i]);
+    cap_vals.push_back(0);
+  }
+  return push_page_updates(h, idx, page, zero, cap_rows, cap_vals, stream);
 }
 
 // Where the next launch of `kind` goes.  With kernel timing on it carries a
@@ -311,6 +421,28 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     delete h;
     return KVC_E_HIP;
   }
+  // Paged: every block-table entry names the zero page, whose K and V are
+  // zero in every paged layer; all pages are free.
+  if (cfg->n_pages > 0) {
+    std::vector<int32_t> tab((size_t)cfg->batch * h->lay.pages_per_row, cfg->n_pages);
+    bool ok = hipMemcpyAsync(h->base + h->lay.table_off, tab.data(), tab.size() * 4,
+                             hipMemcpyHostToDevice, s) == hipSuccess &&
+              hipMemsetAsync(h->base + h->lay.cap_off, 0, (size_t)cfg->batch * 4, s) == hipSuccess;
+    for (const LayerLayout &L : h->lay.layers) {
+      if (!L.paged) continue;
+      const size_t bytes = (size_t)h->lay.page_bytes * L.hkv;
+      const size_t off = (size_t)cfg->n_pages * bytes;
+      ok = ok && hipMemsetAsync(h->base + L.k_off + off, 0, bytes, s) == hipSuccess &&
+           hipMemsetAsync(h->base + L.v_off + off, 0, bytes, s) == hipSuccess;
+    }
+    if (!ok || hipStreamSynchronize(s) != hipSuccess) {
+      delete h;
+      return KVC_E_HIP;
+    }
+    h->free_pages.resize(cfg->n_pages);
+    for (int32_t i = 0; i < cfg->n_pages; ++i) h->free_pages[i] = cfg->n_pages - 1 - i;
+  }
+  h->row_pages.assign(cfg->batch, {});
   if (hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->device) !=
           hipSuccess ||
       h->n_cu <= 0) {
@@ -377,6 +509,7 @@ int kvc_reset(kvc_t *h, const int32_t *rows_host, int32_t n_rows, void *stream) 
   int32_t *first = reinterpret_cast<int32_t *>(h->base + h->lay.first_off);
   int err = kvc::launch_reset_rows(lens, first, rows_host, n_rows, stream);
   if (err) return KVC_E_HIP;
+  if (h->lay.n_pages > 0 && release_pages(h, rows_host, n_rows, stream) != KVC_OK) return KVC_E_HIP;
   for (int32_t i = 0; i < n_rows; ++i) {
     h->lens_host[rows_host[i]] = 0;
     h->first_host[rows_host[i]] = 0;
@@ -424,6 +557,21 @@ int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src, const int32
       if (seen[src_rows[i]]) return KVC_E_ARG;
   if (n_rows == 0) return KVC_OK;
   if (!use_device(dst)) return KVC_E_HIP;
+  if (dst->lay.n_pages > 0) {
+    // the admitted rows' old pages go back first; pages for the copies, all
+    // or nothing
+    int64_t want = 0, back = 0;
+    for (int32_t i = 0; i < n_rows; ++i) {
+      want += (src->lens_host[src_rows[i]] + kvc::kPageRows - 1) / kvc::kPageRows;
+      back += (int64_t)dst->row_pages[dst_rows[i]].size();
+    }
+    if (want > (int64_t)dst->free_pages.size() + back) return KVC_E_FULL;
+    if (release_pages(dst, dst_rows, n_rows, stream) != KVC_OK) return KVC_E_HIP;
+    std::vector<int32_t> rows(dst_rows, dst_rows + n_rows);
+    std::vector<int64_t> tokens;
+    for (int32_t i = 0; i < n_rows; ++i) tokens.push_back(src->lens_host[src_rows[i]]);
+    if (take_pages(dst, rows, tokens, stream) != KVC_OK) return KVC_E_HIP;
+  }
   const int s = kvc::dtype_bytes(a.dtype);
   for (int32_t off = 0; off < n_rows; off += 64) {
     kvc::CopyPairs pairs{};
@@ -433,8 +581,11 @@ int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src, const int32
       for (int32_t j = 0; j < m; ++j) {
         pairs.src_row[j] = src_rows[off + j];
         pairs.dst_row[j] = dst_rows[off + j];
+        // the rows held; a full-layout destination also takes the rest of
+        // the last 32-row tile (zero V past the row's end)
         const int64_t top = std::min<int64_t>(src->lens_host[src_rows[off + j]], sl.rows);
-        pairs.rows[j] = (int32_t)round_up(top, kvc::kRowAlign);
+        const int64_t rows = dl.paged ? top : round_up(top, kvc::kRowAlign);
+        pairs.blocks[j] = (int32_t)((rows + kvc::kPageRows - 1) / kvc::kPageRows);
       }
       if (kvc::launch_copy_rows(dl, sl, a.head_dim, s, pairs, m, stream)) return KVC_E_HIP;
     }
@@ -473,6 +624,18 @@ int begin_append(kvc_t *h, int32_t layer, const int32_t *n_new_host, int32_t C, 
       if (n_new_host[b] < 0 || n_new_host[b] > C) return KVC_E_ARG;
     for (int32_t b = 0; b < B; ++b)
       if ((int64_t)h->lens_host[b] + n_new_host[b] > h->cfg.max_len) return KVC_E_FULL;
+    if (h->lay.n_pages > 0) {  // pages for the new positions, all or nothing
+      if (!use_device(h)) return KVC_E_HIP;
+      std::vector<int32_t> rows;
+      std::vector<int64_t> tokens;
+      for (int32_t b = 0; b < B; ++b)
+        if (n_new_host[b] > 0) {
+          rows.push_back(b);
+          tokens.push_back((int64_t)h->lens_host[b] + n_new_host[b]);
+        }
+      const int rc = take_pages(h, rows, tokens, stream);
+      if (rc != KVC_OK) return rc;
+    }
   } else {
     if (C != h->C) return KVC_E_STATE;
     for (int32_t b = 0; b < B; ++b)
@@ -708,6 +871,39 @@ int kvc_lens(const kvc_t *h, int32_t *lens_host) {
   return KVC_OK;
 }
 
+int kvc_page_stats(const kvc_t *h, int64_t *used, int64_t *allocated, int64_t *reserved) {
+  if (!h || !used || !allocated || !reserved) return KVC_E_ARG;
+  if (h->lens_stale) return KVC_E_STATE;
+  int64_t u = 0, held = 0;
+  for (int32_t b = 0; b < h->cfg.batch; ++b) {
+    u += h->lens_host[b];
+    held += (int64_t)h->row_pages[b].size();
+  }
+  *used = u;
+  if (h->lay.n_pages > 0) {
+    *allocated = held * kvc::kPageRows;
+    *reserved = (int64_t)h->lay.n_pages * kvc::kPageRows;
+  } else {
+    *allocated = *reserved = (int64_t)h->cfg.batch * h->cfg.max_len;
+  }
+  return KVC_OK;
+}
+
+int kvc_reserve(kvc_t *h, const int32_t *rows_host, const int32_t *tokens_host, int32_t n_rows,
+                void *stream) {
+  if (!h || n_rows < 0 || (n_rows > 0 && (!rows_host || !tokens_host))) return KVC_E_ARG;
+  if (h->in_step) return KVC_E_STATE;
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (rows_host[i] < 0 || rows_host[i] >= h->cfg.batch || tokens_host[i] < 0) return KVC_E_ARG;
+  for (int32_t i = 0; i < n_rows; ++i)
+    if (tokens_host[i] > h->cfg.max_len) return KVC_E_FULL;
+  if (h->lay.n_pages == 0 || n_rows == 0) return KVC_OK;
+  if (!use_device(h)) return KVC_E_HIP;
+  std::vector<int32_t> rows(rows_host, rows_host + n_rows);
+  std::vector<int64_t> tokens(tokens_host, tokens_host + n_rows);
+  return take_pages(h, rows, tokens, stream);
+}
+
 int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream) {
   if (!h || !n_new_dev) return KVC_E_ARG;
   if (h->in_step) return KVC_E_STATE;
@@ -718,6 +914,8 @@ int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream) {
   a.n_new = reinterpret_cast<int32_t *>(h->base + h->lay.nnew_off);
   a.lens = reinterpret_cast<const int32_t *>(h->base + h->lay.lens_off);
   a.first = reinterpret_cast<const int32_t *>(h->base + h->lay.first_off);
+  a.cap = h->lay.n_pages > 0 ? reinterpret_cast<const int32_t *>(h->base + h->lay.cap_off)
+                             : nullptr;
   a.flags = reinterpret_cast<int32_t *>(h->base + h->lay.flags_off);
   a.plan_sk = reinterpret_cast<int32_t *>(h->base + h->lay.plan_off);
   a.plan_order = h->cfg.batch <= kvc::kDecodeOrderMax

@@ -30,7 +30,8 @@ constexpr int kChunkSplitCap = 16;
 constexpr int kChunkQTile = 256;
 
 struct LayerLayout {
-  int64_t k_off = 0, v_off = 0;           // byte offsets in the device buffer
+  int64_t k_off = 0, v_off = 0;           // byte offsets in the device buffer (paged: the pools)
+  int32_t paged = 0;                      // full layout from a shared page pool
   int64_t sk_off = -1, sv_off = -1;       // staging (ring layers, max_chunk >= 2)
   int32_t hkv = 0, window = 0, ring = 0;  // ring: 0 < W < max_len and use_ring
   int32_t rows = 0;                       // W (ring) or max_len; scratch = rows
@@ -49,6 +50,12 @@ struct Layout {
   int64_t cnt_off = 0;        // int32 [B][max Hkv]: split arrivals (fused decode), 0 between launches
   int64_t cnt_bytes = 0;
   int64_t flags_off = 0;      // int32: sticky error bits of static steps
+  // paged caches: pages per pool (the zero page and the scratch page follow),
+  // block-table entries per row, the int32 block table [B][pages_per_row]
+  // and the int32 rows each row may hold without new pages [B]
+  int32_t n_pages = 0, pages_per_row = 0;
+  int64_t table_off = -1, cap_off = -1;
+  int64_t page_bytes = 0;     // per layer and KV head: 16 rows x D x dtype
   int64_t plan_off = 0;       // int32 [n_layer] split keys, then uint16 [n_layer][B] row orders
   int64_t pml_off = -1;       // float2 [B][max_chunk][Hq][kChunkSplitCap]
   int64_t pout_off = -1;      // float [B][max_chunk][Hq][kChunkSplitCap][D]
@@ -64,10 +71,18 @@ int dtype_bytes(int dtype);
 // Kernel-side argument blocks
 // ---------------------------------------------------------------------------
 struct LayerArgs {
-  char *k, *v;          // this layer's K and V region
+  char *k, *v;          // this layer's K and V region (paged: page pools)
   char *sk, *sv;        // staging K and V (nullptr when the layer has none)
   int32_t hkv, rep, window, ring, rows, rows_alloc, stage_rows_alloc;
+  // Paged layer: storage row r of row b lives in page table[b * ppr + r / 16]
+  // (row r % 16); the scratch row in page scratch_page.  Page pg of KV head g
+  // holds 16 K rows (row-major) and one 16-row V block, at
+  // ((pg * hkv + g) * 16) * D elements of the pools.
+  int32_t paged;
+  const int32_t *table;
+  int32_t ppr, scratch_page;
 };
+constexpr int kPageRows = 16;
 
 struct StepArgs {
   const int32_t *lens;    // device [B]
@@ -115,6 +130,7 @@ struct StaticBeginArgs {
   int32_t *n_new;         // the step's counts [B]
   const int32_t *lens;    // [B]
   const int32_t *first;   // [B]
+  const int32_t *cap;     // [B] rows a paged row holds pages for, or null
   int32_t *flags;         // sticky error bits
   int32_t *plan_sk;       // [n_class] keys per split
   uint16_t *plan_order;   // [n_class][B] dispatch order, or null (B > kDecodeOrderMax)
@@ -147,13 +163,27 @@ int launch_reset_rows(int32_t *lens, int32_t *first, const int32_t *rows, int32_
 int launch_set_first(int32_t *first, const int32_t *rows, const int32_t *vals, int32_t n,
                      void *stream);
 // Row copies between two caches of the same layer shapes: per pair j, the
-// first `rows[j]` storage rows (a multiple of 32) of every KV head of row
-// src_row[j] (K rows and V blocks), into row dst_row[j].
+// first `blocks[j]` 16-row blocks of every KV head of row src_row[j] (K rows
+// and V blocks, paged or not on either side), into row dst_row[j].
 struct CopyPairs {
-  int32_t src_row[64], dst_row[64], rows[64];
+  int32_t src_row[64], dst_row[64], blocks[64];
 };
 int launch_copy_rows(const LayerArgs &dst, const LayerArgs &src, int D, int dtype_bytes,
                      const CopyPairs &pairs, int32_t n_pairs, void *stream);
+// Paged caches: block-table updates (table[idx[i]] = page[i]) and the zeroing
+// of V of newly taken pages (zero[i] >= 0) in every paged layer, whose V
+// pools are listed with their KV heads.
+struct PageUpdate {
+  int32_t idx[64], page[64], zero[64];
+};
+struct PagedPools {
+  char *v[64];
+  int32_t hkv[64];
+  int32_t n;
+};
+int launch_page_update(int32_t *table, int32_t *cap, const int32_t *cap_rows, const int32_t *cap_vals,
+                       int32_t n_cap, const PageUpdate &u, int32_t n_upd, const PagedPools &pools,
+                       int64_t page_bytes, void *stream);
 // lens / first of dst_row[j] = those of src_row[j] (device arrays).
 int launch_copy_state(int32_t *dst_lens, int32_t *dst_first, const int32_t *src_lens,
                       const int32_t *src_first, const CopyPairs &pairs, int32_t n_pairs,

@@ -56,10 +56,18 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
   if (!cfg->n_kv_head || !cfg->window) return KVC_E_ARG;
   if (!(cfg->rope_base >= 0.0)) return KVC_E_ARG;  // also rejects NaN
   if (cfg->use_ring != 0 && cfg->use_ring != 1) return KVC_E_ARG;
+  if (cfg->n_pages < 0 || cfg->n_pages > (1 << 30)) return KVC_E_ARG;
 
   const int64_t B = cfg->batch, D = cfg->head_dim, Hq = cfg->n_q_head;
   lay->layers.assign(cfg->n_layer, LayerLayout{});
   int64_t cur = 0, kv_bytes = 0;
+  // Paged: a pool of n_pages pages plus a zero page (unassigned block-table
+  // entries point at it) and a scratch page (padded tokens land there).
+  const int64_t pool_pages = cfg->n_pages > 0 ? (int64_t)cfg->n_pages + 2 : 0;
+  lay->n_pages = cfg->n_pages;
+  // whole 32-row tiles: the chunk kernel reads rows up to the next multiple of 32
+  lay->pages_per_row = cfg->n_pages > 0 ? (cfg->max_len + 2 * kPageRows - 1) / (2 * kPageRows) * 2 : 0;
+  lay->page_bytes = (int64_t)kPageRows * D * s;
   for (int l = 0; l < cfg->n_layer; ++l) {
     const int32_t hkv = cfg->n_kv_head[l], w = cfg->window[l];
     if (hkv < 1 || Hq % hkv) return KVC_E_ARG;
@@ -68,16 +76,15 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
     L.hkv = hkv;
     L.window = w;
     L.ring = (cfg->use_ring && w > 0 && w < cfg->max_len) ? 1 : 0;
+    L.paged = (!L.ring && cfg->n_pages > 0) ? 1 : 0;
     L.rows = L.ring ? w : cfg->max_len;
     L.rows_alloc = (int32_t)align_up((int64_t)L.rows + 1, kRowAlign);
-    int64_t region = B;
-    if (!mul(&region, hkv) || !mul(&region, L.rows_alloc) || !mul(&region, D) ||
-        !mul(&region, s))
-      return KVC_E_ARG;
+    int64_t region = L.paged ? pool_pages * kPageRows : B * (int64_t)L.rows_alloc;
+    if (!mul(&region, hkv) || !mul(&region, D) || !mul(&region, s)) return KVC_E_ARG;
     if (!take(&cur, region, &L.k_off) || !take(&cur, region, &L.v_off)) return KVC_E_ARG;
-    int64_t kvl = 2 * B;
-    if (!mul(&kvl, hkv) || !mul(&kvl, L.rows) || !mul(&kvl, D) || !mul(&kvl, s))
-      return KVC_E_ARG;
+    // the size formula: every row's max_len rows, or the page pool
+    int64_t kvl = L.paged ? 2 * (int64_t)cfg->n_pages * kPageRows : 2 * B * (int64_t)L.rows;
+    if (!mul(&kvl, hkv) || !mul(&kvl, D) || !mul(&kvl, s)) return KVC_E_ARG;
     if (kv_bytes > std::numeric_limits<int64_t>::max() - kvl) return KVC_E_ARG;
     kv_bytes += kvl;
     if (L.ring && cfg->max_chunk >= 2) {
@@ -101,6 +108,10 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
   // One counter per (row, KV head); Hq bounds every layer's Hkv.
   lay->cnt_bytes = B * Hq * 4;
   if (!take(&cur, lay->cnt_bytes, &lay->cnt_off)) return KVC_E_ARG;
+  if (cfg->n_pages > 0) {
+    if (!take(&cur, B * lay->pages_per_row * 4, &lay->table_off) || !take(&cur, B * 4, &lay->cap_off))
+      return KVC_E_ARG;
+  }
   // Static steps: error bits, and per layer class a split length and a row order.
   if (!take(&cur, 4, &lay->flags_off)) return KVC_E_ARG;
   if (!take(&cur, (int64_t)cfg->n_layer * (4 + 2 * B), &lay->plan_off)) return KVC_E_ARG;

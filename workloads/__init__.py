@@ -50,6 +50,7 @@ class Workload:
     max_chunk: int
     rope_base: float = 10000.0
     use_ring: bool = True
+    n_pages: int = 0           # > 0: paged full layers with a pool of this many 16-row pages
     notes: str = field(default="", compare=False)
 
     @property
