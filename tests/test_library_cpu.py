@@ -122,3 +122,17 @@ def test_null_handle_calls_fail_cleanly():
     assert L.kvc_attend(None, 0, None, None, None) == K.KVC_E_ARG
     assert L.kvc_lens(None, None) == K.KVC_E_ARG
     L.kvc_destroy(None)
+
+
+def test_paged_sizes_and_validation():
+    # Lab 07 Stretch (16-token blocks): a paged full layer's K and V are the
+    # pool, 2 * Hkv * n_pages * 16 * D * bytes; ring layers keep W rows per
+    # row; a negative pool is rejected.
+    full = K.make_config(2, 4, 8, 64, 256, 16, "bf16", [2, 2], [0, 32])
+    paged = K.make_config(2, 4, 8, 64, 256, 16, "bf16", [2, 2], [0, 32], n_pages=40)
+    ring_bytes = 2 * 4 * 2 * 32 * 64 * 2
+    assert K.kvc_nbytes(full, K.KVC_NB_KV) == 2 * 4 * 2 * 256 * 64 * 2 + ring_bytes
+    assert K.kvc_nbytes(paged, K.KVC_NB_KV) == 2 * 2 * 40 * 16 * 64 * 2 + ring_bytes
+    assert K.kvc_nbytes(paged, K.KVC_NB_ALLOC) > K.kvc_nbytes(paged, K.KVC_NB_KV)
+    bad = K.make_config(2, 4, 8, 64, 256, 16, "bf16", [2, 2], [0, 32], n_pages=-1)
+    assert K.kvc_nbytes(bad, K.KVC_NB_KV) == 0
