@@ -18,6 +18,14 @@ far, plus ``lens`` (tokens per row).  One step is
    ``KVCache.update`` docstring and ``advance``; Lab 07 "Given"; tinyllm
    ``end_step``).
 
+Hybrid layer groups (tiny_agent ``generate.py`` module docstring and
+``_append_chunk``): a layer may have a joint partner ``joint[l] = j`` (an
+earlier layer, the group's global store); its queries then attend, with ONE
+softmax, to layer j's keys under layer j's rules (all positions up to the
+query: a global store) together with its own keys under its own rules (the
+last W positions: the per-layer ring).  Layer j must have been appended in
+the same step first; its own outputs are not part of the group's result.
+
 Left padding (tinyllm ``kv_cache.py``: ``padded_causal_mask`` and
 ``SlotKVCache``): a row may start with ``first[b]`` pad tokens; keys before
 ``first[b]`` are hidden from every query of the row except the pad's own
@@ -91,11 +99,19 @@ class OracleCache:
     """No-cache reference for a stack of attention layers over B rows."""
 
     def __init__(self, batch: int, n_q_head: int, n_kv_head, head_dim: int,
-                 max_len: int, window, rope_base: float = 10000.0):
+                 max_len: int, window, rope_base: float = 10000.0, joint=None):
         n_kv_head = [int(h) for h in n_kv_head]
         window = [int(w) for w in window]
         if len(n_kv_head) != len(window):
             raise ValueError("n_kv_head and window need one entry per layer")
+        joint = [-1] * len(window) if joint is None else [int(j) for j in joint]
+        if len(joint) != len(window):
+            raise ValueError("joint needs one entry per layer")
+        for l, j in enumerate(joint):
+            if j >= 0 and (j >= l or n_kv_head[j] != n_kv_head[l] or joint[j] >= 0):
+                raise ValueError("a joint partner is an earlier layer with the same KV heads "
+                                 "and no partner of its own")
+        self.joint = joint
         self.batch = int(batch)
         self.n_layer = len(n_kv_head)
         self.n_q_head = int(n_q_head)
@@ -156,12 +172,26 @@ class OracleCache:
             self.hist_v[layer][b] = np.concatenate((self.hist_v[layer][b], v[b, :n]), axis=0)
             if not compute:
                 continue
-            T = int(self.lens[b]) + n
-            krot = _rope.rotate(self.hist_k[layer][b], np.arange(T), self.rope_base)
             qrot = _rope.rotate(q[b, :n], self._query_positions(b, n), self.rope_base)
-            blocked = self._blocked(layer, b, n)
-            out[b, :n] = _attn.attend_rows(qrot, krot, self.hist_v[layer][b], blocked)
+            krot, vals, blocked = self._keys(layer, b, n)
+            out[b, :n] = _attn.attend_rows(qrot, krot, vals, blocked)
         return out if compute else None
+
+    def _keys(self, layer: int, b: int, n: int):
+        """Rotated keys, values and the (n, keys) blocked mask the current
+        step's n queries of row b attend to: the joint partner's keys (if
+        any) followed by the layer's own, each under its own layer's rules."""
+        T = int(self.lens[b]) + n
+        parts = [self.joint[layer]] if self.joint[layer] >= 0 else []
+        parts.append(layer)
+        ks, vs, bl = [], [], []
+        for l in parts:
+            if self.hist_k[l][b].shape[0] != T:
+                raise ValueError("append the joint partner's tokens of this step first")
+            ks.append(_rope.rotate(self.hist_k[l][b], np.arange(T), self.rope_base))
+            vs.append(self.hist_v[l][b])
+            bl.append(self._blocked(l, b, n))
+        return np.concatenate(ks), np.concatenate(vs), np.concatenate(bl, axis=1)
 
     def query_rows(self, layer: int, b: int, n: int, q_b, idx) -> np.ndarray:
         """Outputs of the queries ``idx`` (a subset of 0..n-1) of row b, whose
@@ -175,10 +205,9 @@ class OracleCache:
         T = int(self.lens[b]) + int(n)
         if self.hist_k[layer][b].shape[0] != T:
             raise ValueError("append this step's tokens (layer_step) before querying")
-        krot = _rope.rotate(self.hist_k[layer][b], np.arange(T), self.rope_base)
         qrot = _rope.rotate(q_b[idx], self._query_positions(b, n)[idx], self.rope_base)
-        blocked = self._blocked(layer, b, n)[idx]
-        return _attn.attend_rows(qrot, krot, self.hist_v[layer][b], blocked)
+        krot, vals, blocked = self._keys(layer, b, n)
+        return _attn.attend_rows(qrot, krot, vals, blocked[idx])
 
     def advance(self, n_new) -> None:
         self.lens = self.lens + np.asarray(n_new, dtype=np.int64)
@@ -219,7 +248,7 @@ class OracleCache:
         if rows.shape != src_rows.shape:
             raise ValueError("one source row per row")
         if (src.n_kv_head != self.n_kv_head or src.window != self.window
-                or src.head_dim != self.head_dim):
+                or src.head_dim != self.head_dim or src.joint != self.joint):
             raise ValueError("caches of different layer shapes")
         if (src.lens[src_rows] > self.max_len).any():
             raise CacheFull("admitted row longer than max_len")

@@ -451,6 +451,96 @@ def test_mutation_left_pad_hides_diagonal(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
+# Hybrid layer groups (tiny_agent generate.py: a group-global K/V written by
+# the group's full layer plus a per-layer ring, one softmax over both).
+# ---------------------------------------------------------------------------
+_GROUP = dict(n_kv_head=[2, 2, 2], window=[0, 5, 3], joint=[-1, 0, 0])
+
+
+def _group_oracle(batch=2, max_len=40):
+    return oracle.OracleCache(batch, 4, _GROUP["n_kv_head"], 16, max_len, _GROUP["window"],
+                              joint=_GROUP["joint"])
+
+
+def _group_inputs(g, B, C):
+    return [(g.standard_normal((B, C, 4, 16)), g.standard_normal((B, C, 2, 16)),
+             g.standard_normal((B, C, 2, 16))) for _ in range(3)]
+
+
+def test_joint_layers_match_sdpa_over_both_stores():
+    # torch's float64 scaled_dot_product_attention over the concatenated keys
+    # of the group store (visible: j <= p) and the layer's ring (visible:
+    # j <= p and p - j < W), heads expanded by repeat_interleave.
+    g = np.random.default_rng(21)
+    oc = _group_oracle(batch=1)
+    steps = [(np.array([9]), 9), (np.array([4]), 4), (np.array([1]), 1)]
+    hist = [[[], []] for _ in range(3)]
+    for n, C in steps:
+        layers = _group_inputs(g, 1, C)
+        outs = oc.step(n, layers)
+        for l in range(3):
+            hist[l][0].append(layers[l][1][0, :n[0]])
+            hist[l][1].append(layers[l][2][0, :n[0]])
+        T = int(oc.lens[0])
+        pos_q = np.arange(T - n[0], T)
+        for l in (1, 2):
+            parts_k, parts_v, masks = [], [], []
+            for src, W in ((0, 0), (l, _GROUP["window"][l])):
+                k = np.concatenate(hist[src][0]); v = np.concatenate(hist[src][1])
+                parts_k.append(orope.rotate(k, np.arange(T), 1e4)); parts_v.append(v)
+                j = np.arange(T)[None, :]
+                ok = j <= pos_q[:, None]
+                if W:
+                    ok = ok & (pos_q[:, None] - j < W)
+                masks.append(ok)
+            K = torch.from_numpy(np.concatenate(parts_k)).permute(1, 0, 2).repeat_interleave(2, 0)
+            V = torch.from_numpy(np.concatenate(parts_v)).permute(1, 0, 2).repeat_interleave(2, 0)
+            Q = torch.from_numpy(orope.rotate(layers[l][0][0, :n[0]], pos_q, 1e4)).permute(1, 0, 2)
+            M = torch.from_numpy(np.concatenate(masks, axis=1))
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=M)
+            got = outs[l][0, :n[0]]
+            assert np.abs(ref.permute(1, 0, 2).numpy() - got).max() <= 1e-12
+
+
+def test_joint_with_identical_stores_equals_single():
+    # duplicated keys (same K and V in the group store and in a ring that
+    # sees every position) leave the softmax weights' ratios unchanged
+    g = np.random.default_rng(22)
+    dup = oracle.OracleCache(2, 4, [2, 2], 16, 40, [0, 40], joint=[-1, 0])
+    single = oracle.OracleCache(2, 4, [2], 16, 40, [0])
+    for n, C in ((np.array([7, 3]), 7), (np.array([1, 5]), 5), (np.array([1, 1]), 1)):
+        q, k, v = _group_inputs(g, 2, C)[0]
+        a = dup.step(n, [(q, k, v), (q, k, v)])[1]
+        b = single.step(n, [(q, k, v)])[0]
+        assert np.abs(a - b).max() <= 1e-12
+
+
+def test_joint_layers_chunked_equals_single_chunk():
+    g = np.random.default_rng(23)
+    T = 17
+    data = _group_inputs(g, 2, T)
+    one, many = _group_oracle(), _group_oracle()
+    full = one.step(np.array([T, T]), data)
+    outs, done = [], 0
+    for C in (5, 5, 5, 2):
+        part = [tuple(x[:, done:done + C] for x in layer) for layer in data]
+        outs.append(many.step(np.array([C, C]), part))
+        done += C
+    for l in (1, 2):
+        got = np.concatenate([o[l] for o in outs], axis=1)
+        assert np.abs(got - full[l]).max() <= 1e-12
+
+
+def test_mutation_joint_ignored(monkeypatch):
+    def own_only(self, layer, b, n):
+        T = int(self.lens[b]) + n
+        return (orope.rotate(self.hist_k[layer][b], np.arange(T), self.rope_base),
+                self.hist_v[layer][b], self._blocked(layer, b, n))
+    monkeypatch.setattr(ocache.OracleCache, "_keys", own_only)
+    assert _fails(test_joint_layers_match_sdpa_over_both_stores)
+
+
+# ---------------------------------------------------------------------------
 # Sizes: Lab 07 answer 1; colibri PR "Expected memory savings".
 # ---------------------------------------------------------------------------
 def test_kv_bytes_lab07():
