@@ -97,6 +97,21 @@ typedef struct {
                                16-row pages, handed to rows as they grow and
                                returned by kvc_reset; one block table per row
                                serves every such layer                          */
+  const int32_t *joint;     /* NULL, or [n_layer]: joint[l] = j >= 0 makes layer
+                               l's softmax also cover layer j's keys (under
+                               layer j's rules: all positions up to the query
+                               for a global layer) together with its own, one
+                               softmax over both (tiny_agent "generate.py"
+                               module docstring and _append_chunk: hybrid layer
+                               groups, a group-global K/V written by the
+                               group's full layer plus a ring per layer).  j <
+                               l, layer j full-layout (not a ring) with the
+                               same KV heads and no partner of its own; -1 =
+                               none.  Layer j is appended before layer l is
+                               attended in a step (else KVC_E_STATE) and need
+                               not be attended itself.  Joint layers run
+                               append + attend (no single-kernel step) and
+                               not in static steps (KVC_E_ARG)              */
 } kvc_config;
 
 /* Rows per page of a paged cache. */

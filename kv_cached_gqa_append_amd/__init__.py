@@ -60,6 +60,7 @@ class KvcConfig(ctypes.Structure):
         ("use_ring", ctypes.c_int32),
         ("rope_base", ctypes.c_double),
         ("n_pages", ctypes.c_int32),
+        ("joint", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -167,7 +168,8 @@ def _check(code: int, what: str) -> None:
 
 
 def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
-                n_kv_head, window, use_ring=True, rope_base=10000.0, n_pages=0) -> KvcConfig:
+                n_kv_head, window, use_ring=True, rope_base=10000.0, n_pages=0,
+                joint=None) -> KvcConfig:
     """A ``KvcConfig`` that keeps its per-layer arrays alive."""
     if isinstance(dtype, torch.dtype):
         dtype = _DTYPES[dtype]
@@ -179,10 +181,13 @@ def make_config(n_layer, batch, n_q_head, head_dim, max_len, max_chunk, dtype,
         window = [window] * n_layer
     hk = (ctypes.c_int32 * len(n_kv_head))(*[int(x) for x in n_kv_head])
     wn = (ctypes.c_int32 * len(window))(*[int(x) for x in window])
+    jt = None
+    if joint is not None and len(joint) and any(int(j) >= 0 for j in joint):
+        jt = (ctypes.c_int32 * len(joint))(*[int(j) for j in joint])
     cfg = KvcConfig(int(n_layer), int(batch), int(n_q_head), int(head_dim), int(max_len),
                     int(max_chunk), int(dtype), hk, wn, int(bool(use_ring)), float(rope_base),
-                    int(n_pages))
-    cfg._keep = (hk, wn)
+                    int(n_pages), jt)
+    cfg._keep = (hk, wn, jt)
     return cfg
 
 
@@ -190,7 +195,7 @@ def config_from_workload(w) -> KvcConfig:
     """Config for a ``workloads.Workload``."""
     return make_config(w.n_layer, w.batch, w.n_q_head, w.head_dim, w.max_len, w.max_chunk,
                        w.dtype, list(w.n_kv_head), list(w.window), w.use_ring, w.rope_base,
-                       getattr(w, "n_pages", 0))
+                       getattr(w, "n_pages", 0), getattr(w, "joint", None) or None)
 
 
 def kvc_nbytes(cfg: KvcConfig, what: int = KVC_NB_KV) -> int:

@@ -210,6 +210,22 @@ __device__ __forceinline__ void chunk_span_dev(const LayerArgs &la, int64_t L, i
   *base = *lo / kRowAlign * kRowAlign;
 }
 
+// Splits of one layer for a row (see SplitRef): decode splits of a one-token
+// row's span, or the key splits of a chunk row.
+__device__ __forceinline__ int ref_splits(const SplitRef &r, int64_t L, int n, int64_t first) {
+  LayerArgs la{};
+  la.ring = r.ring;
+  la.window = r.window;
+  if (n == 1) {
+    const DecodeSpan sp = decode_span_dev(la, L, first);
+    return (int)cdiv(sp.hi - sp.base, r.dec_sk);
+  }
+  if (r.ring) return 1;
+  int64_t base, lo, hi;
+  chunk_span_dev(la, L, n, first, &base, &lo, &hi);
+  return (int)cdiv(hi - base, r.pre_sk);
+}
+
 // ---------------------------------------------------------------------------
 // tiny state kernels (values arrive as kernel arguments: no host staging)
 // ---------------------------------------------------------------------------
@@ -645,8 +661,8 @@ __device__ __forceinline__ void generic_key(GenericState<T> &S, const T *krow, c
 }
 
 template <typename T>
-__global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const T *__restrict__ q,
-                                                T *__restrict__ out) {
+__global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, LayerArgs lj,
+                                                const T *__restrict__ q, T *__restrict__ out) {
   __shared__ float qs[256];
   const int64_t row = blockIdx.x;  // (b * C + i) * Hq + h
   const int h = (int)(row % st.Hq);
@@ -693,6 +709,15 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
   // left padding: keys before `first` are hidden, except the query's own
   const int64_t first = st.first[b];
   auto hidden = [&](int64_t pos) { return pos < first && pos != p; };
+  // a joint partner's keys (a full layout) join the same softmax first
+  if (lj.k != nullptr) {
+    const int Wj = lj.window;
+    const int64_t lo = Wj > 0 ? (p - Wj + 1 > 0 ? p - Wj + 1 : 0) : 0;
+    for (int64_t t = lo; t <= p; ++t) {
+      if (hidden(t)) continue;
+      generic_key(S, krow_ptr<T>(lj, b, g, t, D), vcol_ptr<T>(lj, b, g, t, D), D, scale);
+    }
+  }
   if (la.ring && n >= 2 && la.sk) {
     // history from the ring (slots holding positions within the window) ...
     const int64_t nh = L < W ? L : W;
@@ -730,13 +755,15 @@ __global__ __launch_bounds__(64) void k_generic(StepArgs st, LayerArgs la, const
   }
 }
 
-int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const void *q, void *out,
-                   const Launch &lc) {
+int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const LayerArgs &lj,
+                   const void *q, void *out, const Launch &lc) {
   const int64_t rows = (int64_t)st.B * st.C * st.Hq;
   if (dtype == KVC_F32)
-    launch_kernel(k_generic<float>, dim3((unsigned)rows), dim3(64), lc, st, la, (const float *)q, (float *)out);
+    launch_kernel(k_generic<float>, dim3((unsigned)rows), dim3(64), lc, st, la, lj, (const float *)q,
+                  (float *)out);
   else
-    launch_kernel(k_generic<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la, (const bf16 *)q, (bf16 *)out);
+    launch_kernel(k_generic<bf16>, dim3((unsigned)rows), dim3(64), lc, st, la, lj, (const bf16 *)q,
+                  (bf16 *)out);
   return (int)hipGetLastError();
 }
 
@@ -1520,17 +1547,19 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     else
       *ptr = val;
   };
+  // (over a joint partner's keys, after the layer's own splits)
+  const int sbase = pa.base.on ? ref_splits(pa.base, p, 1, st.first[b]) : 0;
 #pragma unroll
   for (int u = 0; u < HPL; ++u) {
     if (kr == 0 && writer) {
-      const int64_t slot = ((int64_t)b * st.Hq + h0 + hbase + u) * cap + split;
+      const int64_t slot = ((int64_t)b * st.Hq + h0 + hbase + u) * cap + sbase + split;
       put(pa.dml + slot * 2 + 0, m[u]);
       put(pa.dml + slot * 2 + 1, lh[u]);
     }
   }
 #pragma unroll
   for (int h = 0; h < REP; ++h) {
-    const int64_t slot = ((int64_t)b * st.Hq + h0 + h) * cap + split;
+    const int64_t slot = ((int64_t)b * st.Hq + h0 + h) * cap + sbase + split;
 #pragma unroll
     for (int t = 0; t < VT; ++t) {
       const float o = swap32_sum(acc[h][t]);
@@ -2060,14 +2089,17 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   });
   asm volatile("" ::: "memory");
 
-  // -- partials for this split ---------------------------------------------------
+  // -- partials for this split (over a joint partner's keys: after the
+  // layer's own splits) ------------------------------------------------------------
+  const int sbase = pa.base.on ? ref_splits(pa.base, L, n, first_i) : 0;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     float lt = lrun[blk] + __shfl_xor(lrun[blk], 16);
     lt += __shfl_xor(lt, 32);
     if (rvalid[blk]) {
       const int64_t slot =
-          (((int64_t)b * pa.max_chunk + qi[blk]) * st.Hq + g * REP + hl[blk]) * kChunkSplitCap + ks;
+          (((int64_t)b * pa.max_chunk + qi[blk]) * st.Hq + g * REP + hl[blk]) * kChunkSplitCap +
+          sbase + ks;
       if (q4 == 0) {
         pa.pml[slot * 2 + 0] = lt > 0.f ? mrun[blk] : -INFINITY;
         pa.pml[slot * 2 + 1] = lt;
@@ -2134,9 +2166,11 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
   const float *ml;
   const float *os;
   int ns;
+  // a joint partner's splits follow the layer's own
+  const int nj = pa.joint.on ? ref_splits(pa.joint, L, n, st.first[b]) : 0;
   if (n == 1) {
     const DecodeSpan sp = decode_span_dev(la, L, st.first[b]);
-    ns = (int)cdiv(sp.hi - sp.base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
+    ns = (int)cdiv(sp.hi - sp.base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys) + nj;
     const int64_t s0 = ((int64_t)b * st.Hq + h) * kDecodeSplitCap;
     ml = pa.dml + s0 * 2;
     os = pa.dout + s0 * D;
@@ -2147,6 +2181,7 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
       chunk_span_dev(la, L, n, st.first[b], &base, &lo, &hi);
       ns = (int)cdiv(hi - base, pa.pre_split_keys);
     }
+    ns += nj;
     const int64_t s0 = (((int64_t)b * pa.max_chunk + i) * st.Hq + h) * kChunkSplitCap;
     ml = pa.pml + s0 * 2;
     os = pa.pout + s0 * D;

@@ -25,7 +25,7 @@ using kvc::LayerLayout;
 
 struct kvc_cache {
   kvc_config cfg{};
-  std::vector<int32_t> n_kv_head, window;
+  std::vector<int32_t> n_kv_head, window, joint;
   Layout lay;
   char *base = nullptr;
   size_t bytes = 0;
@@ -40,6 +40,9 @@ struct kvc_cache {
   std::vector<int32_t> n_new;
   int32_t C = 0;
   std::vector<uint8_t> appended, attended;
+  // layers that are some layer's joint partner: their keys serve that layer's
+  // softmax, so they need not be attended on their own
+  std::vector<uint8_t> partner_only;
   // decode split planning: compute units, resident decode waves per CU by
   // query heads per KV head (0 = not yet queried), and overrides
   int32_t n_cu = 0;
@@ -240,7 +243,8 @@ void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t first, int64_t *ba
 // kDecodeSplitCap splits.  The idle rows' items of the single-kernel step
 // take slots too; both entry points plan with them counted, so a step splits
 // its rows the same way (and produces the same bits) through either.
-int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
+int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D,
+                          int32_t cap = kvc::kDecodeSplitCap) {
   const int TK = kvc::kDecodeTile;
   std::vector<int64_t> tiles;
   int64_t max_t = 0, extra = 0;
@@ -252,8 +256,7 @@ int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D) {
     tiles.push_back((hi - base + TK - 1) / TK);
     max_t = std::max(max_t, tiles.back());
   }
-  const int64_t q_cap = std::max<int64_t>(1, (max_t + kvc::kDecodeSplitCap - 1) /
-                                                 kvc::kDecodeSplitCap);
+  const int64_t q_cap = std::max<int64_t>(1, (max_t + cap - 1) / cap);
   if (max_t == 0) return TK;
   const int64_t q_min = std::max<int64_t>(q_cap, h->dec_min_tiles);
   if (h->dec_split_fixed > 0)
@@ -375,6 +378,10 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   h->window.assign(cfg->window, cfg->window + cfg->n_layer);
   h->cfg.n_kv_head = h->n_kv_head.data();
   h->cfg.window = h->window.data();
+  if (cfg->joint) {
+    h->joint.assign(cfg->joint, cfg->joint + cfg->n_layer);
+    h->cfg.joint = h->joint.data();
+  }
   h->lay = std::move(lay);
   h->base = static_cast<char *>(dev_buf);
   h->bytes = buf_bytes;
@@ -383,6 +390,9 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   h->n_new.assign(cfg->batch, 0);
   h->appended.assign(cfg->n_layer, 0);
   h->attended.assign(cfg->n_layer, 0);
+  h->partner_only.assign(cfg->n_layer, 0);
+  for (int32_t l = 0; l < cfg->n_layer; ++l)
+    if (h->lay.layers[l].joint >= 0) h->partner_only[h->lay.layers[l].joint] = 1;
   if (hipGetDevice(&h->device) != hipSuccess) {
     delete h;
     return KVC_E_HIP;
@@ -543,7 +553,8 @@ int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src, const int32
     return KVC_E_ARG;
   for (int32_t l = 0; l < a.n_layer; ++l) {
     const LayerLayout &x = dst->lay.layers[l], &y = src->lay.layers[l];
-    if (x.hkv != y.hkv || x.window != y.window || x.ring != y.ring) return KVC_E_ARG;
+    if (x.hkv != y.hkv || x.window != y.window || x.ring != y.ring || x.joint != y.joint)
+      return KVC_E_ARG;
   }
   std::vector<uint8_t> seen(a.batch, 0);
   for (int32_t i = 0; i < n_rows; ++i) {
@@ -716,9 +727,13 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
   if (!h || !q || !out) return KVC_E_ARG;
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   if (!h->in_step || !h->appended[layer] || h->attended[layer]) return KVC_E_STATE;
+  const int32_t jl = h->lay.layers[layer].joint;
+  const bool joint = jl >= 0;
+  if (joint && !h->appended[jl]) return KVC_E_STATE;  // the partner's keys of this step first
   if (!use_device(h)) return KVC_E_HIP;
   const kvc::StepArgs st = step_args(h);
   const kvc::LayerArgs la = layer_args(h, layer);
+  const kvc::LayerArgs lj = joint ? layer_args(h, jl) : kvc::LayerArgs{};
   const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
   bool staged = false;
   if (!h->step_static)
@@ -737,51 +752,64 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
     err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
     if (err) return KVC_E_HIP;
   } else if (!fast) {
-    err = kvc::launch_generic(h->cfg.dtype, st, la, q, out, launch_on(h, KVC_K_GENERIC, stream));
+    err = kvc::launch_generic(h->cfg.dtype, st, la, lj, q, out, launch_on(h, KVC_K_GENERIC, stream));
     if (err) return KVC_E_HIP;
   } else {
-    // Plan: decode rows (one token) and chunk rows (two or more tokens).
-    int64_t max_chunk_span = 0;
-    for (int32_t b = 0; b < B; ++b) {
-      const int64_t L = h->lens_host[b], n = h->n_new[b];
-      int64_t base, hi;
-      if (n >= 2 && !la.ring) {
-        chunk_span(la, L, n, h->first_host[b], &base, &hi);
-        max_chunk_span = std::max(max_chunk_span, hi - base);
-      }
-    }
-    kvc::PartialArgs pa = partial_args(h);
-    pa.dec_split_keys = decode_split_keys(h, la, D);
-    decode_order(h, la, &pa);
-    pa.pre_split_keys = (int32_t)std::max<int64_t>(
-        kChunkSplitMin, round_up(ceil_div(max_chunk_span, kvc::kChunkSplitCap), kvc::kRowAlign));
-    int64_t dec_items = 0, pre_items = 0;
-    for (int32_t b = 0; b < B; ++b) {
-      const int64_t L = h->lens_host[b], n = h->n_new[b];
-      int64_t base, hi;
-      if (n == 1) {
-        decode_span(la, L, h->first_host[b], &base, &hi);
-        dec_items += ceil_div(hi - base, pa.dec_split_keys);
-      } else if (n >= 2) {
-        const int64_t nqt = ceil_div(n * la.rep, kvc::kChunkQTile);
-        int64_t nks = 1;
-        if (!la.ring) {
-          chunk_span(la, L, n, h->first_host[b], &base, &hi);
-          nks = ceil_div(hi - base, pa.pre_split_keys);
+    // A joint layer's own splits and its partner's share a query's partial
+    // slots: each side is planned within half the caps.
+    const int32_t dcap = joint ? kvc::kDecodeSplitCap / 2 : kvc::kDecodeSplitCap;
+    const int32_t ccap = joint ? kvc::kChunkSplitCap / 2 : kvc::kChunkSplitCap;
+    // Plan one layer's keys: decode rows (one token) and chunk rows (two or
+    // more tokens); launch its decode and chunk kernels.
+    auto run = [&](const kvc::LayerArgs &lx, kvc::PartialArgs *pa) -> int {
+      int64_t max_chunk_span = 0;
+      for (int32_t b = 0; b < B; ++b) {
+        const int64_t L = h->lens_host[b], n = h->n_new[b];
+        int64_t base, hi;
+        if (n >= 2 && !lx.ring) {
+          chunk_span(lx, L, n, h->first_host[b], &base, &hi);
+          max_chunk_span = std::max(max_chunk_span, hi - base);
         }
-        pre_items += nqt * nks;
       }
-    }
-    if (h->log_level >= 2 && layer == 0 && dec_items > 0)
-      std::fprintf(stderr, "[kvc] decode plan: %d keys per split, %lld waves\n",
-                   pa.dec_split_keys, (long long)dec_items * la.hkv);
-    if (dec_items > 0) {
-      err = kvc::launch_decode(st, la, pa, q, (int32_t)dec_items, launch_on(h, KVC_K_DECODE, stream));
-      if (err) return KVC_E_HIP;
-    }
-    if (pre_items > 0) {
-      err = kvc::launch_prefill(st, la, pa, q, (int32_t)pre_items, launch_on(h, KVC_K_PREFILL, stream));
-      if (err) return KVC_E_HIP;
+      pa->dec_split_keys = decode_split_keys(h, lx, D, dcap);
+      decode_order(h, lx, pa);
+      pa->pre_split_keys = (int32_t)std::max<int64_t>(
+          kChunkSplitMin, round_up(ceil_div(max_chunk_span, ccap), kvc::kRowAlign));
+      int64_t dec_items = 0, pre_items = 0;
+      for (int32_t b = 0; b < B; ++b) {
+        const int64_t L = h->lens_host[b], n = h->n_new[b];
+        int64_t base, hi;
+        if (n == 1) {
+          decode_span(lx, L, h->first_host[b], &base, &hi);
+          dec_items += ceil_div(hi - base, pa->dec_split_keys);
+        } else if (n >= 2) {
+          const int64_t nqt = ceil_div(n * lx.rep, kvc::kChunkQTile);
+          int64_t nks = 1;
+          if (!lx.ring) {
+            chunk_span(lx, L, n, h->first_host[b], &base, &hi);
+            nks = ceil_div(hi - base, pa->pre_split_keys);
+          }
+          pre_items += nqt * nks;
+        }
+      }
+      if (h->log_level >= 2 && layer == 0 && dec_items > 0)
+        std::fprintf(stderr, "[kvc] decode plan: %d keys per split, %lld waves\n",
+                     pa->dec_split_keys, (long long)dec_items * lx.hkv);
+      if (dec_items > 0 &&
+          kvc::launch_decode(st, lx, *pa, q, (int32_t)dec_items, launch_on(h, KVC_K_DECODE, stream)))
+        return KVC_E_HIP;
+      if (pre_items > 0 &&
+          kvc::launch_prefill(st, lx, *pa, q, (int32_t)pre_items, launch_on(h, KVC_K_PREFILL, stream)))
+        return KVC_E_HIP;
+      return KVC_OK;
+    };
+    kvc::PartialArgs pa = partial_args(h);
+    if (run(la, &pa) != KVC_OK) return KVC_E_HIP;
+    if (joint) {
+      kvc::PartialArgs pj = partial_args(h);
+      pj.base = kvc::SplitRef{1, la.ring, la.window, pa.dec_split_keys, pa.pre_split_keys};
+      if (run(lj, &pj) != KVC_OK) return KVC_E_HIP;
+      pa.joint = kvc::SplitRef{1, lj.ring, lj.window, pj.dec_split_keys, pj.pre_split_keys};
     }
     err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
     if (err) return KVC_E_HIP;
@@ -802,7 +830,7 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   const kvc::LayerArgs la = layer_args(h, layer);
   const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
   const bool fused = C == 1 && !h->no_fused && h->cfg.dtype == KVC_BF16 &&
-                     kvc::fast_decode_supported(D, la.rep);
+                     kvc::fast_decode_supported(D, la.rep) && h->lay.layers[layer].joint < 0;
   if (!fused) {
     const int rc = kvc_append(h, layer, k, v, n_new_host, C, slot_out_dev, stream);
     if (rc != KVC_OK) return rc;
@@ -849,7 +877,7 @@ int kvc_advance(kvc_t *h, void *stream) {
   if (!h) return KVC_E_ARG;
   if (!h->in_step) return KVC_E_STATE;
   for (int32_t l = 0; l < h->cfg.n_layer; ++l)
-    if (!h->appended[l] || !h->attended[l]) return KVC_E_STATE;
+    if (!h->appended[l] || (!h->attended[l] && !h->partner_only[l])) return KVC_E_STATE;
   if (!use_device(h)) return KVC_E_HIP;
   int32_t *lens = reinterpret_cast<int32_t *>(h->base + h->lay.lens_off);
   const int32_t *nn = reinterpret_cast<const int32_t *>(h->base + h->lay.nnew_off);
@@ -908,6 +936,8 @@ int kvc_static_begin(kvc_t *h, const int32_t *n_new_dev, void *stream) {
   if (!h || !n_new_dev) return KVC_E_ARG;
   if (h->in_step) return KVC_E_STATE;
   if ((int32_t)h->classes.size() > kvc::kStaticClassMax) return KVC_E_ARG;
+  for (const LayerLayout &L : h->lay.layers)
+    if (L.joint >= 0) return KVC_E_ARG;  // joint layers plan on the host
   if (!use_device(h)) return KVC_E_HIP;
   kvc::StaticBeginArgs a{};
   a.n_src = n_new_dev;

@@ -31,6 +31,7 @@ constexpr int kChunkQTile = 256;
 
 struct LayerLayout {
   int64_t k_off = 0, v_off = 0;           // byte offsets in the device buffer (paged: the pools)
+  int32_t joint = -1;                     // partner layer of a joint softmax, or -1
   int32_t paged = 0;                      // full layout from a shared page pool
   int64_t sk_off = -1, sv_off = -1;       // staging (ring layers, max_chunk >= 2)
   int32_t hkv = 0, window = 0, ring = 0;  // ring: 0 < W < max_len and use_ring
@@ -92,6 +93,15 @@ struct StepArgs {
   int32_t B, C, Hq, D, max_len;
 };
 
+// Joint attention (a layer whose softmax also covers a partner layer's
+// keys): a query's partial slots hold the layer's own splits first, then the
+// partner's.  A SplitRef describes one layer's splits so a kernel can count
+// them for a row: decode splits of its span (dec_sk keys each), or for a
+// chunk row its key splits (pre_sk keys each; 1 on a ring).
+struct SplitRef {
+  int32_t on, ring, window, dec_sk, pre_sk;
+};
+
 struct PartialArgs {
   float *dml, *dout;      // decode partials
   float *pml, *pout;      // chunk partials
@@ -109,6 +119,8 @@ struct PartialArgs {
   // dec_split_keys / dec_order (null: host plan).
   const int32_t *dec_plan;
   const uint16_t *dec_order_dev;
+  SplitRef base;   // a launch over the partner's keys: its slots follow these splits
+  SplitRef joint;  // the combine: the partner's splits follow the layer's own
 };
 constexpr int kDecodeOrderMax = 256;
 
@@ -204,8 +216,9 @@ int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &p
                    const void *q, int32_t n_items, const Launch &lc);
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                    void *out, const Launch &lc);
-int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const void *q,
-                   void *out, const Launch &lc);
+// lj: the joint partner's layer (lj.k == nullptr: none).
+int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const LayerArgs &lj,
+                   const void *q, void *out, const Launch &lc);
 bool fast_decode_supported(int D, int rep);
 // Decode workgroups (one wave each) resident per compute unit; 0 on error.
 int decode_waves_per_cu(int D, int rep);

@@ -112,6 +112,17 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
     if (!take(&cur, B * lay->pages_per_row * 4, &lay->table_off) || !take(&cur, B * 4, &lay->cap_off))
       return KVC_E_ARG;
   }
+  // Joint partners: an earlier full-layout layer with the same KV heads and
+  // no partner of its own.
+  for (int l = 0; l < cfg->n_layer; ++l) {
+    const int32_t j = cfg->joint ? cfg->joint[l] : -1;
+    if (j < -1 || j >= l) return KVC_E_ARG;
+    lay->layers[l].joint = j;
+    if (j >= 0) {
+      const LayerLayout &P = lay->layers[j];
+      if (P.ring || P.hkv != lay->layers[l].hkv || (cfg->joint[j] >= 0)) return KVC_E_ARG;
+    }
+  }
   // Static steps: error bits, and per layer class a split length and a row order.
   if (!take(&cur, 4, &lay->flags_off)) return KVC_E_ARG;
   if (!take(&cur, (int64_t)cfg->n_layer * (4 + 2 * B), &lay->plan_off)) return KVC_E_ARG;

@@ -65,7 +65,8 @@ class Pair:
                              device=self.device)
         self.cache = K.Cache(cfg, self.device, buffer=buf)
         self.ref = oracle.OracleCache(work.batch, work.n_q_head, work.n_kv_head, work.head_dim,
-                                      work.max_len, work.window, work.rope_base)
+                                      work.max_len, work.window, work.rope_base,
+                                      joint=work.joint or None)
         self.step_no = 0
         self.worst = 0.0
         self.worst_rel = 0.0

@@ -136,3 +136,16 @@ def test_paged_sizes_and_validation():
     assert K.kvc_nbytes(paged, K.KVC_NB_ALLOC) > K.kvc_nbytes(paged, K.KVC_NB_KV)
     bad = K.make_config(2, 4, 8, 64, 256, 16, "bf16", [2, 2], [0, 32], n_pages=-1)
     assert K.kvc_nbytes(bad, K.KVC_NB_KV) == 0
+
+
+def test_joint_partner_validation():
+    # tiny_agent hybrid groups: a layer's joint partner is an earlier
+    # full-layout layer with the same KV heads and no partner of its own
+    def nb(joint, hkv=(2, 2, 2, 2)):
+        cfg = K.make_config(4, 2, 8, 64, 128, 16, "bf16", list(hkv), [0, 16, 8, 0], joint=joint)
+        return K.kvc_nbytes(cfg, K.KVC_NB_ALLOC)
+    assert nb([-1, 0, 0, -1]) > 0 and nb([-1, 0, 0, 0]) > 0
+    assert nb([-1, 1, 0, -1]) == 0           # itself
+    assert nb([-1, 2, 0, -1]) == 0           # a later layer
+    assert nb([-1, 0, 1, -1]) == 0           # a ring
+    assert nb([-1, 0, 0, -1], hkv=(2, 1, 2, 2)) == 0   # other KV heads

@@ -51,6 +51,7 @@ class Workload:
     rope_base: float = 10000.0
     use_ring: bool = True
     n_pages: int = 0           # > 0: paged full layers with a pool of this many 16-row pages
+    joint: tuple = ()          # per layer: joint softmax partner layer, -1 none (empty: none)
     notes: str = field(default="", compare=False)
 
     @property
