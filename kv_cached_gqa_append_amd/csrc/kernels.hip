@@ -855,15 +855,21 @@ struct DecodeShape {
   static constexpr int NCH = D / 8 / LK;        // 16-byte chunks per lane per key
   static constexpr int VT = D / 32;             // V head-dim rows per lane
   static constexpr int HPL = REP >= LK ? REP / LK : 1;   // heads whose scores a lane owns
-  // Register tile ring and occupancy target per SIMD.  Two tiles in flight
-  // per wave (8 KB of K and V at D 128) keep HBM busy at two waves per SIMD;
-  // deeper rings measured no faster and only lengthen the queues every
-  // dependent round trip waits in.  REP 16 at D 128 holds 64 accumulators and
-  // 64 query registers per lane: it runs one wave per SIMD with the full
-  // register file rather than spill.
+  // Register tile ring and occupancy target per SIMD.  Shapes with
+  // REP * D < 1024 keep one tile in flight beside the one in use and run
+  // three waves per SIMD (136 VGPRs at D 128, REP 4): more independent
+  // streams per CU measured 3 % faster than two waves with two tiles in
+  // flight each (the same bytes in flight).  Larger shapes would spill at
+  // three waves and keep two, with two tiles in flight.  REP 16 at D 128
+  // holds 64 accumulators and 64 query registers per lane: it runs one wave
+  // per SIMD with the full register file rather than spill.
   static constexpr bool BIG = REP * D >= 2048;
-  static constexpr int NBUF = REP <= 8 ? 3 : 2;
-  static constexpr int WAVES = BIG ? 1 : 2;
+  static constexpr bool SMALL = REP * D < 1024;
+  static constexpr int NBUF = SMALL ? 2 : (REP <= 8 ? 3 : 2);
+  static constexpr int WAVES = SMALL ? 3 : (BIG ? 1 : 2);
+  // the single-kernel step (it also holds the merge's registers: two waves)
+  static constexpr int FNBUF = REP <= 8 ? 3 : 2;
+  static constexpr int FWAVES = BIG ? 1 : 2;
   static_assert(NCH >= 1 && NR >= 1 && D % 32 == 0, "unsupported decode shape");
 };
 
@@ -1188,7 +1194,8 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
 // PAGED: a paged full layer; each 16-row tile is one page, found in the
 // block table when the tile's loads are issued.
 template <int D, int REP, bool FUSED = false, bool PAGED = false,
-          int NBUF = DecodeShape<D, REP>::NBUF, int WAVES = DecodeShape<D, REP>::WAVES>
+          int NBUF = FUSED ? DecodeShape<D, REP>::FNBUF : DecodeShape<D, REP>::NBUF,
+          int WAVES = FUSED ? DecodeShape<D, REP>::FWAVES : DecodeShape<D, REP>::WAVES>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
               FusedArgs fa, const int32_t *__restrict__ ptab) {
