@@ -1697,20 +1697,25 @@ struct KeySeg {
 
 // PAGED: a paged full layer; a 32-row tile spans two pages, and the chunks
 // each wave loads lie in one of them.
-template <int D, int REP, bool PAGED = false>
-__global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
-                                               const bf16 *__restrict__ q,
-                                               const int32_t *__restrict__ ptab) {
+// QW: waves per workgroup, 32 query rows each (8: 256-row query tiles, the
+// only workgroup on its CU; 4: 128-row tiles for short chunks, two per CU).
+template <int D, int REP, bool PAGED = false, int QW = 8>
+__global__ __launch_bounds__(QW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
+                                                   const bf16 *__restrict__ q,
+                                                   const int32_t *__restrict__ ptab) {
   constexpr int NDS = D / 32;              // 32-wide d steps (QK contraction)
   constexpr int NDB = D / 16;              // 16-wide d blocks (PV output)
   constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
   constexpr int KCH = 32 * D / 8;          // 16-byte chunks of a K tile (= of a V tile)
+  constexpr int NT = QW * 64;              // threads
+  constexpr int QT = QW * 32;              // query rows per workgroup
+  constexpr int LPT = KCH > NT ? KCH / NT : 1;  // K (and V) chunks per thread per tile
   constexpr int NSTAGE = 3;
-  // Tiles in flight per thread (one K and one V 16-byte chunk each): the
-  // workgroup is the only one on its CU, so its own loads must cover the
-  // memory latency.
-  constexpr int CP = D >= 128 ? 6 : 8;
-  static_assert(KCH <= 512, "one K chunk and one V chunk per thread");
+  // Tiles in flight per thread (LPT K and LPT V 16-byte chunks each): the
+  // workgroup's own loads must cover the memory latency.
+  constexpr int CP = (D >= 128 ? 6 : 8) / LPT;
+  static_assert(KCH <= NT * LPT && CP >= 2, "chunk mapping");
   __shared__ __align__(16) bf16 lk[NSTAGE][32 * KSTR];
   // V^T of a tile: row d holds the 32 keys in the order the PV operand of
   // lane group q4 takes them (keys 4q4..4q4+3, then 16+4q4..16+4q4+3), so an
@@ -1732,7 +1737,11 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
       [&](int r) -> int {
         const int n = st.n_new[r];
         if (n < 2) return 0;
-        const int nqt = (int)cdiv((int64_t)n * REP, kChunkQTile);
+        // with small_rows set, rows of at most 128 query rows go to the
+        // 4-wave launch and the rest to the 8-wave one
+        const bool small = n * REP <= 4 * 32;
+        if (pa.chunk_small && small != (QW == 4)) return 0;
+        const int nqt = (int)cdiv((int64_t)n * REP, QT);
         if (la.ring) return nqt;
         int64_t base, lo, hi;
         chunk_span_dev(la, st.lens[r], n, st.first[r], &base, &lo, &hi);
@@ -1759,7 +1768,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   bf16x8_t qf[2][NDS];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    rq[blk] = qt * kChunkQTile + wave * 32 + blk * 16 + nl;
+    rq[blk] = qt * QT + wave * 32 + blk * 16 + nl;
     rvalid[blk] = rq[blk] < n * REP;
     qi[blk] = rq[blk] / REP;
     hl[blk] = rq[blk] % REP;
@@ -1804,9 +1813,8 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
 
   // -- key segments -------------------------------------------------------------
   // Positions of the whole q-tile span [pmin, pmax].
-  const int rlast = (qt + 1) * kChunkQTile - 1 < n * REP - 1 ? (qt + 1) * kChunkQTile - 1
-                                                              : n * REP - 1;
-  const int64_t pmin = L + (int64_t)(qt * kChunkQTile) / REP;
+  const int rlast = (qt + 1) * QT - 1 < n * REP - 1 ? (qt + 1) * QT - 1 : n * REP - 1;
+  const int64_t pmin = L + (int64_t)(qt * QT) / REP;
   const int64_t pmax = L + rlast / REP;
   KeySeg seg0{}, seg1{};
   if (!la.ring) {
@@ -1857,15 +1865,15 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   const i32x4 dk1 = la.ring ? sgpr_rsrc(seg1.kreg + bg * reg1, (int)reg1) : dk0;
   const i32x4 dv1 = la.ring ? sgpr_rsrc(seg1.vreg + bg * reg1, (int)reg1) : dv0;
   const i32x4 dnone = sgpr_rsrc(seg0.kreg, 0);
-  // Threads past a tile's chunk count (D < 128: whole waves) load nothing.
+  // Thread tid loads chunks tid + e * NT (e < LPT) of each tile; threads
+  // past a tile's chunk count (D < 128: whole waves) load nothing.
   const bool loader = wave * 64 < KCH;
-  const int voffs = tid * 16;
-  // paged: bytes of one head's page, the page of the tile this wave's chunks
-  // fall in (K row tid / (D / 8) and V block tid / (2 D) agree), and the
-  // chunk's offset inside it
+  // paged: bytes of one head's page, the page of the tile a wave's chunk e
+  // falls in (K row c / (D / 8) and V block c / (2 D) agree; 64 chunks never
+  // straddle a page), and the chunk's offset inside it
   constexpr int page_b = kPageRows * D * 2;
-  const int phalf = __builtin_amdgcn_readfirstlane(wave * 32 / D);
-  const int poffs = voffs % page_b;
+  auto voffs = [&](int e) { return (tid + e * NT) * 16; };
+  auto phalf = [&](int e) { return __builtin_amdgcn_readfirstlane(((wave * 64 + e * NT) * 16) / page_b); };
 
   // Tile i: its segment, first storage row and bounds (uniform scalars).
   struct TileInfo {
@@ -1887,37 +1895,44 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   };
   // Issue the loads of tile i (zeros and no memory access past the last
   // tile or for threads without a chunk): one K and one V 16-byte chunk.
-  auto issue = [&](int i, u32x4 &rk, u32x4 &rv) __attribute__((always_inline)) {
+  auto issue = [&](int i, u32x4 (&rk)[LPT], u32x4 (&rv)[LPT]) __attribute__((always_inline)) {
     const bool live = loader && i < ntiles;
     const bool second = i >= n0;
     const TileInfo ti = tile_of(live ? i : 0);
     const int64_t t0 = ti.t0;
-    if constexpr (PAGED) {
-      // this wave's K rows and V block of the tile lie in its page `phalf`
-      const int idx = live ? (int)(t0 / kPageRows) + phalf : 0;
-      const int pg = ptab[(int64_t)b * la.ppr + idx];
-      const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
-      const i32x4 ka = rsrc_sel(live, sgpr_rsrc(la.k + off, page_b), dnone);
-      const i32x4 va = rsrc_sel(live, sgpr_rsrc(la.v + off, page_b), dnone);
-      tile_load<0>(rk, ka, poffs, 0);
-      tile_load<0>(rv, va, poffs, 0);
-    } else {
-      const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
-      const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
-      // K rows and V blocks advance by the same bytes per row
-      const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
-      tile_load<0>(rk, ka, voffs, so);
-      tile_load<0>(rv, va, voffs, so);
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+      if constexpr (PAGED) {
+        // this wave's chunk e of the tile lies in the tile's page phalf(e)
+        const int idx = live ? (int)(t0 / kPageRows) + phalf(e) : 0;
+        const int pg = ptab[(int64_t)b * la.ppr + idx];
+        const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
+        const i32x4 ka = rsrc_sel(live, sgpr_rsrc(la.k + off, page_b), dnone);
+        const i32x4 va = rsrc_sel(live, sgpr_rsrc(la.v + off, page_b), dnone);
+        tile_load<0>(rk[e], ka, voffs(e) % page_b, 0);
+        tile_load<0>(rv[e], va, voffs(e) % page_b, 0);
+      } else {
+        const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
+        const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
+        // K rows and V blocks advance by the same bytes per row
+        const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
+        tile_load<0>(rk[e], ka, voffs(e), so);
+        tile_load<0>(rv[e], va, voffs(e), so);
+      }
     }
   };
   // Write tile i's chunks (already waited for) to LDS stage s; V rows outside
   // the segment's data are zeroed (their p is 0, and 0 times garbage could be
   // NaN).
-  auto store = [&](int i, const u32x4 &rk, const u32x4 &rv, int s) __attribute__((always_inline)) {
+  auto store = [&](int i, const u32x4 (&rka)[LPT], const u32x4 (&rva)[LPT], int s)
+                   __attribute__((always_inline)) {
     if (!loader) return;
     const TileInfo ti = tile_of(i < ntiles ? i : 0);
     const int64_t t0 = ti.t0, vlo = ti.vlo, vhi = ti.vhi;
-    const int c = tid;
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+    const u32x4 &rk = rka[e], &rv = rva[e];
+    const int c = tid + e * NT;
     const int rr = c / (D / 8), cc = c % (D / 8);
     *reinterpret_cast<u32x4 *>(&lk[s][rr * KSTR + cc * 8]) = rk;
     u32x4 x = rv;
@@ -1939,6 +1954,7 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
     bf16 *row = &lv[s][dd * VSTR + blk * 4];
     *reinterpret_cast<uint2 *>(row + (2 * kh) * 8) = make_uint2(x[0], x[1]);
     *reinterpret_cast<uint2 *>(row + (2 * kh + 1) * 8) = make_uint2(x[2], x[3]);
+    }
   };
 
   const float scale = kLog2e * rsqrtf((float)D);
@@ -2071,18 +2087,26 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   // is padded with empty steps, so every path keeps the same loads in flight.
   // The queries' loads above are retired before the first tile load.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  u32x4 rk[CP], rv[CP];
+  // (a set's loads retire together: waiting for its first register while
+  // the later sets' 2 LPT (P - 1) loads stay outstanding covers all of it)
+  constexpr int AFTER = 2 * LPT * (CP - 1);
+  auto wait_set = [&](u32x4 (&rka)[LPT], u32x4 (&rva)[LPT]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+      tile_wait<AFTER>(rka[e]);
+      tile_wait<AFTER>(rva[e]);
+    }
+  };
+  u32x4 rk[CP][LPT], rv[CP][LPT];
   static_for<0, CP>([&](auto t) { issue(decltype(t)::value, rk[decltype(t)::value], rv[decltype(t)::value]); });
-  tile_wait<2 * (CP - 1)>(rk[0]);
-  tile_wait<2 * (CP - 1)>(rv[0]);
+  wait_set(rk[0], rv[0]);
   store(0, rk[0], rv[0], 0);
   issue(CP, rk[0], rv[0]);
   for (int i0 = 0; i0 < ntiles; i0 += CP) {
     static_for<0, CP>([&](auto u) {
       constexpr int S = (decltype(u)::value + 1) % CP;   // set of tile i + 1
       const int i = i0 + decltype(u)::value;
-      tile_wait<2 * (CP - 1)>(rk[S]);
-      tile_wait<2 * (CP - 1)>(rv[S]);
+      wait_set(rk[S], rv[S]);
       store(i + 1, rk[S], rv[S], (i + 1) % NSTAGE);
       issue(i + 1 + CP, rk[S], rv[S]);
       lds_barrier();
@@ -2091,8 +2115,11 @@ __global__ __launch_bounds__(512) void k_chunk(StepArgs st, LayerArgs la, Partia
   }
   // Retire the loads still in flight before their registers go away.
   static_for<0, CP>([&](auto t) {
-    tile_wait<0>(rk[decltype(t)::value]);
-    tile_wait<0>(rv[decltype(t)::value]);
+#pragma unroll
+    for (int e = 0; e < LPT; ++e) {
+      tile_wait<0>(rk[decltype(t)::value][e]);
+      tile_wait<0>(rv[decltype(t)::value][e]);
+    }
   });
   asm volatile("" ::: "memory");
 
@@ -2126,20 +2153,28 @@ bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && re
 
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                           const void *q, int32_t n_items, const Launch &lc) {
+                           const void *q, int32_t n_items, int qw, const Launch &lc) {
   const dim3 grid((unsigned)n_items, (unsigned)la.hkv);
-  if (la.paged)
+  if (qw == 4) {
+    if (la.paged)
+      launch_kernel((k_chunk<D, REP, true, 4>), grid, dim3(256), lc, st, la, pa, (const bf16 *)q,
+                    la.table);
+    else
+      launch_kernel((k_chunk<D, REP, false, 4>), grid, dim3(256), lc, st, la, pa, (const bf16 *)q,
+                    la.table);
+  } else if (la.paged) {
     launch_kernel((k_chunk<D, REP, true>), grid, dim3(512), lc, st, la, pa, (const bf16 *)q,
                   la.table);
-  else
+  } else {
     launch_kernel((k_chunk<D, REP>), grid, dim3(512), lc, st, la, pa, (const bf16 *)q, la.table);
+  }
 }
 
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa, const void *q,
-                   int32_t n_items, const Launch &lc) {
+                   int32_t n_items, int qw, const Launch &lc) {
 #define KVC_CHK(DD, RR)                                         \
   if (st.D == DD && la.rep == RR) {                             \
-    launch_chunk_t<DD, RR>(st, la, pa, q, n_items, lc);     \
+    launch_chunk_t<DD, RR>(st, la, pa, q, n_items, qw, lc);     \
     return (int)hipGetLastError();                              \
   }
   KVC_CHK(128, 1) KVC_CHK(128, 2) KVC_CHK(128, 4) KVC_CHK(128, 8) KVC_CHK(128, 16)

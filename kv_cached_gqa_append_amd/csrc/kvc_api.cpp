@@ -52,6 +52,7 @@ struct kvc_cache {
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
+  bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
   bool lens_stale = false;            // a static step advanced the device lengths only
@@ -474,6 +475,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     if (v >= 1 && v <= 4096) h->dec_min_tiles = (int32_t)v;
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
     const LayerLayout &L = h->lay.layers[l];
@@ -775,7 +777,11 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       decode_order(h, lx, pa);
       pa->pre_split_keys = (int32_t)std::max<int64_t>(
           kChunkSplitMin, round_up(ceil_div(max_chunk_span, ccap), kvc::kRowAlign));
-      int64_t dec_items = 0, pre_items = 0;
+      // Chunk rows of at most 128 query rows (a 4-wave workgroup's tile) go
+      // to a 4-wave launch, two of whose workgroups share a CU, instead of
+      // leaving half of an 8-wave workgroup idle.
+      pa->chunk_small = h->no_chunk_small ? 0 : 1;
+      int64_t dec_items = 0, pre_items = 0, small_items = 0;
       for (int32_t b = 0; b < B; ++b) {
         const int64_t L = h->lens_host[b], n = h->n_new[b];
         int64_t base, hi;
@@ -783,24 +789,32 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
           decode_span(lx, L, h->first_host[b], &base, &hi);
           dec_items += ceil_div(hi - base, pa->dec_split_keys);
         } else if (n >= 2) {
-          const int64_t nqt = ceil_div(n * lx.rep, kvc::kChunkQTile);
+          const bool small = pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2;
+          const int64_t nqt = ceil_div(n * lx.rep, small ? kvc::kChunkQTile / 2 : kvc::kChunkQTile);
           int64_t nks = 1;
           if (!lx.ring) {
             chunk_span(lx, L, n, h->first_host[b], &base, &hi);
             nks = ceil_div(hi - base, pa->pre_split_keys);
           }
-          pre_items += nqt * nks;
+          (small ? small_items : pre_items) += nqt * nks;
         }
       }
       if (h->log_level >= 2 && layer == 0 && dec_items > 0)
         std::fprintf(stderr, "[kvc] decode plan: %d keys per split, %lld waves\n",
                      pa->dec_split_keys, (long long)dec_items * lx.hkv);
+      // (Running the decode launch on a second stream beside the chunk
+      // launches measured 4 % slower on mixed steps: they take CUs from each
+      // other, so they stay in order on one stream.)
       if (dec_items > 0 &&
           kvc::launch_decode(st, lx, *pa, q, (int32_t)dec_items, launch_on(h, KVC_K_DECODE, stream)))
         return KVC_E_HIP;
-      if (pre_items > 0 &&
-          kvc::launch_prefill(st, lx, *pa, q, (int32_t)pre_items, launch_on(h, KVC_K_PREFILL, stream)))
+      if (pre_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)pre_items, 8,
+                                               launch_on(h, KVC_K_PREFILL, stream)))
         return KVC_E_HIP;
+      if (small_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)small_items, 4,
+                                                 launch_on(h, KVC_K_PREFILL, stream)))
+        return KVC_E_HIP;
+
       return KVC_OK;
     };
     kvc::PartialArgs pa = partial_args(h);

@@ -119,6 +119,7 @@ struct PartialArgs {
   // dec_split_keys / dec_order (null: host plan).
   const int32_t *dec_plan;
   const uint16_t *dec_order_dev;
+  int32_t chunk_small;  // chunk rows of <= 128 query rows go to a 4-wave launch
   SplitRef base;   // a launch over the partner's keys: its slots follow these splits
   SplitRef joint;  // the combine: the partner's splits follow the layer's own
 };
@@ -212,8 +213,11 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // idle row.
 int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                         const void *q, const FusedArgs &fa, int32_t n_items, const Launch &lc);
+// qw: waves per workgroup (8: 256 query rows per item; 4: 128).  With
+// pa.chunk_small, the 4-wave launch takes the rows of at most 128 query rows
+// and the 8-wave launch the rest.
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                   const void *q, int32_t n_items, const Launch &lc);
+                   const void *q, int32_t n_items, int qw, const Launch &lc);
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                    void *out, const Launch &lc);
 // lj: the joint partner's layer (lj.k == nullptr: none).
