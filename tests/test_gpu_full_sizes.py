@@ -177,3 +177,39 @@ def test_long_5to1_full_size():
     z = torch.zeros(work.batch, 1, 8, work.head_dim, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(K.CacheFullError):
         cache.append(0, z, z, [1] + [0] * (work.batch - 1))
+
+
+def test_decode_b64_paged_full_size():
+    # The headline shape on a paged cache (pool = the contiguous cache's
+    # rows) against the contiguous cache, bit for bit, with a sampled oracle
+    # on a few rows; rows fill in turns, so their pages interleave.
+    say("case: decode_b64 full size (2 layers), paged vs contiguous, sampled oracle")
+    steps = 3
+    work = wl.DECODE_B64.replace(n_layer=2, n_kv_head=(8, 8), window=(0, 0))
+    paged_work = work.replace(n_pages=work.batch * work.max_len // 16)
+    lens0 = np.minimum(wl.initial_lens_decode_b64(work.batch), work.max_len - steps)
+    flat = K.Cache(K.config_from_workload(work), DEV)
+    paged = K.Cache(K.config_from_workload(paged_work), DEV)
+    r = wl.rng("full_sizes", "paged_rows")
+    rows = sorted({int(np.argmax(lens0))} | set(int(x) for x in r.choice(work.batch, 3, replace=False)))
+    so = SampledOracle(work, rows)
+    _fill([flat, paged], work, lens0, "pfill", so)
+    st = paged.page_stats()
+    assert st["used"] == int(lens0.sum()) and st["allocated"] == int(sum(-(-int(L) // 16) for L in lens0)) * 16
+    for s in range(steps):
+        n = wl.n_new_decode_b64(s, work.batch)
+        qkv = [wl.device_step_qkv(work, l, 30_000 + s, 1, DEV, "pdec") for l in range(2)]
+        of, op = [], []
+        for l, (q, k, v) in enumerate(qkv):
+            flat.append(l, k, v, n)
+            of.append(flat.attend(l, q))
+            op.append(paged.append_attend(l, q, k, v, n) if s % 2 else
+                      (paged.append(l, k, v, n), paged.attend(l, q))[1])
+        flat.advance()
+        paged.advance()
+        torch.cuda.synchronize()
+        for l in range(2):  # (odd steps: the paged cache through the single-kernel step)
+            assert torch.equal(of[l], op[l]), f"step {s} layer {l}: paged output differs"
+        mx, rel = so.check_step(n, qkv, op, lambda b, nb: [0], f"paged decode_b64 step {s}")
+        say(f"  step {s}: rows {rows} worst abs {mx:.2e} rel {rel:.2e}")
+    assert paged.lens() == flat.lens()
