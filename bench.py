@@ -286,7 +286,9 @@ def fill_history(cache, work, target, dev):
             torch.cuda.synchronize()
             log(f"[bench] fill step {si + 1}/{len(plan)} ({time.perf_counter() - t0:.1f}s)")
     torch.cuda.synchronize()
-    log(f"[bench] history filled: {len(plan)} chunk steps in {time.perf_counter() - t0:.1f}s")
+    dt = time.perf_counter() - t0
+    log(f"[bench] history filled: {len(plan)} chunk steps in {dt:.1f}s")
+    return dt
 
 
 PEAK_BF16_TFLOPS = 2500.0
@@ -458,7 +460,9 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
     cache = K.Cache(cfg, dev)
     B, D, L = work.batch, work.head_dim, work.n_layer
     prefill = 510 * 64
-    fill_history(cache, work, np.full(B, prefill), dev)
+    fill_s = fill_history(cache, work, np.full(B, prefill), dev)
+    log(f"[bench] long prefill: {B * prefill / fill_s:.0f} tok/s over the {L}-layer stack "
+        f"(510 chunk steps of 64 tokens, {fill_s:.2f} s wall, with the progress syncs)")
     assert 2 * (warmup + steps + class_steps) + warmup + steps <= work.max_len - prefill
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed_of(work.name, "decode"))
@@ -559,6 +563,9 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
                          f"Hq{work.n_q_head}/Hkv8, D{D}, bf16, max_len {work.max_len}"),
             "steps": steps, "warmup": warmup, "class_steps": class_steps,
             "kv_nbytes": {"rings": nb_ring, "full": nb_full},
+            "prefill": {"tokens_per_s": round(B * prefill / fill_s, 1), "wall_s": round(fill_s, 3),
+                        "what": "510 chunk steps of 64 tokens through kvc_append + kvc_attend "
+                                "over all 66 layers, B 8, to 32,640 tokens"},
             "entries": legs}
 
 def paged_leg(dev, steps, warmup):
