@@ -1280,44 +1280,8 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     }
   }
 
-  // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
-  const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
-  for (int e = lane; e < REP * D; e += 64) {
-    const int h = e / D, d = e % D;
-    float x = (float)qsrc[e];
-    if (st.rope) {
-      const int di = d < D / 2 ? d : d - D / 2;
-      const float c = st.rope[(p * (D / 2) + di) * 2 + 0];
-      const float sn = st.rope[(p * (D / 2) + di) * 2 + 1];
-      const float other = (float)qsrc[h * D + (d < D / 2 ? d + D / 2 : d - D / 2)];
-      x = d < D / 2 ? x * c - other * sn : other * sn + x * c;
-    }
-    qs[e] = x;
-  }
-  __syncthreads();
   const int kr = lane / LK, j = lane % LK;          // QK: key in round, chunk group
   const int half = lane >> 5, mm = lane & 31;       // PV: key half, head-dim row
-  uint32_t qp[REP][NCH][4];
-#pragma unroll
-  for (int h = 0; h < REP; ++h)
-#pragma unroll
-    for (int t = 0; t < NCH; ++t)
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int d = (j + LK * t) * 8 + 2 * e2;
-        qp[h][t][e2] = pack_bf16(qs[h * D + d], qs[h * D + d + 1]);
-      }
-  if constexpr (FUSED) {
-    if (appender) {
-      float y1 = ax1, y2 = ax2;
-      if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
-      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
-    }
-    // The tile loads below come after these stores in program order (the
-    // barrier keeps the compiler from moving the stores past them), and the
-    // memory pipeline keeps one wave's accesses to one address in order.
-    asm volatile("" ::: "memory");
-  }
 
   // -- buffer resources over this head's K and V ------------------------------
   const int64_t region = (int64_t)la.rows_alloc * D * 2;  // bytes per (b, g)
@@ -1376,6 +1340,72 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
 #pragma unroll
     for (int t = 0; t < VT; ++t) tile_wait<N>(T.v[t]);
   };
+
+  // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
+  // The loads of the queries and their rotation go out first.  The plain
+  // kernel then issues its first tiles before it waits for them, so the
+  // queries' round trip and the first tiles' overlap; the single-kernel step
+  // issues its tiles after the appending wave has stored the new row.
+  constexpr int QE = REP * D / 64;                  // query elements per lane
+  const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
+  // (no branch around the loads, so they go out back to back and their
+  // values are converted where they are used: without a table, the
+  // rotation's load reads the query row, 16-byte aligned, and is not used)
+  bf16 qx[QE], qo[QE];
+  float2 qcs[QE];
+  const bool rot = st.rope != nullptr;
+#pragma unroll
+  for (int i = 0; i < QE; ++i) {
+    const int e = lane + 64 * i, h = e / D, d = e % D;
+    const int di = d < D / 2 ? d : d - D / 2;
+    qx[i] = qsrc[e];
+    qo[i] = qsrc[h * D + (d < D / 2 ? d + D / 2 : d - D / 2)];
+    qcs[i] = *reinterpret_cast<const float2 *>(
+        rot ? st.rope + (p * (D / 2) + di) * 2 : reinterpret_cast<const float *>(qsrc));
+  }
+  Tile T[NBUF];
+  if constexpr (!FUSED) {
+    // (the barrier keeps the compiler from issuing the loads above after the
+    // tile loads: every vector memory access of the wave is then older than
+    // the tiles, as the hand-placed tile waits require)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < QE; ++i) {
+    const int e = lane + 64 * i, d = e % D;
+    const float x = (float)qx[i];
+    const float o = (float)qo[i], c = qcs[i].x, sn = qcs[i].y;
+    const float xr = d < D / 2 ? x * c - o * sn : o * sn + x * c;
+    qs[e] = rot ? xr : x;
+  }
+  // One wave: its LDS accesses execute in order, so the reads below see the
+  // writes above without a barrier (which would also wait for the tiles).
+  __builtin_amdgcn_wave_barrier();
+  uint32_t qp[REP][NCH][4];
+#pragma unroll
+  for (int h = 0; h < REP; ++h)
+#pragma unroll
+    for (int t = 0; t < NCH; ++t)
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const int d = (j + LK * t) * 8 + 2 * e2;
+        qp[h][t][e2] = pack_bf16(qs[h * D + d], qs[h * D + d + 1]);
+      }
+  if constexpr (FUSED) {
+    if (appender) {
+      float y1 = ax1, y2 = ax2;
+      if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
+      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
+    }
+    // The tile loads below come after these stores in program order (the
+    // barrier keeps the compiler from moving the stores past them), and the
+    // memory pipeline keeps one wave's accesses to one address in order.
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
+  }
 
   const float scale = kLog2e * rsqrtf((float)D);
   float m[HPL], lsum[HPL], acc[REP][VT];
@@ -1492,14 +1522,11 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     if (REP < LK) writer = (j & (LK / REP - 1)) == 0;
   }
 
-  // Ring of NBUF register tiles; NBUF - 1 tiles are in flight while one
-  // computes.  Unrolled by NBUF so buffer indices are compile-time.  Loads
+  // Ring of NBUF register tiles (the first NBUF - 1 issued above); NBUF - 1
+  // tiles are in flight while one computes.  Unrolled by NBUF so buffer indices are compile-time.  Loads
   // and waits run for whole groups (loads past the end read nothing and
   // return zeros) and only the compute is skipped past the end, so the
   // loop has one back edge and always the same loads in flight.
-  Tile T[NBUF];
-#pragma unroll
-  for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
   for (int it = 0; it < n_iter; it += NBUF) {
 #pragma unroll
     for (int u = 0; u < NBUF; ++u) {
