@@ -1258,8 +1258,8 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const int64_t bg = (int64_t)b * la.hkv + g;
   // Fused: the new key's storage row (full layout: p; ring: p % W) lies in
   // exactly one split.  That wave loads the token's key, value and rotation
-  // here, with the queries' loads (one round trip for both), and stores the
-  // rotated row once the queries are staged, before its tile loads.
+  // here, ahead of the queries' loads, and stores the rotated row before its
+  // tile loads.
   bool appender = false;
   float ax1 = 0.f, ax2 = 0.f, arc = 1.f, ars = 0.f;
   bf16 av1 = (bf16)0.f, av2 = (bf16)0.f;
@@ -1342,42 +1342,54 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   };
 
   // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
-  // The loads of the queries and their rotation go out first.  The plain
-  // kernel then issues its first tiles before it waits for them, so the
-  // queries' round trip and the first tiles' overlap; the single-kernel step
-  // issues its tiles after the appending wave has stored the new row.
+  // The loads of the queries and their rotation go out first, then the
+  // first tiles, before any of them is waited for, so the queries' round
+  // trip and the first tiles' overlap.  In the single-kernel step the wave
+  // whose split holds the new row stores it before its tile loads.
   constexpr int QE = REP * D / 64;                  // query elements per lane
   const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
-  // (no branch around the loads, so they go out back to back and their
-  // values are converted where they are used: without a table, the
-  // rotation's load reads the query row, 16-byte aligned, and is not used)
-  bf16 qx[QE], qo[QE];
-  float2 qcs[QE];
+  // Lane l holds elements l + 64 i, all at head-dim index d = l + 64 i mod D,
+  // so it needs one rotation entry (frequency l mod D/2); the partner of an
+  // element (d + D/2 mod D) is its own element i ^ 1 at D 128 and lane
+  // l ^ 32's element i at D 64.  No branch around the loads, so they go out
+  // back to back: without a table, the rotation's load reads the query row
+  // (16-byte aligned) and is not used.  bf16 values stay as loaded bits.
+  static_assert(D == 64 || D == 128, "query staging covers head_dim 64 and 128");
+  const uint16_t *qraw = reinterpret_cast<const uint16_t *>(qsrc);
+  uint16_t qx[QE];
   const bool rot = st.rope != nullptr;
 #pragma unroll
-  for (int i = 0; i < QE; ++i) {
-    const int e = lane + 64 * i, h = e / D, d = e % D;
-    const int di = d < D / 2 ? d : d - D / 2;
-    qx[i] = qsrc[e];
-    qo[i] = qsrc[h * D + (d < D / 2 ? d + D / 2 : d - D / 2)];
-    qcs[i] = *reinterpret_cast<const float2 *>(
-        rot ? st.rope + (p * (D / 2) + di) * 2 : reinterpret_cast<const float *>(qsrc));
+  for (int i = 0; i < QE; ++i) qx[i] = qraw[lane + 64 * i];
+  const float2 qcs = *reinterpret_cast<const float2 *>(
+      rot ? st.rope + (p * (D / 2) + lane % (D / 2)) * 2 : reinterpret_cast<const float *>(qsrc));
+  const float qc = qcs.x, qsn = qcs.y;
+  if constexpr (FUSED) {
+    if (appender) {
+      float y1 = ax1, y2 = ax2;
+      if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
+      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
+    }
   }
+  // The barrier keeps the compiler from moving the loads and stores above
+  // past the tile loads: every vector memory access of the wave is then
+  // older than the tiles, as the hand-placed tile waits require, and the
+  // appending wave's tiles come after its store (the memory pipeline keeps
+  // one wave's accesses to one address in order).
+  asm volatile("" ::: "memory");
   Tile T[NBUF];
-  if constexpr (!FUSED) {
-    // (the barrier keeps the compiler from issuing the loads above after the
-    // tile loads: every vector memory access of the wave is then older than
-    // the tiles, as the hand-placed tile waits require)
-    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
-  }
+  for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
+  // Nothing below moves above the tile loads: the compiler computes nothing
+  // from the query values, and so waits for none of them, before they are out.
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < QE; ++i) {
     const int e = lane + 64 * i, d = e % D;
-    const float x = (float)qx[i];
-    const float o = (float)qo[i], c = qcs[i].x, sn = qcs[i].y;
-    const float xr = d < D / 2 ? x * c - o * sn : o * sn + x * c;
+    const uint32_t xb = qx[i];
+    const uint32_t ob = D == 128 ? (uint32_t)qx[i ^ 1] : (uint32_t)__shfl_xor((int)xb, 32);
+    const float x = __builtin_bit_cast(float, xb << 16);
+    const float o = __builtin_bit_cast(float, ob << 16);
+    const float xr = d < D / 2 ? x * qc - o * qsn : o * qsn + x * qc;
     qs[e] = rot ? xr : x;
   }
   // One wave: its LDS accesses execute in order, so the reads below see the
@@ -1393,19 +1405,6 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
         const int d = (j + LK * t) * 8 + 2 * e2;
         qp[h][t][e2] = pack_bf16(qs[h * D + d], qs[h * D + d + 1]);
       }
-  if constexpr (FUSED) {
-    if (appender) {
-      float y1 = ax1, y2 = ax2;
-      if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
-      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
-    }
-    // The tile loads below come after these stores in program order (the
-    // barrier keeps the compiler from moving the stores past them), and the
-    // memory pipeline keeps one wave's accesses to one address in order.
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
-  }
 
   const float scale = kLog2e * rsqrtf((float)D);
   float m[HPL], lsum[HPL], acc[REP][VT];
