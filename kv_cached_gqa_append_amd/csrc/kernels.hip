@@ -859,17 +859,25 @@ struct DecodeShape {
   // REP * D < 1024 keep one tile in flight beside the one in use and run
   // three waves per SIMD (136 VGPRs at D 128, REP 4): more independent
   // streams per CU measured 3 % faster than two waves with two tiles in
-  // flight each (the same bytes in flight).  Larger shapes would spill at
-  // three waves and keep two, with two tiles in flight.  REP 16 at D 128
-  // holds 64 accumulators and 64 query registers per lane: it runs one wave
-  // per SIMD with the full register file rather than spill.
+  // flight each (the same bytes in flight).  REP 16 keeps one tile in flight
+  // at two waves (D 64) or, holding 64 accumulators and 64 query registers
+  // per lane at D 128, at one wave with the full register file rather than
+  // spill.
+  // REP * D = 1024 with REP <= 8 (D 128, REP 8) keeps four tiles in flight
+  // at one wave per SIMD, in both kernels: on 32k-key rows (B 8) the decode
+  // kernel measured 182 -> 174 us per layer against two waves with two
+  // tiles in flight, and the single-kernel step 210 -> 177 us (half the
+  // waves, so half the splits for the last split of a row to merge).  Five
+  // tiles at one wave did not help REP 4 (about 4k-key rows), and six or
+  // eight tiles at REP 4 were slower or did not fit.
   static constexpr bool BIG = REP * D >= 2048;
   static constexpr bool SMALL = REP * D < 1024;
-  static constexpr int NBUF = SMALL ? 2 : (REP <= 8 ? 3 : 2);
-  static constexpr int WAVES = SMALL ? 3 : (BIG ? 1 : 2);
+  static constexpr bool DEEP = REP * D == 1024 && REP <= 8;
+  static constexpr int NBUF = SMALL ? 2 : DEEP ? 5 : 2;
+  static constexpr int WAVES = SMALL ? 3 : DEEP ? 1 : (BIG ? 1 : 2);
   // the single-kernel step (it also holds the merge's registers: two waves)
-  static constexpr int FNBUF = REP <= 8 ? 3 : 2;
-  static constexpr int FWAVES = BIG ? 1 : 2;
+  static constexpr int FNBUF = DEEP ? 5 : REP <= 8 ? 3 : 2;
+  static constexpr int FWAVES = DEEP ? 1 : BIG ? 1 : 2;
   static_assert(NCH >= 1 && NR >= 1 && D % 32 == 0, "unsupported decode shape");
 };
 
