@@ -2034,20 +2034,25 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     const int t0i = (int)t0, vloi = (int)vlo, vhii = (int)vhi;
     const bool full = kind == 0 && t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
                       (W == 0 || pmax_i - t0i < W) && t0i >= first_i;
-    bf16x8_t pf[2];
+    // Both blocks' masks and maxima first, then one (rarely taken) branch
+    // for the accumulators' rescale, so that the exponentials and the P.V
+    // products of the two blocks share one basic block and the scheduler can
+    // run one block's exponentials beside the other's matrix products.
+    float sv[2][2][4];  // raw scores q.k (the scale enters with the exponent)
+    float tmax[2] = {-INFINITY, -INFINITY};
+    if (full) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float sv[2][4];  // raw scores q.k (the scale enters with the exponent)
-      float tmax = -INFINITY;
-      if (full) {
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            sv[kb][jj] = sacc[blk][kb][jj];
-            tmax = fmaxf(tmax, sv[kb][jj]);
+            sv[blk][kb][jj] = sacc[blk][kb][jj];
+            tmax[blk] = fmaxf(tmax[blk], sv[blk][kb][jj]);
           }
-      } else {
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
         const int qp = (int)qpos[blk];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -2065,47 +2070,77 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
                       (pos >= first_i || pos == qp);
             if (W > 0) ok = ok && (qp - pos < W);
             const float x = ok ? sacc[blk][kb][jj] : -INFINITY;
-            sv[kb][jj] = x;
-            tmax = fmaxf(tmax, x);
+            sv[blk][kb][jj] = x;
+            tmax[blk] = fmaxf(tmax[blk], x);
           }
       }
+    }
+    // Reference max, in the scaled log2 domain, moved only when the tile's
+    // max passes it by more than kLazyRescale: p = 2^(s*scale - m) then
+    // stays below 2^kLazyRescale, and the accumulators are rescaled on rare
+    // tiles instead of whenever some row's max grows.
+    float mu[2], alpha[2];
+    bool any_move = false;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
       // the row's max over the tile: its 4 lane groups hold 8 keys each
-      tmax = swap32_max(swap16_max(tmax));
-      // Reference max, in the scaled log2 domain, moved only when the tile's
-      // max passes it by more than kLazyRescale: p = 2^(s*scale - m) then
-      // stays below 2^kLazyRescale, and the accumulators are rescaled on
-      // rare tiles instead of whenever some row's max grows.
-      const float tm = tmax * scale;
+      const float tm = swap32_max(swap16_max(tmax[blk])) * scale;
       const bool move = tm > mrun[blk] + kLazyRescale;
       const float mn = move ? tm : mrun[blk];
-      const float alpha = move ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
-      const float mu = mn == -INFINITY ? 0.f : mn;
+      alpha[blk] = move ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
+      mu[blk] = mn == -INFINITY ? 0.f : mn;
+      mrun[blk] = mn;
+      any_move |= move;
+    }
+    if (__ballot(any_move) != 0) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha[blk];
+    }
+    // O^T += V^T P^T; k-slot 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4);
+    // each V operand (head-dim row db * 16 + nl) serves both blocks
+    bf16x8_t pf[2];
+    uint4 av[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      av[db] = *reinterpret_cast<const uint4 *>(&lv[s][(db * 16 + nl) * VSTR + q4 * 8]);
+    auto probs = [&](int blk) __attribute__((always_inline)) {
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(sv[kb][jj], scale, -mu));
+          const float pe = __builtin_amdgcn_exp2f(fmaf(sv[blk][kb][jj], scale, -mu[blk]));
           ps += pe;
           pf[blk][kb * 4 + jj] = (bf16)pe;
         }
-      lrun[blk] = lrun[blk] * alpha + ps;
-      mrun[blk] = mn;
-      if (__ballot(move) != 0) {
+      lrun[blk] = lrun[blk] * alpha[blk] + ps;
+    };
+    probs(0);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha;
-      }
+    for (int db = 0; db < NDB; ++db)
+      oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, av[db]), pf[0], oacc[0][db], 0, 0, 0);
+    probs(1);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+      oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+          __builtin_bit_cast(bf16x8_t, av[db]), pf[1], oacc[1][db], 0, 0, 0);
+    // Instruction order for the scheduler: the V operand reads, block 0's
+    // probabilities, then block 0's products each followed by a share of
+    // block 1's vector work (its exponentials run while the matrix core
+    // works), then block 1's products.  Measured on the 32k prefill of the
+    // long-context workload: 620 -> 671 TFLOP/s with the softmax
+    // restructured into one basic block, 648 of that without this order.
+    __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // DS read
+    __builtin_amdgcn_sched_group_barrier(0x002, 30, 0);      // VALU (block 0)
+#pragma unroll
+    for (int k = 0; k < NDB; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // VALU
     }
-    // O^T += V^T P^T; k-slot 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 16 + nl;
-      const uint4 av = *reinterpret_cast<const uint4 *>(&lv[s][d * VSTR + q4 * 8]);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-        oacc[blk][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, av), pf[blk], oacc[blk][db], 0, 0, 0);
-    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);     // MFMA
   };
 
   // LDS stores of a tile complete, then every wave meets: the tile is
