@@ -2298,6 +2298,66 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
     os = pa.pout + s0 * D;
   }
   // split weights 2^(m_s - M) / L (splits with no visible key have l == 0)
+  if (D == 64 || D == 128) {
+    // Every load of a merge of up to 8 splits goes out at once: this lane's
+    // (m, l) and its D/64 consecutive elements of the first 8 splits (one
+    // round trip instead of one per split and element); later splits load
+    // 8 at a time.  The sums are those of the loop below, in its order.
+    const int dpl = D / 64, d0 = lane * dpl;
+    const float lsr = lane < ns ? ml[2 * lane + 1] : 0.f;
+    const float msr = lane < ns ? ml[2 * lane] : 0.f;
+    float x0[8][2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        x0[u][e] = (u < ns && e < dpl) ? os[(int64_t)u * D + d0 + e] : 0.f;
+    const float ms = (lane < ns && lsr > 0.f) ? msr : -INFINITY;
+    const float M = wave_max(ms);
+    const float w = lsr > 0.f ? exp2f(ms - M) : 0.f;
+    const float Lt = wave_sum(w * lsr);
+    wts[lane] = w / Lt;
+    __syncthreads();
+    float a[2][8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[e][u] = 0.f;
+    int s = 0;
+    for (; s + 8 <= ns; s += 8) {
+      float x[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          x[u][e] = s == 0 ? x0[u][e] : (e < dpl ? os[(int64_t)(s + u) * D + d0 + e] : 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const float wu = wts[s + u];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) a[e][u] = combine_acc(a[e][u], wu, x[u][e]);
+      }
+    }
+    if (s < ns) {  // the last ns % 8 splits, summed in order into slot 0
+      float x[8][2];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          x[u][e] = s == 0 ? x0[u][e]
+                           : ((s + u < ns && e < dpl) ? os[(int64_t)(s + u) * D + d0 + e] : 0.f);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (s + u < ns) {
+          const float wu = wts[s + u];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) a[e][0] = combine_acc(a[e][0], wu, x[u][e]);
+        }
+      }
+    }
+    for (int e = 0; e < dpl; ++e) o[d0 + e] = from_f<T>(combine_tree(a[e]));
+    return;
+  }
   const float ls = lane < ns ? ml[2 * lane + 1] : 0.f;
   const float ms = (lane < ns && ls > 0.f) ? ml[2 * lane] : -INFINITY;
   const float M = wave_max(ms);
