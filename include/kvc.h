@@ -300,6 +300,12 @@ int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info);
  * extra packets enter the stream.
  *   kvc_timing_begin: allocate a pool for `max_launches` launches and start
  *                     recording (KVC_E_HIP if events cannot be created).
+ *   kvc_timing_begin_kinds: the same for the kinds whose bit (1 << kind) is
+ *                     set in `kind_mask` only; other launches carry no
+ *                     events (KVC_E_ARG for bits past the last kind).  A
+ *                     dispatch that stamps events leaves a longer gap before
+ *                     the next dependent dispatch, so timing fewer kinds
+ *                     disturbs a timed sequence less.
  *   kvc_timing_end:   wait for the recorded events, write the summed kernel
  *                     time in ms and the launch count per kind, stop.
  * Kinds: 0 append, 1 decode attention, 2 chunk attention, 3 split combine,
@@ -308,6 +314,7 @@ int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info);
 enum { KVC_K_APPEND = 0, KVC_K_DECODE = 1, KVC_K_PREFILL = 2, KVC_K_COMBINE = 3,
        KVC_K_COMMIT = 4, KVC_K_GENERIC = 5, KVC_K_FUSED = 6, KVC_K_NKINDS = 7 };
 int kvc_timing_begin(kvc_t *h, int32_t max_launches);
+int kvc_timing_begin_kinds(kvc_t *h, int32_t max_launches, int32_t kind_mask);
 int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind);
 
 /* Static text for a status code. */

@@ -140,6 +140,8 @@ def lib():
         L.kvc_buffer_info.restype = ctypes.c_int
         L.kvc_timing_begin.argtypes = [VP, I32]
         L.kvc_timing_begin.restype = ctypes.c_int
+        L.kvc_timing_begin_kinds.argtypes = [VP, I32, I32]
+        L.kvc_timing_begin_kinds.restype = ctypes.c_int
         L.kvc_timing_end.argtypes = [VP, P(ctypes.c_double), P(I32)]
         L.kvc_timing_end.restype = ctypes.c_int
         L.kvc_strerror.argtypes = [ctypes.c_int]
@@ -328,8 +330,15 @@ def kvc_buffer_info(h) -> KvcBufferInfo:
     return info
 
 
-def kvc_timing_begin(h, max_launches: int) -> None:
-    _check(lib().kvc_timing_begin(h, int(max_launches)), "kvc_timing_begin")
+def kvc_timing_begin(h, max_launches: int, kinds=None) -> None:
+    """Time every kernel kind, or only ``kinds`` (names from KERNEL_KINDS)."""
+    if kinds is None:
+        _check(lib().kvc_timing_begin(h, int(max_launches)), "kvc_timing_begin")
+        return
+    mask = 0
+    for k in kinds:
+        mask |= 1 << KERNEL_KINDS.index(k)
+    _check(lib().kvc_timing_begin_kinds(h, int(max_launches), mask), "kvc_timing_begin_kinds")
 
 
 def kvc_timing_end(h):

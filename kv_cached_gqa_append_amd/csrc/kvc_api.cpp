@@ -63,6 +63,7 @@ struct kvc_cache {
   std::vector<hipEvent_t> ev;      // 2 per launch
   std::vector<int> ev_kind;
   int32_t ev_used = 0;
+  int32_t ev_mask = 0;             // kinds (bit per KVC_K_*) whose launches are timed
 };
 
 namespace {
@@ -226,7 +227,8 @@ int release_pages(kvc_t *h, const int32_t *rows, int32_t n, void *stream) {
 kvc::Launch launch_on(kvc_t *h, int kind, void *stream) {
   kvc::Launch lc;
   lc.stream = stream;
-  if (!h->timing || 2 * (h->ev_used + 1) > (int32_t)h->ev.size()) return lc;
+  if (!h->timing || !((h->ev_mask >> kind) & 1) || 2 * (h->ev_used + 1) > (int32_t)h->ev.size())
+    return lc;
   const int i = h->ev_used++;
   h->ev_kind[i] = kind;
   lc.t0 = h->ev[2 * i];
@@ -1042,7 +1044,11 @@ int kvc_buffer_info(const kvc_t *h, kvc_buffer_info_t *info) {
 }
 
 int kvc_timing_begin(kvc_t *h, int32_t max_launches) {
-  if (!h || max_launches < 1) return KVC_E_ARG;
+  return kvc_timing_begin_kinds(h, max_launches, (1 << KVC_K_NKINDS) - 1);
+}
+
+int kvc_timing_begin_kinds(kvc_t *h, int32_t max_launches, int32_t kind_mask) {
+  if (!h || max_launches < 1 || (kind_mask & ~((1 << KVC_K_NKINDS) - 1)) != 0) return KVC_E_ARG;
   if ((int32_t)h->ev.size() < 2 * max_launches) {
     while ((int32_t)h->ev.size() < 2 * max_launches) {
       hipEvent_t e;
@@ -1052,6 +1058,7 @@ int kvc_timing_begin(kvc_t *h, int32_t max_launches) {
   }
   h->ev_kind.assign(max_launches, 0);
   h->ev_used = 0;
+  h->ev_mask = kind_mask;
   h->timing = true;
   return KVC_OK;
 }
