@@ -195,13 +195,17 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
  * arguments (q and out as for kvc_attend), same checks, same results, same
  * step protocol (the layer counts as appended and attended).  A one-token
  * step (C == 1) in bf16 with a decode-kernel head shape (D in {64, 128},
- * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs as a single kernel: the rotation and
- * store of each row's new key and value, decode attention over its key
- * splits, and the merge of the splits (the last split of a row and KV head to
- * finish merges them; tiny_agent "generate.py" _append_chunk writes a token
- * and attends over it in one pass).  Other steps enqueue the two calls' work.
- * While one such single-kernel launch runs, no other launch of the same
- * handle may run concurrently (they share split counters in the buffer).
+ * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs the rotation and store of each row's
+ * new key and value and the decode attention over its key splits as one
+ * kernel (tiny_agent "generate.py" _append_chunk writes a token and attends
+ * over it in one pass), then the merge of the splits as a second.  With the
+ * environment variable KVC_FUSED_MERGE=1 at kvc_create, the first kernel
+ * merges too (the last split of a row and KV head to finish merges them):
+ * one launch per layer, for callers whose launch rate bounds them; it reads
+ * the partials back at the end of the launch, so a GPU-bound step is faster
+ * without it.  Other steps enqueue the two calls' work.  While a merging
+ * launch runs, no other launch of the same handle may run concurrently (they
+ * share split counters in the buffer).
  * Errors as for kvc_append; KVC_E_HIP if a launch fails after the append's
  * work was enqueued. */
 int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k,

@@ -866,7 +866,7 @@ struct DecodeShape {
   // REP * D = 1024 with REP <= 8 (D 128, REP 8) keeps four tiles in flight
   // at one wave per SIMD, in both kernels: on 32k-key rows (B 8) the decode
   // kernel measured 182 -> 174 us per layer against two waves with two
-  // tiles in flight, and the single-kernel step 210 -> 177 us (half the
+  // tiles in flight, and the in-launch merge form 210 -> 177 us (half the
   // waves, so half the splits for the last split of a row to merge).  Five
   // tiles at one wave did not help REP 4 (about 4k-key rows), and six or
   // eight tiles at REP 4 were slower or did not fit.
@@ -875,7 +875,7 @@ struct DecodeShape {
   static constexpr bool DEEP = REP * D == 1024 && REP <= 8;
   static constexpr int NBUF = SMALL ? 2 : DEEP ? 5 : 2;
   static constexpr int WAVES = SMALL ? 3 : DEEP ? 1 : (BIG ? 1 : 2);
-  // the single-kernel step (it also holds the merge's registers: two waves)
+  // the in-launch merge form (it also holds the merge's registers: two waves)
   static constexpr int FNBUF = DEEP ? 5 : REP <= 8 ? 3 : 2;
   static constexpr int FWAVES = DEEP ? 1 : BIG ? 1 : 2;
   static_assert(NCH >= 1 && NR >= 1 && D % 32 == 0, "unsupported decode shape");
@@ -1194,16 +1194,19 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
   }
 }
 
-// FUSED: the single-token step of a layer in one launch (C == 1): the wave
-// whose split holds the new key's row first appends it (RoPE, K row, V
-// column, slot report); rows with n_new == 0 get one item that writes their
-// padded token to the scratch row and zero outputs; and the last split of a
-// (row, KV head) to finish combines the splits into the output.
+// FUSED: the single-token step of a layer (C == 1) appends in the same
+// launch: the wave whose split holds the new key's row first appends it
+// (RoPE, K row, V column, slot report); rows with n_new == 0 get one item
+// that writes their padded token to the scratch row.  MERGE: the last split
+// of a (row, KV head) to finish also combines the splits into the output
+// (and idle rows' items write zero outputs); else the partials are left for
+// k_combine, as the plain kernel leaves them.
 // PAGED: a paged full layer; each 16-row tile is one page, found in the
 // block table when the tile's loads are issued.
 template <int D, int REP, bool FUSED = false, bool PAGED = false,
           int NBUF = FUSED ? DecodeShape<D, REP>::FNBUF : DecodeShape<D, REP>::NBUF,
-          int WAVES = FUSED ? DecodeShape<D, REP>::FWAVES : DecodeShape<D, REP>::WAVES>
+          int WAVES = FUSED ? DecodeShape<D, REP>::FWAVES : DecodeShape<D, REP>::WAVES,
+          bool MERGE = FUSED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
               FusedArgs fa, const int32_t *__restrict__ ptab) {
@@ -1235,10 +1238,12 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   if (b < 0) return;
   b = __builtin_amdgcn_readfirstlane(row_at(b));
   if constexpr (FUSED) {
-    if (st.n_new[b] == 0) {  // idle row: its padded token and zero outputs
+    if (st.n_new[b] == 0) {  // idle row: its padded token (and zero outputs)
       store_idle_token<D>(la, fa, b, g, st.lens[b], lane);
-      bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
-      for (int e = lane; e < REP * D; e += 64) o[e] = (bf16)0.f;
+      if constexpr (MERGE) {  // (else the merge kernel writes them)
+        bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
+        for (int e = lane; e < REP * D; e += 64) o[e] = (bf16)0.f;
+      }
       return;
     }
   }
@@ -1352,7 +1357,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
   // The loads of the queries and their rotation go out first, then the
   // first tiles, before any of them is waited for, so the queries' round
-  // trip and the first tiles' overlap.  In the single-kernel step the wave
+  // trip and the first tiles' overlap.  In the appending kernel the wave
   // whose split holds the new row stores it before its tile loads.
   constexpr int QE = REP * D / 64;                  // query elements per lane
   const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
@@ -1558,7 +1563,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   float lh[HPL];
 #pragma unroll
   for (int u = 0; u < HPL; ++u) lh[u] = keys_sum<LK>(lsum[u]);
-  if constexpr (FUSED) {
+  if constexpr (MERGE) {
     if (nsplit == 1) {
       // One split: the output is o / l, rounded as the merge rounds a
       // single split (weight 1 / l times o, then the sum with zeros).
@@ -1583,7 +1588,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   // agent-scope stores (written through to the device's point of coherence,
   // which every XCD reads).
   auto put = [&](float *ptr, float val) {
-    if constexpr (FUSED)
+    if constexpr (MERGE)
       __hip_atomic_store(ptr, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
       *ptr = val;
@@ -1607,7 +1612,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
       if (half == 0) put(pa.dout + slot * D + mm + 32 * t, o);
     }
   }
-  if constexpr (FUSED) {
+  if constexpr (MERGE) {
     // Count this split's arrival once its partials are complete: the wait
     // retires every store of the wave (acknowledged at the point of
     // coherence) before lane 0's agent-scope increment.  The split that reads
@@ -1649,15 +1654,26 @@ static void launch_decode_t(const StepArgs &st, const LayerArgs &la, const Parti
 template <int D, int REP>
 static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                                   const void *q, const FusedArgs &fa, int32_t n_items,
-                                  const Launch &lc) {
+                                  bool merge, const Launch &lc) {
+  using S = DecodeShape<D, REP>;
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)n_items)
                                      : dim3((unsigned)n_items, (unsigned)la.hkv);
-  if (la.paged)
-    launch_kernel((k_decode<D, REP, true, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q,
-                  fa, la.table);
-  else
-    launch_kernel((k_decode<D, REP, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, fa,
-                  la.table);
+  // without the merge: the plain kernel's register ring and occupancy
+  if (merge) {
+    if (la.paged)
+      launch_kernel((k_decode<D, REP, true, true>), grid, dim3(64), lc, st, la, pa,
+                    (const bf16 *)q, fa, la.table);
+    else
+      launch_kernel((k_decode<D, REP, true>), grid, dim3(64), lc, st, la, pa, (const bf16 *)q, fa,
+                    la.table);
+  } else {
+    if (la.paged)
+      launch_kernel((k_decode<D, REP, true, true, S::NBUF, S::WAVES, false>), grid, dim3(64), lc,
+                    st, la, pa, (const bf16 *)q, fa, la.table);
+    else
+      launch_kernel((k_decode<D, REP, true, false, S::NBUF, S::WAVES, false>), grid, dim3(64), lc,
+                    st, la, pa, (const bf16 *)q, fa, la.table);
+  }
 }
 
 template <int D, int REP>
@@ -1678,11 +1694,12 @@ int decode_waves_per_cu(int D, int rep) {
 }
 
 int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                        const void *q, const FusedArgs &fa, int32_t n_items, const Launch &lc) {
+                        const void *q, const FusedArgs &fa, int32_t n_items, bool merge,
+                        const Launch &lc) {
   if (st.C != 1) return (int)hipErrorInvalidValue;
 #define KVC_DEC(DD, RR)                                                  \
   if (st.D == DD && la.rep == RR) {                                      \
-    launch_decode_fused_t<DD, RR>(st, la, pa, q, fa, n_items, lc);       \
+    launch_decode_fused_t<DD, RR>(st, la, pa, q, fa, n_items, merge, lc); \
     return (int)hipGetLastError();                                       \
   }
   KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8) KVC_DEC(128, 16)

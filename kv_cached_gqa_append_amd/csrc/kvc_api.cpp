@@ -52,6 +52,7 @@ struct kvc_cache {
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
+  bool fused_merge = false;       // KVC_FUSED_MERGE=1: the single kernel merges its splits
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -477,6 +478,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     if (v >= 1 && v <= 4096) h->dec_min_tiles = (int32_t)v;
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_FUSED_MERGE")) h->fused_merge = std::atoi(e) != 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -881,8 +883,11 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   fa.slot_out = slot_out_dev;
   fa.out = out;
   fa.cnt = reinterpret_cast<int32_t *>(h->base + h->lay.cnt_off);
-  if (kvc::launch_decode_fused(st, la, pa, q, fa, (int32_t)items,
+  if (kvc::launch_decode_fused(st, la, pa, q, fa, (int32_t)items, h->fused_merge,
                                launch_on(h, KVC_K_FUSED, stream)))
+    return KVC_E_HIP;
+  if (!h->fused_merge &&
+      kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream)))
     return KVC_E_HIP;
   h->appended[layer] = 1;
   h->attended[layer] = 1;

@@ -208,11 +208,13 @@ int launch_append(int dtype, const StepArgs &st, const LayerArgs &la, const void
 int launch_commit(int dtype, const StepArgs &st, const LayerArgs &la, const Launch &lc);
 int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                   const void *q, int32_t n_items, const Launch &lc);
-// Rows with n_new in {0, 1}, C == 1: RoPE + append, decode attention and the
-// split combine in one launch; n_items counts decode splits plus one item per
+// Rows with n_new in {0, 1}, C == 1: RoPE + append and decode attention in
+// one launch, and with `merge` the split combine too (else the partials are
+// left for launch_combine); n_items counts decode splits plus one item per
 // idle row.
 int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
-                        const void *q, const FusedArgs &fa, int32_t n_items, const Launch &lc);
+                        const void *q, const FusedArgs &fa, int32_t n_items, bool merge,
+                        const Launch &lc);
 // qw: waves per workgroup (8: 256 query rows per item; 4: 128).  With
 // pa.chunk_small, the 4-wave launch takes the rows of at most 128 query rows
 // and the 8-wave launch the rest.

@@ -193,8 +193,12 @@ def _fused_vs_two_calls(work, prompts, decode_steps, tag):
     say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
 
 
-def test_fused_decode_rings_and_idle_rows():
-    say("case: fused one-token steps, ring_bf16 (rings W=8 + global), idle rows")
+# merge "1": the single kernel merges its splits (KVC_FUSED_MERGE=1); "0"
+# (default): it appends and attends, and the merge kernel combines the splits
+@pytest.mark.parametrize("merge", ["0", "1"])
+def test_fused_decode_rings_and_idle_rows(merge, monkeypatch):
+    monkeypatch.setenv("KVC_FUSED_MERGE", merge)
+    say(f"case: fused one-token steps, ring_bf16 (rings W=8 + global), idle rows, merge={merge}")
     work = wl.RING_BF16
     prompts = [(np.array([12, 3, 9, 0]), 12)]
     steps = [np.array([1, 1, 1, 1]), np.array([1, 0, 1, 1]), np.array([0, 1, 1, 0])]
@@ -202,8 +206,11 @@ def test_fused_decode_rings_and_idle_rows():
     _fused_vs_two_calls(work, prompts, steps, "fused_ring")
 
 
-def test_fused_decode_many_splits():
-    say("case: fused one-token steps with many key splits, D128 rep4, W=700 window mask")
+@pytest.mark.parametrize("merge", ["0", "1"])
+def test_fused_decode_many_splits(merge, monkeypatch):
+    monkeypatch.setenv("KVC_FUSED_MERGE", merge)
+    say(f"case: fused one-token steps with many key splits, D128 rep4, W=700 window mask, "
+        f"merge={merge}")
     work = wl.Workload("fused_splits", 2, 6, 32, (8, 8), 128, 3200, (0, 700), "bf16", 64,
                        use_ring=False)
     a = Pair(work, poison=True, tag="fs")
@@ -222,9 +229,11 @@ def test_fused_decode_many_splits():
     say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
 
 
+@pytest.mark.parametrize("merge", ["0", "1"])
 @pytest.mark.parametrize("D,rep", [(64, 1), (64, 16), (128, 2), (128, 8), (128, 16)])
-def test_fused_head_shapes(D, rep):
-    say(f"case: fused head shapes D={D} rep={rep}")
+def test_fused_head_shapes(D, rep, merge, monkeypatch):
+    monkeypatch.setenv("KVC_FUSED_MERGE", merge)
+    say(f"case: fused head shapes D={D} rep={rep} merge={merge}")
     hkv = 2
     work = wl.Workload(f"fshape_{D}_{rep}", 1, 3, hkv * rep, (hkv,), D, 400, (0,), "bf16", 40)
     _fused_vs_two_calls(work, wl.fill_plan([300, 40, 5], 40),
