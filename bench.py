@@ -72,13 +72,12 @@ def decode_kernel_bytes(lens, n_new, work):
 
 
 def fused_kernel_bytes(lens, n_new, work):
-    """Algorithmic bytes of one single-kernel launch (one layer): the decode
-    bytes, every row's new (or padded) k and v read and written to its slot,
-    and every row's output written (zeros for idle rows)."""
+    """Algorithmic bytes of one appending decode launch of kvc_append_attend
+    (one layer): the decode bytes and every row's new (or padded) k and v
+    read and written to its slot (the merge kernel writes the outputs)."""
     s = work.dtype_bytes
-    hkv, D, hq, B = work.n_kv_head[0], work.head_dim, work.n_q_head, work.batch
-    return (decode_kernel_bytes(lens, n_new, work) + B * hkv * D * s * 2 * 2
-            + B * hq * D * s)
+    hkv, D, B = work.n_kv_head[0], work.head_dim, work.batch
+    return decode_kernel_bytes(lens, n_new, work) + B * hkv * D * s * 2 * 2
 
 
 def step_bytes(lens, n_new, work):
@@ -448,7 +447,8 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
     through both entry points in turn (kvc_append + kvc_attend, then
     kvc_append_attend), then as replays of a captured static step.  Attention GB/s = algorithmic bytes (global layers
     read every key, ring layers min(p + 1, W) keys; queries read, outputs
-    written; for the single kernel also the new k, v rows read and written)
+    written; through kvc_append_attend also the new k, v rows read and
+    written)
     over the summed attention kernel time; a few more steps, timed a layer at
     a time, split that into global and ring layers."""
     work = wl.LONG_5TO1
@@ -476,7 +476,7 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
     glob = [l for l in range(L) if work.window[l] == 0]
 
     def one_entry(fused):
-        att_kinds = ("fused",) if fused else ("decode", "combine")
+        att_kinds = ("fused", "combine") if fused else ("decode", "combine")
 
         def layer_bytes(l, lens):
             vis = lens + 1 if work.window[l] == 0 else np.minimum(lens + 1, work.window[l])
