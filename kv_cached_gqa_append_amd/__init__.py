@@ -19,6 +19,7 @@ The library must be built first (``__graft_entry__.build()`` or
 import ctypes
 import os
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -108,25 +109,25 @@ def lib():
         L.kvc_create.restype = ctypes.c_int
         L.kvc_destroy.argtypes = [VP]
         L.kvc_destroy.restype = None
-        L.kvc_reset.argtypes = [VP, P(I32), I32, VP]
+        L.kvc_reset.argtypes = [VP, VP, I32, VP]
         L.kvc_reset.restype = ctypes.c_int
-        L.kvc_append.argtypes = [VP, I32, VP, VP, P(I32), I32, VP, VP]
+        L.kvc_append.argtypes = [VP, I32, VP, VP, VP, I32, VP, VP]
         L.kvc_append.restype = ctypes.c_int
         L.kvc_attend.argtypes = [VP, I32, VP, VP, VP]
         L.kvc_attend.restype = ctypes.c_int
-        L.kvc_append_attend.argtypes = [VP, I32, VP, VP, VP, P(I32), I32, VP, VP, VP]
+        L.kvc_append_attend.argtypes = [VP, I32, VP, VP, VP, VP, I32, VP, VP, VP]
         L.kvc_append_attend.restype = ctypes.c_int
         L.kvc_advance.argtypes = [VP, VP]
         L.kvc_advance.restype = ctypes.c_int
         L.kvc_lens.argtypes = [VP, P(I32)]
         L.kvc_lens.restype = ctypes.c_int
-        L.kvc_set_first.argtypes = [VP, P(I32), P(I32), I32, VP]
+        L.kvc_set_first.argtypes = [VP, VP, VP, I32, VP]
         L.kvc_set_first.restype = ctypes.c_int
-        L.kvc_admit.argtypes = [VP, P(I32), VP, P(I32), I32, VP]
+        L.kvc_admit.argtypes = [VP, VP, VP, VP, I32, VP]
         L.kvc_admit.restype = ctypes.c_int
         L.kvc_page_stats.argtypes = [VP, P(ctypes.c_int64), P(ctypes.c_int64), P(ctypes.c_int64)]
         L.kvc_page_stats.restype = ctypes.c_int
-        L.kvc_reserve.argtypes = [VP, P(I32), P(I32), I32, VP]
+        L.kvc_reserve.argtypes = [VP, VP, VP, I32, VP]
         L.kvc_reserve.restype = ctypes.c_int
         L.kvc_static_begin.argtypes = [VP, VP, VP]
         L.kvc_static_begin.restype = ctypes.c_int
@@ -224,21 +225,39 @@ def kvc_destroy(h) -> None:
     lib().kvc_destroy(h)
 
 
+class _Rows:
+    """Host int32 array for the C ABI; ``ptr`` is valid while this lives."""
+
+    __slots__ = ("arr", "ptr", "n")
+
+    def __init__(self, values):
+        arr = np.ascontiguousarray(values, dtype=np.int32)
+        if arr.ndim != 1:
+            raise ValueError("row values must be one-dimensional")
+        self.n = int(arr.size)
+        # (an empty list still passes a valid pointer, with count 0)
+        self.arr = arr if arr.size else np.zeros(1, dtype=np.int32)
+        self.ptr = ctypes.c_void_p(self.arr.ctypes.data)
+
+
 def _rows_array(values):
-    if values is None:  # a static step: the counts are on the device
-        return None, 0
-    vals = [int(x) for x in values]
-    return (ctypes.c_int32 * max(1, len(vals)))(*vals), len(vals)
+    """(pointer, count) of int32 row values (None: a static step's counts
+    are on the device, passed as NULL).  The pointer's owner rides along as
+    a third element so that it outlives the call."""
+    if values is None:
+        return None, 0, None
+    r = _Rows(values)
+    return r.ptr, r.n, r
 
 
 def kvc_reset(h, rows, stream=None) -> None:
-    arr, n = _rows_array(rows)
+    arr, n, _keep = _rows_array(rows)
     _check(lib().kvc_reset(h, arr, n, _stream_handle(stream)), "kvc_reset")
 
 
 def kvc_append(h, layer: int, k: torch.Tensor, v: torch.Tensor, n_new, C: int,
                slot_out=None, stream=None) -> None:
-    arr, _ = _rows_array(n_new)
+    arr, _, _keep = _rows_array(n_new)
     so = ctypes.c_void_p(slot_out.data_ptr()) if slot_out is not None else ctypes.c_void_p()
     _check(lib().kvc_append(h, int(layer), ctypes.c_void_p(k.data_ptr()),
                             ctypes.c_void_p(v.data_ptr()), arr, int(C), so,
@@ -253,7 +272,7 @@ def kvc_attend(h, layer: int, q: torch.Tensor, out: torch.Tensor, stream=None) -
 
 def kvc_append_attend(h, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_new,
                       C: int, out: torch.Tensor, slot_out=None, stream=None) -> None:
-    arr, _ = _rows_array(n_new)
+    arr, _, _keep = _rows_array(n_new)
     so = ctypes.c_void_p(slot_out.data_ptr()) if slot_out is not None else ctypes.c_void_p()
     _check(lib().kvc_append_attend(h, int(layer), ctypes.c_void_p(q.data_ptr()),
                                    ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
@@ -266,16 +285,16 @@ def kvc_advance(h, stream=None) -> None:
 
 
 def kvc_set_first(h, rows, first, stream=None) -> None:
-    r, n = _rows_array(rows)
-    f, m = _rows_array(first)
+    r, n, _kr = _rows_array(rows)
+    f, m, _kf = _rows_array(first)
     if n != m:
         raise ValueError("one first per row")
     _check(lib().kvc_set_first(h, r, f, n, _stream_handle(stream)), "kvc_set_first")
 
 
 def kvc_admit(dst, dst_rows, src, src_rows, stream=None) -> None:
-    d, n = _rows_array(dst_rows)
-    r, m = _rows_array(src_rows)
+    d, n, _kd = _rows_array(dst_rows)
+    r, m, _kr = _rows_array(src_rows)
     if n != m:
         raise ValueError("one source row per row")
     _check(lib().kvc_admit(dst, d, src, r, n, _stream_handle(stream)), "kvc_admit")
@@ -289,8 +308,8 @@ def kvc_page_stats(h):
 
 
 def kvc_reserve(h, rows, tokens, stream=None) -> None:
-    r, n = _rows_array(rows)
-    t, m = _rows_array(tokens)
+    r, n, _kr = _rows_array(rows)
+    t, m, _kt = _rows_array(tokens)
     if n != m:
         raise ValueError("one token count per row")
     _check(lib().kvc_reserve(h, r, t, n, _stream_handle(stream)), "kvc_reserve")
