@@ -281,7 +281,9 @@ int kvc_sync_lens(kvc_t *h, void *stream);
  * V is stored transposed in blocks of 16 rows: element (b, g, r, d) sits at
  * v_offset + ((((b*Hkv + g)*rows_alloc/16 + r/16)*D + d)*16 + r%16)*s.
  * rows excludes the scratch row (index `rows`); rows_alloc = rows + 1 rounded
- * up to 32.  Staging (ring layers, max_chunk >= 2) uses the same two layouts
+ * up to 32, plus 16 on a contiguous (not paged) layer where that many rows
+ * would take a multiple of 8 KB (rows_alloc*D*s), so that no two (row, KV
+ * head) regions start a multiple of 8 KB apart.  Staging (ring layers, max_chunk >= 2) uses the same two layouts
  * with stage_rows_alloc rows; stage offsets are -1 when there is none. */
 typedef struct {
   int64_t k_offset, v_offset, stage_k_offset, stage_v_offset;
