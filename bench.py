@@ -10,8 +10,9 @@ synthetic N(0, 1) tensors already resident in HBM.
 One step = for each of the 32 layers kvc_append + kvc_attend (append, decode
 attention and split-combine kernels), then one kvc_advance; the decode
 attention kernel is the roofline kernel.  A second timed leg then runs the
-same steps through kvc_append_attend (one kernel per layer: RoPE + append,
-decode attention, split merge) and reports it next to the headline
+same steps through kvc_append_attend (per layer an appending decode kernel,
+RoPE + append + decode attention, and the split merge) and reports it next
+to the headline
 (``--fused`` makes it the headline, ``--no-other-leg`` skips it), and a
 third replays a captured static step (kvc_static_begin, kvc_append_attend
 per layer, kvc_advance) from a HIP graph, reported as ``graph``.  Warmup
@@ -735,7 +736,7 @@ def main():
     ap.add_argument("--only", choices=("mixed", "long_decode", "paged"),
                     help="run only that leg and print its object")
     ap.add_argument("--fused", action="store_true",
-                    help="headline leg through kvc_append_attend (one kernel per layer) instead "
+                    help="headline leg through kvc_append_attend (appending decode + merge) instead "
                          "of kvc_append + kvc_attend")
     ap.add_argument("--no-other-leg", action="store_true",
                     help="skip the second timed leg through the other entry point")

@@ -52,7 +52,7 @@ struct kvc_cache {
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
-  bool fused_merge = false;       // KVC_FUSED_MERGE=1: the single kernel merges its splits
+  bool fused_merge = false;       // KVC_FUSED_MERGE=1: the appending decode merges its splits
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -244,7 +244,7 @@ void decode_span(const kvc::LayerArgs &la, int64_t p, int64_t first, int64_t *ba
 // wave count, summed over the decoding rows and KV heads, fits the waves the
 // chip holds at once.  A partial second round or a few long waves would leave
 // most of the chip idle at the end of the launch.  Each row keeps at most
-// kDecodeSplitCap splits.  The idle rows' items of the single-kernel step
+// kDecodeSplitCap splits.  The idle rows' items of kvc_append_attend's kernel
 // take slots too; both entry points plan with them counted, so a step splits
 // its rows the same way (and produces the same bits) through either.
 int32_t decode_split_keys(kvc_t *h, const kvc::LayerArgs &la, int D,

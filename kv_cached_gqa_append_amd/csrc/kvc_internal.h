@@ -151,9 +151,10 @@ struct StaticBeginArgs {
   StaticClass cls[kStaticClassMax];
 };
 
-// The single-token step of one layer in one launch (append, decode, combine):
-// the new token's K (pre-RoPE) and V, the slot report, the output and the
-// per-(row, KV head) split arrival counters (zero between launches).
+// The single-token step of one layer whose decode launch also appends (and,
+// with the in-launch merge, combines): the new token's K (pre-RoPE) and V,
+// the slot report, the output and the per-(row, KV head) split arrival
+// counters of the in-launch merge (zero between launches).
 struct FusedArgs {
   const void *k = nullptr, *v = nullptr;  // (B, 1, Hkv, D)
   int32_t *slot_out = nullptr;            // (B, 1) or null

@@ -6,8 +6,8 @@ configuration the bench times, and checks chosen queries of a few rows
 against the oracle (the oracle finishes them in seconds; all rows at these
 sizes it would not).  Properties that hold at any size are checked on every
 row: slot indices and lengths bit-exact, padded and idle outputs exactly
-zero, outputs finite, and (for one-token steps) the single-kernel entry point
-equal bit for bit to append + attend.  Histories are drawn on the GPU from
+zero, outputs finite, and (for one-token steps) kvc_append_attend equal bit
+for bit to append + attend.  Histories are drawn on the GPU from
 seeded generators (``workloads.device_step_qkv``); the sampled rows' tokens
 are copied back for the oracle.
 """
@@ -208,7 +208,7 @@ def test_decode_b64_paged_full_size():
         flat.advance()
         paged.advance()
         torch.cuda.synchronize()
-        for l in range(2):  # (odd steps: the paged cache through the single-kernel step)
+        for l in range(2):  # (odd steps: the paged cache through kvc_append_attend)
             assert torch.equal(of[l], op[l]), f"step {s} layer {l}: paged output differs"
         mx, rel = so.check_step(n, qkv, op, lambda b, nb: [0], f"paged decode_b64 step {s}")
         say(f"  step {s}: rows {rows} worst abs {mx:.2e} rel {rel:.2e}")

@@ -159,7 +159,7 @@ def test_guards_and_step_order():
     torch.cuda.synchronize()
 
 
-# -- the single-kernel one-token step (kvc_append_attend) ------------------------
+# -- the one-token step through kvc_append_attend ---------------------------------
 def _same_cache(a, b, layer):
     # Raw bits of the cache rows proper (rows never written hold the NaN
     # poison in both).  The scratch row is left out: the padded tokens of a
@@ -193,7 +193,7 @@ def _fused_vs_two_calls(work, prompts, decode_steps, tag):
     say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
 
 
-# merge "1": the single kernel merges its splits (KVC_FUSED_MERGE=1); "0"
+# merge "1": the appending decode merges its splits (KVC_FUSED_MERGE=1); "0"
 # (default): it appends and attends, and the merge kernel combines the splits
 @pytest.mark.parametrize("merge", ["0", "1"])
 def test_fused_decode_rings_and_idle_rows(merge, monkeypatch):
