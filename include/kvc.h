@@ -125,7 +125,18 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  * (>= kvc_nbytes(cfg, KVC_NB_ALLOC)) on the current HIP device.  Copies cfg
  * (the arrays too).  Enqueues the RoPE table upload and the zeroing of the
  * row lengths on `stream` and waits for them (create is not part of a step).
- * All rows start empty.  On error *out is NULL and nothing was enqueued. */
+ * All rows start empty.  On error *out is NULL and nothing was enqueued.
+ *
+ * Tuning read from the environment at create (none changes results beyond
+ * the split order's rounding; out-of-range values are ignored):
+ *   KVC_DECODE_WAVES=n      decode split plan for n waves per launch instead
+ *                           of the waves the chip holds at once;
+ *   KVC_DECODE_SPLIT=k      a fixed decode split of k keys (a multiple of 16);
+ *   KVC_DECODE_MIN_TILES=t  shortest decode split, in 16-key tiles (default 4);
+ *   KVC_DECODE_FUSED=0      kvc_append_attend enqueues kvc_append + kvc_attend;
+ *   KVC_FUSED_MERGE=1       kvc_append_attend merges in its decode launch;
+ *   KVC_CHUNK_SMALL=0       every chunk row in 8-wave workgroups;
+ *   KVC_LOG=1 or 2          sizes at create (2: also decode plans) on stderr. */
 int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes,
                void *stream, kvc_t **out);
 
@@ -198,8 +209,8 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
  * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs the rotation and store of each row's
  * new key and value and the decode attention over its key splits as one
  * kernel (tiny_agent "generate.py" _append_chunk writes a token and attends
- * over it in one pass), then the merge of the splits as a second.  With the
- * environment variable KVC_FUSED_MERGE=1 at kvc_create, the first kernel
+ * over it in one pass), then the merge of the splits as a second.  With
+ * KVC_FUSED_MERGE=1 (see kvc_create), the first kernel
  * merges too (the last split of a row and KV head to finish merges them):
  * one launch per layer, for callers whose launch rate bounds them; it reads
  * the partials back at the end of the launch, so a GPU-bound step is faster

@@ -463,7 +463,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     delete h;
     return KVC_E_HIP;
   }
-  // Experiment overrides of the decode split plan.
+  // Tuning overrides (documented at kvc_create in kvc.h).
   if (const char *e = std::getenv("KVC_DECODE_SPLIT")) {
     const long v = std::strtol(e, nullptr, 10);
     if (v >= kvc::kDecodeTile && v <= (1 << 20) && v % kvc::kDecodeTile == 0)
