@@ -136,6 +136,9 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_DECODE_FUSED=0      kvc_append_attend enqueues kvc_append + kvc_attend;
  *   KVC_FUSED_MERGE=1       kvc_append_attend merges in its decode launch;
  *   KVC_CHUNK_SMALL=0       every chunk row in 8-wave workgroups;
+ *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
+ *                           1024 rows) take the split plan and the merge
+ *                           kernel instead of one workgroup per row;
  *   KVC_LOG=1 or 2          sizes at create (2: also decode plans) on stderr. */
 int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes,
                void *stream, kvc_t **out);
@@ -209,7 +212,8 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
  * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs the rotation and store of each row's
  * new key and value and the decode attention over its key splits as one
  * kernel (tiny_agent "generate.py" _append_chunk writes a token and attends
- * over it in one pass), then the merge of the splits as a second.  With
+ * over it in one pass), then the merge of the splits as a second (a ring
+ * layer of at most 1024 rows: one launch whose workgroups merge).  With
  * KVC_FUSED_MERGE=1 (see kvc_create), the first kernel
  * merges too (the last split of a row and KV head to finish merges them):
  * one launch per layer, for callers whose launch rate bounds them; it reads

@@ -1206,17 +1206,24 @@ __device__ __forceinline__ void combine_group(const PartialArgs &pa, const StepA
 template <int D, int REP, bool FUSED = false, bool PAGED = false,
           int NBUF = FUSED ? DecodeShape<D, REP>::FNBUF : DecodeShape<D, REP>::NBUF,
           int WAVES = FUSED ? DecodeShape<D, REP>::FWAVES : DecodeShape<D, REP>::WAVES,
-          bool MERGE = FUSED>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(WAVES)))
+          bool MERGE = FUSED, int NW = 1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(WAVES)))
 void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
               FusedArgs fa, const int32_t *__restrict__ ptab) {
   using S = DecodeShape<D, REP>;
   constexpr int LK = S::LK, KR = S::KR, TK = S::TK, NR = S::NR, NCH = S::NCH, VT = S::VT;
   constexpr int HPL = S::HPL;
-  __shared__ __align__(16) float qs[REP * D];               // rotated q staging
-  __shared__ __align__(16) uint16_t pls[2][REP][TK];       // p of a tile, bf16
+  // NW > 1: one workgroup per (row, KV head) whose NW waves take the row's
+  // splits and merge them through LDS (short rows: a windowed layer), no
+  // partials in HBM and no merge launch.
+  static_assert(NW == 1 || (!MERGE && !PAGED && NW <= 16), "workgroup merge form");
+  __shared__ __align__(16) float qs_all[NW][REP * D];           // rotated q staging
+  __shared__ __align__(16) uint16_t pls_all[NW][2][REP][TK];   // p of a tile, bf16
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6) : 0;
+  float *qs = qs_all[wv];
+  auto &pls = pls_all[wv];
   const int g = pa.dec_transpose ? blockIdx.x : blockIdx.y;
   const int item = pa.dec_transpose ? blockIdx.y : blockIdx.x;
   const int SK = __builtin_amdgcn_readfirstlane(pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
@@ -1230,6 +1237,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
       [&](int r0) -> int {
         const int r = row_at(r0);
         const int nr = st.n_new[r];
+        if (NW > 1) return nr <= 1 ? 1 : 0;  // one workgroup per row
         if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
         const DecodeSpan sp = decode_span_dev(la, st.lens[r], st.first[r]);
         return (int)cdiv(sp.hi - sp.base, SK);
@@ -1237,17 +1245,17 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
       &b, &split64);
   if (b < 0) return;
   b = __builtin_amdgcn_readfirstlane(row_at(b));
-  if constexpr (FUSED) {
+  if constexpr (FUSED || NW > 1) {
     if (st.n_new[b] == 0) {  // idle row: its padded token (and zero outputs)
-      store_idle_token<D>(la, fa, b, g, st.lens[b], lane);
-      if constexpr (MERGE) {  // (else the merge kernel writes them)
+      if (FUSED && wv == 0) store_idle_token<D>(la, fa, b, g, st.lens[b], lane);
+      if constexpr (MERGE || NW > 1) {  // (else the merge kernel writes them)
         bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
-        for (int e = lane; e < REP * D; e += 64) o[e] = (bf16)0.f;
+        for (int e = wv * 64 + lane; e < REP * D; e += 64 * NW) o[e] = (bf16)0.f;
       }
       return;
     }
   }
-  const int split = (int)split64;
+  const int split = NW > 1 ? wv : (int)split64;
   const int h0 = g * REP;
   const int64_t p = st.lens[b];
   const DecodeSpan span = decode_span_dev(la, p, st.first[b]);
@@ -1262,7 +1270,9 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   // split count cdiv(hi - base, SK) is also cdiv(tiles, SK / TK) and every
   // split gets a tile.
   const int ntile = (hi - (int)base64 + TK - 1) / TK;
-  const int nsplit = (hi - (int)base64 + SK - 1) / SK;
+  // (the workgroup form: one split per wave, at most one per tile; waves
+  // past the row's splits stream nothing and hold empty partials)
+  const int nsplit = NW > 1 ? (ntile < NW ? ntile : NW) : (hi - (int)base64 + SK - 1) / SK;
   // (uniform values; readfirstlane keeps them in scalar registers, where the
   // tile loads take their offsets)
   const int t_begin = __builtin_amdgcn_readfirstlane((int)base64 + split * TK);
@@ -1563,6 +1573,49 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   float lh[HPL];
 #pragma unroll
   for (int u = 0; u < HPL; ++u) lh[u] = keys_sum<LK>(lsum[u]);
+  if constexpr (NW > 1) {
+    // The workgroup form: each wave's partial to LDS, then wave w merges
+    // heads w, w + NW, ... with the weights and the order of k_combine.
+    __shared__ float wml[NW][REP][2];
+    __shared__ __align__(16) float wout[NW][REP][D];
+#pragma unroll
+    for (int u = 0; u < HPL; ++u) {
+      if (kr == 0 && writer) {
+        wml[wv][hbase + u][0] = m[u];
+        wml[wv][hbase + u][1] = lh[u];
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < REP; ++h)
+#pragma unroll
+      for (int t = 0; t < VT; ++t) {
+        const float o = swap32_sum(acc[h][t]);
+        if (half == 0) wout[wv][h][mm + 32 * t] = o;
+      }
+    __syncthreads();
+    bf16 *ob = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + h0) * D;
+    for (int h = wv; h < REP; h += NW) {
+      // split weights 2^(m_s - M) / L (a split with no visible key: l == 0)
+      const float ls = lane < nsplit ? wml[lane][h][1] : 0.f;
+      const float ms = (lane < nsplit && ls > 0.f) ? wml[lane][h][0] : -INFINITY;
+      const float M = wave_max(ms);
+      const float w = ls > 0.f ? exp2f(ms - M) : 0.f;
+      const float Lt = wave_sum(w * ls);
+      const int wt = __builtin_bit_cast(int, w / Lt);
+      auto wt_of = [&](int sp) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(wt, sp)); };
+      for (int d = lane; d < D; d += 64) {
+        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int sp = 0;
+        for (; sp + 8 <= nsplit; sp += 8) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) a[u] = combine_acc(a[u], wt_of(sp + u), wout[sp + u][h][d]);
+        }
+        for (; sp < nsplit; ++sp) a[0] = combine_acc(a[0], wt_of(sp), wout[sp][h][d]);
+        ob[h * D + d] = (bf16)combine_tree(a);
+      }
+    }
+    return;
+  }
   if constexpr (MERGE) {
     if (nsplit == 1) {
       // One split: the output is o / l, rounded as the merge rounds a
@@ -1674,6 +1727,40 @@ static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const
       launch_kernel((k_decode<D, REP, true, false, S::NBUF, S::WAVES, false>), grid, dim3(64), lc,
                     st, la, pa, (const bf16 *)q, fa, la.table);
   }
+}
+
+// The workgroup form (NW waves per (row, KV head), merged through LDS):
+// three register tiles, two waves per SIMD so that a workgroup's eight waves
+// share one CU.
+constexpr int kDecodeWgWaves = 8;
+
+template <int D, int REP>
+static void launch_decode_wg_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                               const void *q, const FusedArgs &fa, bool fused,
+                               const Launch &lc) {
+  const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)st.B)
+                                     : dim3((unsigned)st.B, (unsigned)la.hkv);
+  const dim3 block(64 * kDecodeWgWaves);
+  if (fused)
+    launch_kernel((k_decode<D, REP, true, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
+                  st, la, pa, (const bf16 *)q, fa, la.table);
+  else
+    launch_kernel((k_decode<D, REP, false, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
+                  st, la, pa, (const bf16 *)q, fa, la.table);
+}
+
+int launch_decode_wg(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                     const void *q, const FusedArgs &fa, bool fused, const Launch &lc) {
+  if (st.C != 1 || la.paged || la.rep > 8) return (int)hipErrorInvalidValue;
+#define KVC_DEC(DD, RR)                                                  \
+  if (st.D == DD && la.rep == RR) {                                      \
+    launch_decode_wg_t<DD, RR>(st, la, pa, q, fa, fused, lc);           \
+    return (int)hipGetLastError();                                       \
+  }
+  KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8)
+  KVC_DEC(64, 1) KVC_DEC(64, 2) KVC_DEC(64, 4) KVC_DEC(64, 8)
+#undef KVC_DEC
+  return (int)hipErrorInvalidValue;
 }
 
 template <int D, int REP>

@@ -53,6 +53,7 @@ struct kvc_cache {
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
   bool fused_merge = false;       // KVC_FUSED_MERGE=1: the appending decode merges its splits
+  bool no_wg = false;             // KVC_DECODE_WG=0: short windows take the split plan too
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -71,6 +72,9 @@ namespace {
 
 // Smallest chunk-attention split (keys) before the split count per row is capped.
 constexpr int32_t kChunkSplitMin = 256;
+// One-token steps of a ring layer of at most this many rows run in the
+// workgroup form of the decode kernel (see wg_layer).
+constexpr int32_t kWgMaxWindow = 1024;
 
 int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
 int64_t round_up(int64_t a, int64_t b) { return (a + b - 1) / b * b; }
@@ -479,6 +483,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_FUSED_MERGE")) h->fused_merge = std::atoi(e) != 0;
+  if (const char *e = std::getenv("KVC_DECODE_WG")) h->no_wg = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -683,6 +688,19 @@ kvc::PartialArgs partial_args(const kvc_t *h) {
   return pa;
 }
 
+// A ring layer of at most kWgMaxWindow rows spends a one-token step mostly on
+// fixed latencies: launch, prologue, a few tiles, the partials' round trip
+// through HBM and a merge launch.  Its one-token steps take the workgroup
+// form instead: one workgroup per (row, KV head) whose waves take the splits
+// and merge through LDS.  (A window mask over a full-length layout keeps the
+// split plan, which its paged form shares, so that the two give the same
+// bits; joint layers and REP > 8 keep it too.)
+bool wg_layer(const kvc_t *h, int32_t layer, const kvc::LayerArgs &la) {
+  return !h->no_wg && la.ring && la.window <= kWgMaxWindow && !la.paged && la.rep <= 8 &&
+         h->lay.layers[layer].joint < 0 && h->cfg.dtype == KVC_BF16 &&
+         kvc::fast_decode_supported(h->cfg.head_dim, la.rep);
+}
+
 // Target waves of one decode round for a layer: resident decode waves per CU
 // (queried once per query-heads-per-KV-head) times the CUs, unless overridden.
 int64_t decode_wave_target(kvc_t *h, const kvc::LayerArgs &la, int D) {
@@ -749,7 +767,15 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
   const bool fast = h->cfg.dtype == KVC_BF16 && kvc::fast_decode_supported(D, la.rep) &&
                     kvc::fast_prefill_supported(D, la.rep);
   int err = 0;
-  if (fast && h->step_static) {
+  if (fast && h->C == 1 && wg_layer(h, layer, la)) {
+    // a one-token step over a short window: the workgroup form writes every
+    // row's output (static steps too: its grid is one workgroup per row)
+    kvc::PartialArgs pa = partial_args(h);
+    kvc::FusedArgs fa;
+    fa.out = out;
+    if (kvc::launch_decode_wg(st, la, pa, q, fa, false, launch_on(h, KVC_K_DECODE, stream)))
+      return KVC_E_HIP;
+  } else if (fast && h->step_static) {
     // one-token rows only; the plan is on the device
     kvc::PartialArgs pa = partial_args(h);
     const int32_t items = static_plan(h, layer, &pa);
@@ -858,6 +884,18 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   if (rc != KVC_OK) return rc;
   const kvc::StepArgs st = step_args(h);
   kvc::PartialArgs pa = partial_args(h);
+  if (wg_layer(h, layer, la)) {  // the workgroup form, appending too
+    kvc::FusedArgs fa;
+    fa.k = k;
+    fa.v = v;
+    fa.slot_out = slot_out_dev;
+    fa.out = out;
+    if (kvc::launch_decode_wg(st, la, pa, q, fa, true, launch_on(h, KVC_K_FUSED, stream)))
+      return KVC_E_HIP;
+    h->appended[layer] = 1;
+    h->attended[layer] = 1;
+    return KVC_OK;
+  }
   int64_t items = 0;
   if (h->step_static) {
     items = static_plan(h, layer, &pa);

@@ -216,6 +216,13 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                         const void *q, const FusedArgs &fa, int32_t n_items, bool merge,
                         const Launch &lc);
+// One-token steps of a short ring layer: one workgroup
+// per (row, KV head), its waves take the row's splits and merge them through
+// LDS into `fa.out` (every row: idle rows get zeros), so there are no
+// partials and no launch_combine.  fused: also the rotation and store of the
+// new key and value (fa.k, fa.v, fa.slot_out), as launch_decode_fused.
+int launch_decode_wg(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
+                     const void *q, const FusedArgs &fa, bool fused, const Launch &lc);
 // qw: waves per workgroup (8: 256 query rows per item; 4: 128).  With
 // pa.chunk_small, the 4-wave launch takes the rows of at most 128 query rows
 // and the 8-wave launch the rest.
