@@ -195,10 +195,15 @@ def _fused_vs_two_calls(work, prompts, decode_steps, tag):
 
 # merge "1": the appending decode merges its splits (KVC_FUSED_MERGE=1); "0"
 # (default): it appends and attends, and the merge kernel combines the splits
-@pytest.mark.parametrize("merge", ["0", "1"])
-def test_fused_decode_rings_and_idle_rows(merge, monkeypatch):
+# wg "1" (default): the ring layers' one-token steps take the workgroup form;
+# "0": the split plan (and the merge kernel, or with merge "1" the in-launch
+# merge), as a longer window would
+@pytest.mark.parametrize("merge,wg", [("0", "1"), ("0", "0"), ("1", "0")])
+def test_fused_decode_rings_and_idle_rows(merge, wg, monkeypatch):
     monkeypatch.setenv("KVC_FUSED_MERGE", merge)
-    say(f"case: fused one-token steps, ring_bf16 (rings W=8 + global), idle rows, merge={merge}")
+    monkeypatch.setenv("KVC_DECODE_WG", wg)
+    say(f"case: fused one-token steps, ring_bf16 (rings W=8 + global), idle rows, "
+        f"merge={merge} wg={wg}")
     work = wl.RING_BF16
     prompts = [(np.array([12, 3, 9, 0]), 12)]
     steps = [np.array([1, 1, 1, 1]), np.array([1, 0, 1, 1]), np.array([0, 1, 1, 0])]
