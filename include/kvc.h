@@ -136,6 +136,8 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_DECODE_FUSED=0      kvc_append_attend enqueues kvc_append + kvc_attend;
  *   KVC_FUSED_MERGE=1       kvc_append_attend merges in its decode launch;
  *   KVC_CHUNK_SMALL=0       every chunk row in 8-wave workgroups;
+ *   KVC_CHUNK_PLAN=0        chunk splits at the cap (16 per longest row)
+ *                           instead of the cost-model plan;
  *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
  *                           1024 rows) take the split plan and the merge
  *                           kernel instead of one workgroup per row;

@@ -54,6 +54,7 @@ struct kvc_cache {
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
   bool fused_merge = false;       // KVC_FUSED_MERGE=1: the appending decode merges its splits
   bool no_wg = false;             // KVC_DECODE_WG=0: short windows take the split plan too
+  bool chunk_cap_only = false;    // KVC_CHUNK_PLAN=0: chunk splits from the split cap alone
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -72,6 +73,9 @@ namespace {
 
 // Smallest chunk-attention split (keys) before the split count per row is capped.
 constexpr int32_t kChunkSplitMin = 256;
+// Price of one chunk-attention split beyond its keys, in keys: staging the
+// query tile, writing its partial and merging it.
+constexpr int64_t kChunkSplitCost = 384;
 // One-token steps of a ring layer of at most this many rows run in the
 // workgroup form of the decode kernel (see wg_layer).
 constexpr int32_t kWgMaxWindow = 1024;
@@ -484,6 +488,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_FUSED_MERGE")) h->fused_merge = std::atoi(e) != 0;
   if (const char *e = std::getenv("KVC_DECODE_WG")) h->no_wg = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_PLAN")) h->chunk_cap_only = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -805,12 +810,60 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       }
       pa->dec_split_keys = decode_split_keys(h, lx, D, dcap);
       decode_order(h, lx, pa);
-      pa->pre_split_keys = (int32_t)std::max<int64_t>(
-          kChunkSplitMin, round_up(ceil_div(max_chunk_span, ccap), kvc::kRowAlign));
       // Chunk rows of at most 128 query rows (a 4-wave workgroup's tile) go
       // to a 4-wave launch, two of whose workgroups share a CU, instead of
       // leaving half of an 8-wave workgroup idle.
       pa->chunk_small = h->no_chunk_small ? 0 : 1;
+      // Chunk split length.  Each launch (8-wave and 4-wave workgroups) is
+      // priced as a list schedule over its resident slots (two 8-wave or four
+      // 4-wave workgroups per CU): the larger of its total work over the
+      // slots and its longest item, where an item costs its keys plus a fixed
+      // kChunkSplitCost (staging the query tile, writing and merging a
+      // partial).  The split count per row (1 .. ccap, never under
+      // kChunkSplitMin keys) with the lowest sum wins, ties to more splits.
+      // Uniform long rows (a batched prefill) come out at fewer splits than
+      // the cap; rows of mixed lengths, whose longest item sets the time,
+      // keep the cap.
+      {
+        const int64_t slots8 = 2 * (int64_t)h->n_cu, slots4 = 4 * (int64_t)h->n_cu;
+        auto cost = [&](int64_t sk) {
+          int64_t sum8 = 0, sum4 = 0, top8 = 0, top4 = 0;
+          for (int32_t b = 0; b < B; ++b) {
+            const int64_t L = h->lens_host[b], n = h->n_new[b];
+            if (n < 2 || lx.ring) continue;
+            const bool small = pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2;
+            const int64_t nqt =
+                ceil_div(n * lx.rep, small ? kvc::kChunkQTile / 2 : kvc::kChunkQTile);
+            int64_t base, span_hi;
+            chunk_span(lx, L, n, h->first_host[b], &base, &span_hi);
+            const int64_t span = span_hi - base;
+            const int64_t w = nqt * lx.hkv * (span + ceil_div(span, sk) * kChunkSplitCost);
+            (small ? sum4 : sum8) += w;
+            int64_t &top = small ? top4 : top8;
+            top = std::max(top, std::min(span, sk) + kChunkSplitCost);
+          }
+          return std::max((sum8 + slots8 - 1) / slots8, top8) +
+                 std::max((sum4 + slots4 - 1) / slots4, top4);
+        };
+        auto keys_for = [&](int64_t k) {
+          return std::max<int64_t>(kChunkSplitMin,
+                                   round_up(ceil_div(max_chunk_span, k), kvc::kRowAlign));
+        };
+        int64_t best = keys_for(ccap);
+        if (!h->chunk_cap_only && max_chunk_span > 0) {
+          int64_t best_cost = cost(best);
+          for (int64_t k = ccap - 1; k >= 1; --k) {
+            const int64_t sk = keys_for(k);
+            if (sk == best) continue;
+            const int64_t c = cost(sk);
+            if (c < best_cost) best = sk, best_cost = c;
+          }
+        }
+        pa->pre_split_keys = (int32_t)std::min<int64_t>(best, 1 << 30);
+      }
+      if (h->log_level >= 2 && layer == 0 && max_chunk_span > 0)
+        std::fprintf(stderr, "[kvc] chunk plan: %d keys per split (longest span %lld)\n",
+                     pa->pre_split_keys, (long long)max_chunk_span);
       int64_t dec_items = 0, pre_items = 0, small_items = 0;
       for (int32_t b = 0; b < B; ++b) {
         const int64_t L = h->lens_host[b], n = h->n_new[b];
