@@ -138,6 +138,8 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_CHUNK_SMALL=0       every chunk row in 8-wave workgroups;
  *   KVC_CHUNK_PLAN=0        chunk splits at the cap (16 per longest row)
  *                           instead of the cost-model plan;
+ *   KVC_CHUNK_DIRECT=0      ring layers' full-chunk steps merge in the
+ *                           merge kernel too;
  *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
  *                           1024 rows) take the split plan and the merge
  *                           kernel instead of one workgroup per row;
@@ -204,7 +206,10 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
  * p - j < W.  Query head h reads KV head h / (Hq / Hkv_l).  Scores are
  * q.k / sqrt(D) in float32, softmax in float32.  Outputs of padded queries
  * (i >= n_new[b]) and of rows with n_new[b] == 0 are exactly zero.  Must
- * follow this layer's kvc_append in the same step (else KVC_E_STATE). */
+ * follow this layer's kvc_append in the same step (else KVC_E_STATE).
+ * Launches: the split attention kernels, then a merge of the splits; on a
+ * ring layer whose step has every row a full chunk (n_new[b] == C >= 2) the
+ * chunk kernel writes `out` itself (one split per row) and no merge runs. */
 int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
 
 /* kvc_append followed by kvc_attend for one layer, in one call: same

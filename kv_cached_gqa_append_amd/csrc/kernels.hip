@@ -2303,6 +2303,22 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   for (int blk = 0; blk < 2; ++blk) {
     float lt = lrun[blk] + __shfl_xor(lrun[blk], 16);
     lt += __shfl_xor(lt, 32);
+    if (pa.direct_out) {
+      // The row's only split: its final output, with the arithmetic of the
+      // merge of one split (weight 1 / l, one fused term, then the merge's
+      // additions of zeros), so it has the bits the merge launch would write.
+      if (rvalid[blk]) {
+        const float inv = 1.f / lt;
+        bf16 *o = static_cast<bf16 *>(pa.direct_out) +
+                  (((int64_t)b * st.C + qi[blk]) * st.Hq + g * REP + hl[blk]) * D;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            o[db * 16 + q4 * 4 + jj] = from_f<bf16>(fmaf(inv, oacc[blk][db][jj], 0.f) + 0.f);
+      }
+      continue;
+    }
     if (rvalid[blk]) {
       const int64_t slot =
           (((int64_t)b * pa.max_chunk + qi[blk]) * st.Hq + g * REP + hl[blk]) * kChunkSplitCap +

@@ -55,6 +55,7 @@ struct kvc_cache {
   bool fused_merge = false;       // KVC_FUSED_MERGE=1: the appending decode merges its splits
   bool no_wg = false;             // KVC_DECODE_WG=0: short windows take the split plan too
   bool chunk_cap_only = false;    // KVC_CHUNK_PLAN=0: chunk splits from the split cap alone
+  bool no_direct = false;         // KVC_CHUNK_DIRECT=0: ring chunk steps merge in k_combine
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -489,6 +490,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_FUSED_MERGE")) h->fused_merge = std::atoi(e) != 0;
   if (const char *e = std::getenv("KVC_DECODE_WG")) h->no_wg = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_PLAN")) h->chunk_cap_only = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_DIRECT")) h->no_direct = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -901,6 +903,12 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       return KVC_OK;
     };
     kvc::PartialArgs pa = partial_args(h);
+    // A ring layer's chunk rows are one split each; when every row is a full
+    // chunk (no decode rows, no padded queries, no idle rows) the chunk
+    // kernel writes the outputs itself and the merge launch is skipped.
+    bool direct = la.ring && !joint && h->C >= 2 && !h->no_direct;
+    for (int32_t b = 0; b < B && direct; ++b) direct = h->n_new[b] == h->C;
+    if (direct) pa.direct_out = out;
     if (run(la, &pa) != KVC_OK) return KVC_E_HIP;
     if (joint) {
       kvc::PartialArgs pj = partial_args(h);
@@ -908,8 +916,10 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       if (run(lj, &pj) != KVC_OK) return KVC_E_HIP;
       pa.joint = kvc::SplitRef{1, lj.ring, lj.window, pj.dec_split_keys, pj.pre_split_keys};
     }
-    err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
-    if (err) return KVC_E_HIP;
+    if (!direct) {
+      err = kvc::launch_combine(h->cfg.dtype, st, la, pa, out, launch_on(h, KVC_K_COMBINE, stream));
+      if (err) return KVC_E_HIP;
+    }
   }
   if (staged) {
     err = kvc::launch_commit(h->cfg.dtype, st, la, launch_on(h, KVC_K_COMMIT, stream));

@@ -120,6 +120,10 @@ struct PartialArgs {
   const int32_t *dec_plan;
   const uint16_t *dec_order_dev;
   int32_t chunk_small;  // chunk rows of <= 128 query rows go to a 4-wave launch
+  // Non-null: every row of the step is a full chunk with one split (a ring
+  // layer), and the chunk kernel writes the final outputs [B, C, Hq, D] here
+  // instead of partials; no merge launch follows.
+  void *direct_out;
   SplitRef base;   // a launch over the partner's keys: its slots follow these splits
   SplitRef joint;  // the combine: the partner's splits follow the layer's own
 };

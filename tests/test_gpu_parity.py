@@ -101,6 +101,31 @@ def test_rep8_ring_and_global_prefill_then_decode():
     pair.check_cache_rows(1)
 
 
+@pytest.mark.parametrize("D,rep", [(64, 2), (128, 4), (128, 8)])
+def test_ring_full_chunks_write_outputs_directly(D, rep, monkeypatch):
+    # When every row of a step is a full chunk, a ring layer's chunk kernel
+    # writes the final outputs itself (one split per row, no merge launch):
+    # checked against the oracle and for the same bits as the merge launch
+    # (KVC_CHUNK_DIRECT=0), over steps that wrap the W=48 ring, with padded
+    # and idle rows in between (those steps take the merge launch).
+    say(f"case: ring full chunks, direct outputs, D={D} rep={rep}")
+    work = wl.Workload(f"ring_direct_{D}_{rep}", 2, 3, 2 * rep, (2, 2), D, 400, (48, 0),
+                       "bf16", 40)
+    monkeypatch.setenv("KVC_CHUNK_DIRECT", "0")
+    ref = Pair(work, poison=True, tag="rd")
+    monkeypatch.setenv("KVC_CHUNK_DIRECT", "1")
+    pair = Pair(work, poison=True, tag="rd")
+    for n in ([40, 40, 40], [40, 40, 40], [40, 17, 0], [40, 40, 40], [40, 40, 40], [1, 1, 1],
+              [40, 40, 40]):
+        C = max(n)
+        got = pair.step(n, C)
+        want = ref.step(n, C, check=False)
+        for l in range(work.n_layer):
+            assert torch.equal(got[l], want[l]), f"n {n} layer {l}: differs from the merge launch"
+    pair.check_cache_rows(0)
+    say(f"  worst abs {pair.worst:.2e} rel {pair.worst_rel:.2e}")
+
+
 def test_decode_many_splits():
     say("case: decode with lengths up to ~3000 (many splits), D128 rep4")
     work = wl.Workload("decode_splits", 1, 6, 32, (8,), 128, 3200, (0,), "bf16", 64)
