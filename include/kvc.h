@@ -140,6 +140,9 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *                           instead of the cost-model plan;
  *   KVC_CHUNK_DIRECT=0      ring layers' full-chunk steps merge in the
  *                           merge kernel too;
+ *   KVC_CHUNK_RING_SMALL=0  ring layers' chunk rows take 8-wave workgroups
+ *                           by size, as other layers' do, even when that
+ *                           launch would hold fewer workgroups than CUs;
  *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
  *                           1024 rows) take the split plan and the merge
  *                           kernel instead of one workgroup per row;

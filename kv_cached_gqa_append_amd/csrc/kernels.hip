@@ -1875,9 +1875,10 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
       [&](int r) -> int {
         const int n = st.n_new[r];
         if (n < 2) return 0;
-        // with small_rows set, rows of at most 128 query rows go to the
-        // 4-wave launch and the rest to the 8-wave one
-        const bool small = n * REP <= 4 * 32;
+        // with chunk_small 1, rows of at most 128 query rows go to the
+        // 4-wave launch and the rest to the 8-wave one; with 2, every row
+        // goes to the 4-wave launch
+        const bool small = pa.chunk_small == 2 || n * REP <= 4 * 32;
         if (pa.chunk_small && small != (QW == 4)) return 0;
         const int nqt = (int)cdiv((int64_t)n * REP, QT);
         if (la.ring) return nqt;

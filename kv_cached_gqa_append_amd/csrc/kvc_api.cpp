@@ -56,6 +56,7 @@ struct kvc_cache {
   bool no_wg = false;             // KVC_DECODE_WG=0: short windows take the split plan too
   bool chunk_cap_only = false;    // KVC_CHUNK_PLAN=0: chunk splits from the split cap alone
   bool no_direct = false;         // KVC_CHUNK_DIRECT=0: ring chunk steps merge in k_combine
+  bool no_ring_small = false;     // KVC_CHUNK_RING_SMALL=0: ring chunk rows by size as others
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -491,6 +492,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_DECODE_WG")) h->no_wg = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_PLAN")) h->chunk_cap_only = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_DIRECT")) h->no_direct = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_RING_SMALL")) h->no_ring_small = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -816,6 +818,18 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       // to a 4-wave launch, two of whose workgroups share a CU, instead of
       // leaving half of an 8-wave workgroup idle.
       pa->chunk_small = h->no_chunk_small ? 0 : 1;
+      // A ring layer's chunk rows are one split each, so a small batch gives
+      // its 8-wave launch fewer workgroups than CUs; then every chunk row
+      // goes to the 4-wave launch, twice the workgroups for the same work.
+      if (pa->chunk_small && lx.ring && !h->no_ring_small) {
+        int64_t wg8 = 0;
+        for (int32_t b = 0; b < B; ++b) {
+          const int64_t n = h->n_new[b];
+          if (n >= 2 && n * lx.rep > kvc::kChunkQTile / 2)
+            wg8 += ceil_div(n * lx.rep, kvc::kChunkQTile) * lx.hkv;
+        }
+        if (wg8 > 0 && wg8 < h->n_cu) pa->chunk_small = 2;
+      }
       // Chunk split length.  Each launch (8-wave and 4-wave workgroups) is
       // priced as a list schedule over its resident slots (two 8-wave or four
       // 4-wave workgroups per CU): the larger of its total work over the
@@ -833,7 +847,8 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
           for (int32_t b = 0; b < B; ++b) {
             const int64_t L = h->lens_host[b], n = h->n_new[b];
             if (n < 2 || lx.ring) continue;
-            const bool small = pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2;
+            const bool small =
+                pa->chunk_small == 2 || (pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2);
             const int64_t nqt =
                 ceil_div(n * lx.rep, small ? kvc::kChunkQTile / 2 : kvc::kChunkQTile);
             int64_t base, span_hi;
@@ -874,7 +889,8 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
           decode_span(lx, L, h->first_host[b], &base, &hi);
           dec_items += ceil_div(hi - base, pa->dec_split_keys);
         } else if (n >= 2) {
-          const bool small = pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2;
+          const bool small =
+              pa->chunk_small == 2 || (pa->chunk_small && n * lx.rep <= kvc::kChunkQTile / 2);
           const int64_t nqt = ceil_div(n * lx.rep, small ? kvc::kChunkQTile / 2 : kvc::kChunkQTile);
           int64_t nks = 1;
           if (!lx.ring) {

@@ -119,7 +119,9 @@ struct PartialArgs {
   // dec_split_keys / dec_order (null: host plan).
   const int32_t *dec_plan;
   const uint16_t *dec_order_dev;
-  int32_t chunk_small;  // chunk rows of <= 128 query rows go to a 4-wave launch
+  // 1: chunk rows of <= 128 query rows go to a 4-wave launch; 2: every
+  // chunk row does (a ring layer whose 8-wave launch would not fill the CUs)
+  int32_t chunk_small;
   // Non-null: every row of the step is a full chunk with one split (a ring
   // layer), and the chunk kernel writes the final outputs [B, C, Hq, D] here
   // instead of partials; no merge launch follows.

@@ -101,14 +101,19 @@ def test_rep8_ring_and_global_prefill_then_decode():
     pair.check_cache_rows(1)
 
 
+# ring_small "1" (default): with fewer 8-wave workgroups than CUs, a ring
+# layer's chunk rows all go to the 4-wave launch; "0": rows by size as on a
+# global layer (8-wave workgroups for more than 128 query rows)
+@pytest.mark.parametrize("ring_small", ["1", "0"])
 @pytest.mark.parametrize("D,rep", [(64, 2), (128, 4), (128, 8)])
-def test_ring_full_chunks_write_outputs_directly(D, rep, monkeypatch):
+def test_ring_full_chunks_write_outputs_directly(D, rep, ring_small, monkeypatch):
     # When every row of a step is a full chunk, a ring layer's chunk kernel
     # writes the final outputs itself (one split per row, no merge launch):
     # checked against the oracle and for the same bits as the merge launch
     # (KVC_CHUNK_DIRECT=0), over steps that wrap the W=48 ring, with padded
     # and idle rows in between (those steps take the merge launch).
-    say(f"case: ring full chunks, direct outputs, D={D} rep={rep}")
+    say(f"case: ring full chunks, direct outputs, D={D} rep={rep} ring_small={ring_small}")
+    monkeypatch.setenv("KVC_CHUNK_RING_SMALL", ring_small)
     work = wl.Workload(f"ring_direct_{D}_{rep}", 2, 3, 2 * rep, (2, 2), D, 400, (48, 0),
                        "bf16", 40)
     monkeypatch.setenv("KVC_CHUNK_DIRECT", "0")
