@@ -143,6 +143,12 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_CHUNK_RING_SMALL=0  ring layers' chunk rows take 8-wave workgroups
  *                           by size, as other layers' do, even when that
  *                           launch would hold fewer workgroups than CUs;
+ *   KVC_CHUNK_SIDE=0        both chunk launches on the caller's stream
+ *                           (default: with rows of both sizes, the 4-wave
+ *                           launch runs on a second stream of the handle,
+ *                           forked from and joined back to the caller's by
+ *                           events, so a capture of the caller's stream
+ *                           takes it in);
  *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
  *                           1024 rows) take the split plan and the merge
  *                           kernel instead of one workgroup per row;

@@ -57,6 +57,12 @@ struct kvc_cache {
   bool chunk_cap_only = false;    // KVC_CHUNK_PLAN=0: chunk splits from the split cap alone
   bool no_direct = false;         // KVC_CHUNK_DIRECT=0: ring chunk steps merge in k_combine
   bool no_ring_small = false;     // KVC_CHUNK_RING_SMALL=0: ring chunk rows by size as others
+  bool no_side = false;           // KVC_CHUNK_SIDE=0: both chunk launches on the caller's stream
+  // A second stream (default priority) for the 4-wave chunk launch beside the
+  // 8-wave one, forked from and joined back to the caller's stream by events;
+  // made at its first use.
+  hipStream_t side = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -493,6 +499,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_CHUNK_PLAN")) h->chunk_cap_only = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_DIRECT")) h->no_direct = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_RING_SMALL")) h->no_ring_small = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_SIDE")) h->no_side = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
@@ -525,6 +532,9 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
 void kvc_destroy(kvc_t *h) {
   if (!h) return;
   for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  if (h->fork) (void)hipEventDestroy(h->fork);
+  if (h->join) (void)hipEventDestroy(h->join);
+  if (h->side) (void)hipStreamDestroy(h->side);
   delete h;
 }
 
@@ -909,11 +919,31 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       if (dec_items > 0 &&
           kvc::launch_decode(st, lx, *pa, q, (int32_t)dec_items, launch_on(h, KVC_K_DECODE, stream)))
         return KVC_E_HIP;
+      // With rows of both sizes, neither chunk launch fills the chip alone:
+      // the 4-wave one runs on the side stream beside the 8-wave one (they
+      // write disjoint partial slots), joined back before the merge.
+      void *s4 = stream;
+      if (pre_items > 0 && small_items > 0 && !h->no_side) {
+        if (!h->side) {
+          if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+              hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+              hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess)
+            return KVC_E_HIP;
+        }
+        if (hipEventRecord(h->fork, static_cast<hipStream_t>(stream)) != hipSuccess ||
+            hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
+          return KVC_E_HIP;
+        s4 = h->side;
+      }
       if (pre_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)pre_items, 8,
                                                launch_on(h, KVC_K_PREFILL, stream)))
         return KVC_E_HIP;
       if (small_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)small_items, 4,
-                                                 launch_on(h, KVC_K_PREFILL, stream)))
+                                                 launch_on(h, KVC_K_PREFILL, s4)))
+        return KVC_E_HIP;
+      if (s4 != stream && (hipEventRecord(h->join, h->side) != hipSuccess ||
+                           hipStreamWaitEvent(static_cast<hipStream_t>(stream), h->join, 0) !=
+                               hipSuccess))
         return KVC_E_HIP;
 
       return KVC_OK;
