@@ -13,10 +13,12 @@ d = 0 .. D/2 - 1, the usual Llama choice.  ``base == 0`` means "already
 rotated": the identity.
 
 Pins: identity at position 0, norm preservation, relativity
-<R(q,m), R(k,n)> = <R(q,m-n), k> and a unit-vector value check (tests).  The
-half-split pairing itself is fixed only by the tiny_agent code; the
-interleaved alternative satisfies the same properties, so the pairing is
-"parity unpinned" beyond that page.
+<R(q,m),R(k,n)> = <R(q,m-n),k> and a unit-vector value check; and, for the
+frequency schedule and the half-split pairing, a comparison with the
+``transformers`` Llama rotary embedding within the error bound of its float32
+tables (the colibri PR, "Tests done", checks against that model), including
+exact-angle cases at positions up to 32767.  A wrong exponent, the
+interleaved pairing or a flipped sign fails those bounds.
 """
 
 import numpy as np
