@@ -36,8 +36,12 @@
  *   - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
  *     on it; all calls of one step must be on one stream (or ordered).
  *   - Every check happens on the host before anything is enqueued: a call
- *     that returns an error has changed nothing.  Asynchronous device faults
- *     surface at the caller's next synchronisation, not here.
+ *     that returns an error has changed nothing.  The one exception is
+ *     KVC_E_HIP, the runtime refusing a launch or call part way: work the
+ *     call enqueued before it stays enqueued (a forked side stream is still
+ *     joined back) and the step cannot be completed; treat it as fatal for
+ *     the handle.  Asynchronous device faults surface at the caller's next
+ *     synchronisation, not here.
  *   - A handle is not thread-safe.
  *   - Integer status codes: KVC_OK (0) or a negative KVC_E_* value.
  */
@@ -77,7 +81,12 @@ typedef struct {
   int32_t batch;            /* B rows, >= 1                                     */
   int32_t n_q_head;         /* Hq                                               */
   int32_t head_dim;         /* D: a multiple of 8 in [8, 256]                    */
-  int32_t max_len;          /* positions per row, >= 1                          */
+  int32_t max_len;          /* positions per row, >= 1; one row's keys of one
+                               KV head (max_len + 1 rows rounded up to 32, or
+                               W + 1 on a ring, times D x dtype bytes) must
+                               take under 2^31 bytes, else KVC_E_ARG: the
+                               kernels address that region with 32-bit
+                               offsets (bf16 D 128: max_len up to 8,388,575) */
   int32_t max_chunk;        /* largest C accepted by kvc_append, in [1, 1024]    */
   int32_t dtype;            /* KVC_F32 or KVC_BF16: cache, q, k, v and out      */
   const int32_t *n_kv_head; /* [n_layer] Hkv_l, Hq % Hkv_l == 0 (host memory)   */
@@ -118,11 +127,18 @@ typedef struct {
 enum { KVC_PAGE_ROWS = 16 };
 
 /* Size in bytes for `what` (KVC_NB_KV or KVC_NB_ALLOC); 0 if cfg is invalid.
- * Pure host computation. */
+ * KVC_NB_KV is the size formula of "Lab 07 - KV cache and sampling" section
+ * 1 (2 x layers x KV heads x head_dim x bytes per token and row) with W rows
+ * for ring layers (colibri PR "Expected memory savings").  Pure host
+ * computation. */
 size_t kvc_nbytes(const kvc_config *cfg, int what);
 
 /* Create a handle over caller-owned device memory `dev_buf` of `buf_bytes`
- * (>= kvc_nbytes(cfg, KVC_NB_ALLOC)) on the current HIP device.  Copies cfg
+ * (>= kvc_nbytes(cfg, KVC_NB_ALLOC)) on the current HIP device: the
+ * preallocated cache of pycraft-1 "model/kv_cache.py" (KVCache.__init__:
+ * every buffer sized once for max_len, keys stored before the GQA
+ * expansion) and tiny_agent "generate.py" KVCache (a global cache with one
+ * scratch row, a W-row ring per sliding layer).  Copies cfg
  * (the arrays too).  Enqueues the RoPE table upload and the zeroing of the
  * row lengths on `stream` and waits for them (create is not part of a step).
  * All rows start empty.  On error *out is NULL and nothing was enqueued.
@@ -148,7 +164,10 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *                           launch runs on a second stream of the handle,
  *                           forked from and joined back to the caller's by
  *                           events, so a capture of the caller's stream
- *                           takes it in);
+ *                           takes it in; the stream and its two events are
+ *                           created here when max_chunk >= 2, never inside
+ *                           a step, and a failure to create them returns
+ *                           KVC_E_HIP);
  *   KVC_DECODE_WG=0         one-token steps of short ring layers (at most
  *                           1024 rows) take the split plan and the merge
  *                           kernel instead of one workgroup per row;
@@ -156,7 +175,9 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
 int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes,
                void *stream, kvc_t **out);
 
-/* Free the host handle.  The device buffer stays the caller's. */
+/* Free the host handle and the side stream and events made at create.  The
+ * device buffer stays the caller's (pycraft-1 "model/kv_cache.py": the cache
+ * memory is the model's, reset only rewinds lengths). */
 void kvc_destroy(kvc_t *h);
 
 /* Empty `n_rows` rows (host array of row indices): their length and left
@@ -190,7 +211,14 @@ int kvc_set_first(kvc_t *h, const int32_t *rows_host, const int32_t *first_host,
 int kvc_admit(kvc_t *dst, const int32_t *dst_rows, const kvc_t *src,
               const int32_t *src_rows, int32_t n_rows, void *stream);
 
-/* Append layer `layer`'s new keys and values.
+/* Append layer `layer`'s new keys and values: tiny_agent "generate.py"
+ * _append_chunk (key rotated at its absolute position lens[b] + i, then
+ * written with the value to slot pos on a global layer or pos % W on a ring,
+ * padding to the scratch row), pycraft-1 "model/kv_cache.py" update (writes
+ * without advancing) and its overflow guard; on a ring with C >= 2 the rows
+ * are staged and committed only after the layer's attention (colibri PR
+ * "inkling: ring-buffer KV cache", "How it works": append after scoring,
+ * keep the last W rows of the chunk).
  *   k, v          device, (B, C, Hkv_l, D) in the cache dtype; k is pre-RoPE
  *                 (rotated here at position lens[b]+i) unless rope_base == 0.
  *   n_new_host    host, [B]: real tokens of row b, 0 <= n_new[b] <= C; tokens
@@ -209,8 +237,13 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
                const int32_t *n_new_host, int32_t C, int32_t *slot_out_dev,
                void *stream);
 
-/* Attend layer `layer`'s queries: q device (B, C, Hq, D) pre-RoPE (unless
- * rope_base == 0); out device (B, C, Hq, D).  Query i of row b sits at
+/* Attend layer `layer`'s queries (tiny_agent "generate.py" _append_chunk:
+ * grouped-query attention straight against the cache under the offset
+ * causal mask of "Lab 07 - KV cache and sampling" section 2, clamped to the
+ * window on a sliding layer as in the colibri PR "What this does"): q device
+ * (B, C, Hq, D) pre-RoPE (unless rope_base == 0); out device (B, C, Hq, D);
+ * C is the step's chunk width latched by its first append (q and out must
+ * hold exactly that many tokens per row).  Query i of row b sits at
  * p = lens[b] + i and sees cached key j iff j <= p and, on a sliding layer,
  * p - j < W.  Query head h reads KV head h / (Hq / Hkv_l).  Scores are
  * q.k / sqrt(D) in float32, softmax in float32.  Outputs of padded queries
@@ -243,8 +276,11 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k,
                       const void *v, const int32_t *n_new_host, int32_t C,
                       int32_t *slot_out_dev, void *out, void *stream);
 
-/* End the step: lens[b] += n_new[b] on the device and in the host mirror.
- * Every layer must have been appended and attended (else KVC_E_STATE). */
+/* End the step: lens[b] += n_new[b] on the device and in the host mirror
+ * (pycraft-1 "model/kv_cache.py" advance, run once after every layer;
+ * tinyllm "kv_cache.py" end_step; "Lab 07 - KV cache and sampling" section 3:
+ * the cache length grows by the chunk's real tokens).  Every layer must have
+ * been appended and attended (else KVC_E_STATE). */
 int kvc_advance(kvc_t *h, void *stream);
 
 /* Paged caches: page use in tokens (tinyllm "kv_cache.py" SlotKVCache:
@@ -263,9 +299,11 @@ int kvc_page_stats(const kvc_t *h, int64_t *used, int64_t *allocated, int64_t *r
 int kvc_reserve(kvc_t *h, const int32_t *rows_host, const int32_t *tokens_host, int32_t n_rows,
                 void *stream);
 
-/* Copy the host mirror of the row lengths into lens_host[B].  KVC_E_STATE
- * while the mirror is behind the device (after a static step, until
- * kvc_sync_lens). */
+/* Copy the host mirror of the row lengths into lens_host[B] (tiny_agent
+ * "generate.py" KVCache keeps the lengths on the host as well, so that no
+ * step reads the device; tinyllm "kv_cache.py" keeps a host copy of the
+ * per-slot positions).  KVC_E_STATE while the mirror is behind the device
+ * (after a static step, until kvc_sync_lens). */
 int kvc_lens(const kvc_t *h, int32_t *lens_host);
 
 /* Static one-token steps: a step whose work does not depend on anything the
@@ -354,7 +392,8 @@ int kvc_timing_begin(kvc_t *h, int32_t max_launches);
 int kvc_timing_begin_kinds(kvc_t *h, int32_t max_launches, int32_t kind_mask);
 int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind);
 
-/* Static text for a status code. */
+/* Static text for a status code; KVC_E_FULL reads "KV cache full", the
+ * message of tiny_agent "generate.py" append and pycraft-1 update. */
 const char *kvc_strerror(int code);
 
 #ifdef __cplusplus

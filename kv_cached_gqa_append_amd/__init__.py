@@ -431,8 +431,16 @@ class Cache:
         if slot_out is not None and (slot_out.dtype != torch.int32 or slot_out.numel() != self.batch * C):
             raise ValueError("slot_out must be int32 (B, C)")
         kvc_append(self.handle, layer, k, v, n_new, C, slot_out, stream)
+        self._step_C = C
 
     def attend(self, layer, q, out=None, stream=None):
+        # The library strides q and out by the chunk width its step latched
+        # at the first append; a narrower tensor would be read past its end.
+        # (Outside a step the library refuses the call: StepOrderError.)
+        C = getattr(self, "_step_C", None)
+        if C is not None and int(q.shape[1]) != C:
+            raise ValueError(f"q: {int(q.shape[1])} tokens per row, the step's appends "
+                             f"latched C = {C}")
         C = int(q.shape[1])
         self._check_tensor(q, self.n_q_head, C, "q")
         if out is None:
@@ -460,10 +468,12 @@ class Cache:
         if slot_out is not None and (slot_out.dtype != torch.int32 or slot_out.numel() != self.batch * C):
             raise ValueError("slot_out must be int32 (B, C)")
         kvc_append_attend(self.handle, layer, q, k, v, n_new, C, out, slot_out, stream)
+        self._step_C = C
         return out
 
     def advance(self, stream=None):
         kvc_advance(self.handle, stream)
+        self._step_C = None
 
     def static_begin(self, n_new_dev: torch.Tensor, stream=None):
         """Begin a static one-token step whose counts (int32 [B], 0 or 1) are
@@ -473,6 +483,7 @@ class Cache:
             raise ValueError(f"n_new_dev must be a contiguous int32 tensor of {self.batch} "
                              f"entries on {self.buffer.device}")
         kvc_static_begin(self.handle, n_new_dev, stream)
+        self._step_C = 1
 
     def static_status(self, stream=None) -> int:
         """Read and clear the sticky flags of static steps (KVC_STATIC_*)."""

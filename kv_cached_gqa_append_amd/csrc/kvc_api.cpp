@@ -60,7 +60,7 @@ struct kvc_cache {
   bool no_side = false;           // KVC_CHUNK_SIDE=0: both chunk launches on the caller's stream
   // A second stream (default priority) for the 4-wave chunk launch beside the
   // 8-wave one, forked from and joined back to the caller's stream by events;
-  // made at its first use.
+  // made at create (max_chunk >= 2), so that no step creates anything.
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
@@ -501,6 +501,13 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
   if (const char *e = std::getenv("KVC_CHUNK_RING_SMALL")) h->no_ring_small = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SIDE")) h->no_side = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_SMALL")) h->no_chunk_small = std::atoi(e) == 0;
+  if (cfg->max_chunk >= 2 && !h->no_side &&
+      (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
+       hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
+       hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess)) {
+    kvc_destroy(h);
+    return KVC_E_HIP;
+  }
   // Plan classes of static steps: layers with the same KV heads, window and layout.
   for (int32_t l = 0; l < cfg->n_layer; ++l) {
     const LayerLayout &L = h->lay.layers[l];
@@ -921,31 +928,27 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
         return KVC_E_HIP;
       // With rows of both sizes, neither chunk launch fills the chip alone:
       // the 4-wave one runs on the side stream beside the 8-wave one (they
-      // write disjoint partial slots), joined back before the merge.
+      // write disjoint partial slots), joined back before the merge.  Once
+      // forked, the join is enqueued whatever the launches return.
       void *s4 = stream;
-      if (pre_items > 0 && small_items > 0 && !h->no_side) {
-        if (!h->side) {
-          if (hipStreamCreateWithFlags(&h->side, hipStreamNonBlocking) != hipSuccess ||
-              hipEventCreateWithFlags(&h->fork, hipEventDisableTiming) != hipSuccess ||
-              hipEventCreateWithFlags(&h->join, hipEventDisableTiming) != hipSuccess)
-            return KVC_E_HIP;
-        }
+      if (pre_items > 0 && small_items > 0 && h->side) {
         if (hipEventRecord(h->fork, static_cast<hipStream_t>(stream)) != hipSuccess ||
             hipStreamWaitEvent(h->side, h->fork, 0) != hipSuccess)
           return KVC_E_HIP;
         s4 = h->side;
       }
+      int rc = KVC_OK;
       if (pre_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)pre_items, 8,
                                                launch_on(h, KVC_K_PREFILL, stream)))
-        return KVC_E_HIP;
-      if (small_items > 0 && kvc::launch_prefill(st, lx, *pa, q, (int32_t)small_items, 4,
-                                                 launch_on(h, KVC_K_PREFILL, s4)))
-        return KVC_E_HIP;
+        rc = KVC_E_HIP;
+      if (rc == KVC_OK && small_items > 0 &&
+          kvc::launch_prefill(st, lx, *pa, q, (int32_t)small_items, 4, launch_on(h, KVC_K_PREFILL, s4)))
+        rc = KVC_E_HIP;
       if (s4 != stream && (hipEventRecord(h->join, h->side) != hipSuccess ||
                            hipStreamWaitEvent(static_cast<hipStream_t>(stream), h->join, 0) !=
                                hipSuccess))
-        return KVC_E_HIP;
-
+        rc = KVC_E_HIP;
+      if (rc != KVC_OK) return rc;
       return KVC_OK;
     };
     kvc::PartialArgs pa = partial_args(h);

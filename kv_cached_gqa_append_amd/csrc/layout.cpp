@@ -15,6 +15,8 @@ namespace kvc {
 namespace {
 
 constexpr int64_t kAlign = 256;
+// Largest (row, KV head) region of K or V the kernels can address.
+constexpr int64_t kMaxRegionBytes = int64_t(1) << 31;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -86,6 +88,11 @@ int compute_layout(const kvc_config *cfg, Layout *lay) {
     // variant in both process positions on one box: +16 rows 6.26 TB/s,
     // +48 6.28, +80 6.29 against 6.08 without.
     if (!L.paged && ((int64_t)L.rows_alloc * D * s) % 8192 == 0) L.rows_alloc += kVBlock;
+    // The attention kernels address one (row, KV head) region of K or V
+    // through a buffer descriptor whose size and offsets are 32-bit: such a
+    // region (rows_alloc * D * s bytes) must stay below 2^31.  The row
+    // offsets themselves are 64-bit.
+    if ((int64_t)L.rows_alloc * D * s >= kMaxRegionBytes) return KVC_E_ARG;
     int64_t region = L.paged ? pool_pages * kPageRows : B * (int64_t)L.rows_alloc;
     if (!mul(&region, hkv) || !mul(&region, D) || !mul(&region, s)) return KVC_E_ARG;
     if (!take(&cur, region, &L.k_off) || !take(&cur, region, &L.v_off)) return KVC_E_ARG;

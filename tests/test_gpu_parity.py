@@ -171,6 +171,8 @@ def test_guards_and_step_order():
     with pytest.raises(K.StepOrderError):
         c.attend(0, q)                                    # attend before append
     c.append(0, k, v, [2, 2])
+    with pytest.raises(ValueError):
+        c.attend(0, q[:, :4].contiguous())                 # fewer tokens than the step's C
     with pytest.raises(K.StepOrderError):
         c.append(0, k, v, [2, 2])                          # same layer twice
     with pytest.raises(K.StepOrderError):

@@ -149,3 +149,23 @@ def test_joint_partner_validation():
     assert nb([-1, 2, 0, -1]) == 0           # a later layer
     assert nb([-1, 0, 1, -1]) == 0           # a ring
     assert nb([-1, 0, 0, -1], hkv=(2, 1, 2, 2)) == 0   # other KV heads
+
+
+def test_region_of_two_gib_is_rejected():
+    # colibri PR "Tests done": cache offsets must not overflow.  The kernels
+    # address one (row, KV head) region of K or V with 32-bit offsets, so a
+    # config whose region reaches 2^31 bytes is refused, not wrapped.
+    def nb(max_len, dtype="bf16", head_dim=128, window=0, n_pages=0):
+        cfg = K.make_config(1, 2, 8, head_dim, max_len, 1, dtype, 2, window, n_pages=n_pages)
+        return K.kvc_nbytes(cfg, K.KVC_NB_ALLOC)
+    # bf16 D 128: rows_alloc = round_up(max_len + 1, 32) + 16 rows of 256 B
+    assert nb(8_388_575) > 0
+    assert nb(8_388_576) == 0
+    assert nb(9_000_000) == 0
+    # D 64 bf16 holds twice the rows; fp32 half as many
+    assert nb(16_777_000, head_dim=64) > 0 and nb(16_777_200, head_dim=64) == 0
+    assert nb(4_194_000, dtype="f32") > 0 and nb(4_194_400, dtype="f32") == 0
+    # a ring layer's region is its window's: a long max_len is fine there
+    assert nb(9_000_000, window=4096) > 0
+    # paged layers address the same logical rows
+    assert nb(9_000_000, n_pages=64) == 0
