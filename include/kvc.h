@@ -63,7 +63,9 @@ enum {
   KVC_E_FULL = -2,    /* "KV cache full": some row would pass max_len         */
   KVC_E_DTYPE = -3,   /* unknown dtype                                        */
   KVC_E_STATE = -4,   /* call out of the step protocol's order                */
-  KVC_E_HIP = -5      /* the HIP runtime reported an error while enqueueing   */
+  KVC_E_HIP = -5,     /* the HIP runtime reported an error while enqueueing   */
+  KVC_E_SCRATCH = -6  /* kvc_attend_noalloc: the step's split partials need
+                         more than its fixed scratch (KVC_NOALLOC_SCRATCH_BYTES) */
 };
 
 enum { KVC_F32 = 0, KVC_BF16 = 1 };
@@ -253,6 +255,27 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
  * ring layer whose step has every row a full chunk (n_new[b] == C >= 2) the
  * chunk kernel writes `out` itself (one split per row) and no merge runs. */
 int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
+
+/* For callers that cannot allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same operation, checks, launches and results as kvc_attend (the same
+ * kernels and split plan, so the same bits), except that the split-K
+ * partials live in a fixed array of KVC_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU for the life of the process, instead of the
+ * handle's buffer.  Nothing is allocated, freed or cleared by the call
+ * (every partial slot the merge reads is written by the same call first).
+ * The step's partials take
+ *     round_up(B*Hq*64*8, 256) + round_up(B*Hq*64*D*4, 256)
+ *   + (a step with a chunk row: round_up(B*C*Hq*16*8, 256) + round_up(B*C*Hq*16*D*4, 256))
+ * bytes (a B 64, Hq 32, D 128 decode step: 65 MiB); a step needing more
+ * returns KVC_E_SCRATCH with nothing enqueued and the layer still
+ * unattended (kvc_attend can then take it).  KVC_E_HIP if the array's
+ * device address could not be looked up at kvc_create.  Every handle on a
+ * GPU shares that GPU's array: calls that may overlap on one GPU (other
+ * streams, other threads, other handles) race and must be ordered by the
+ * caller. */
+#define KVC_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int kvc_attend_noalloc(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
 
 /* kvc_append followed by kvc_attend for one layer, in one call: same
  * arguments (q and out as for kvc_attend), same checks, same results, same

@@ -26,6 +26,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libkvc.so")
 
 KVC_OK, KVC_E_ARG, KVC_E_FULL, KVC_E_DTYPE, KVC_E_STATE, KVC_E_HIP = 0, -1, -2, -3, -4, -5
+KVC_E_SCRATCH = -6
+KVC_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 KVC_F32, KVC_BF16 = 0, 1
 KVC_NB_KV, KVC_NB_ALLOC = 0, 1
 KVC_STATIC_BAD_COUNT, KVC_STATIC_FULL = 1, 2
@@ -45,6 +47,10 @@ class CacheFullError(ValueError):
 
 class StepOrderError(KvcError):
     """A call broke the append -> attend -> advance protocol."""
+
+
+class ScratchTooSmallError(KvcError):
+    """kvc_attend_noalloc: the step's partials exceed the fixed scratch."""
 
 
 class KvcConfig(ctypes.Structure):
@@ -115,6 +121,8 @@ def lib():
         L.kvc_append.restype = ctypes.c_int
         L.kvc_attend.argtypes = [VP, I32, VP, VP, VP]
         L.kvc_attend.restype = ctypes.c_int
+        L.kvc_attend_noalloc.argtypes = [VP, I32, VP, VP, VP]
+        L.kvc_attend_noalloc.restype = ctypes.c_int
         L.kvc_append_attend.argtypes = [VP, I32, VP, VP, VP, VP, I32, VP, VP, VP]
         L.kvc_append_attend.restype = ctypes.c_int
         L.kvc_advance.argtypes = [VP, VP]
@@ -167,6 +175,8 @@ def _check(code: int, what: str) -> None:
         raise ValueError(msg)
     if code == KVC_E_STATE:
         raise StepOrderError(msg)
+    if code == KVC_E_SCRATCH:
+        raise ScratchTooSmallError(msg)
     raise KvcError(msg)
 
 
@@ -268,6 +278,12 @@ def kvc_attend(h, layer: int, q: torch.Tensor, out: torch.Tensor, stream=None) -
     _check(lib().kvc_attend(h, int(layer), ctypes.c_void_p(q.data_ptr()),
                             ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
            "kvc_attend")
+
+
+def kvc_attend_noalloc(h, layer: int, q: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    _check(lib().kvc_attend_noalloc(h, int(layer), ctypes.c_void_p(q.data_ptr()),
+                                    ctypes.c_void_p(out.data_ptr()), _stream_handle(stream)),
+           "kvc_attend_noalloc")
 
 
 def kvc_append_attend(h, layer: int, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, n_new,
@@ -448,6 +464,19 @@ class Cache:
         else:
             self._check_tensor(out, self.n_q_head, C, "out")
         kvc_attend(self.handle, layer, q, out, stream)
+        return out
+
+    def attend_noalloc(self, layer, q, out, stream=None):
+        """attend() with the split partials in the library's fixed per-GPU
+        scratch: the caller passes ``out``; nothing is allocated."""
+        C = getattr(self, "_step_C", None)
+        if C is not None and int(q.shape[1]) != C:
+            raise ValueError(f"q: {int(q.shape[1])} tokens per row, the step's appends "
+                             f"latched C = {C}")
+        C = int(q.shape[1])
+        self._check_tensor(q, self.n_q_head, C, "q")
+        self._check_tensor(out, self.n_q_head, C, "out")
+        kvc_attend_noalloc(self.handle, layer, q, out, stream)
         return out
 
     def append_attend(self, layer, q, k, v, n_new, out=None, slot_out=None, stream=None):

@@ -24,11 +24,36 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "kvc_internal.h"
 
 namespace kvc {
+
+// ---------------------------------------------------------------------------
+// The fixed scratch of kvc_attend_noalloc: one array per GPU, alive until the
+// process ends.  Host code never passes `scratch` itself to a kernel (on the
+// host it names a stand-in, not device memory): noalloc_scratch() looks up
+// its device address once per device and every launch takes that address.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+std::once_flag g_scratch_once[kNoAllocMaxDevices];
+void *g_scratch_ptr[kNoAllocMaxDevices];
+}  // namespace
+
+void *noalloc_scratch(int device) {
+  if (device < 0 || device >= kNoAllocMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[device], [device] {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != device) return;
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[device] = ptr;
+  });
+  return g_scratch_ptr[device];
+}
 
 typedef __bf16 bf16;
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

@@ -63,6 +63,9 @@ struct kvc_cache {
   // made at create (max_chunk >= 2), so that no step creates anything.
   hipStream_t side = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
+  // The device address of this GPU's fixed scratch array (kvc_attend_noalloc),
+  // looked up at create; null if the lookup failed.
+  void *scratch = nullptr;
   bool no_chunk_small = false;    // KVC_CHUNK_SMALL=0: every chunk row in 8-wave workgroups
   // static one-token steps (counts in device memory, planned on the device)
   bool step_static = false;           // the current step is one
@@ -369,6 +372,7 @@ const char *kvc_strerror(int code) {
     case KVC_E_DTYPE: return "unknown dtype";
     case KVC_E_STATE: return "call out of step order";
     case KVC_E_HIP: return "HIP runtime error";
+    case KVC_E_SCRATCH: return "step needs more than the fixed scratch of kvc_attend_noalloc";
     default: return "unknown status";
   }
 }
@@ -417,6 +421,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     delete h;
     return KVC_E_HIP;
   }
+  h->scratch = kvc::noalloc_scratch(h->device);
   hipStream_t s = (hipStream_t)stream;
   // RoPE table: angle p * base^(-2d/D) in double, cos/sin rounded once to fp32.
   if (h->lay.rope_off >= 0) {
@@ -773,13 +778,70 @@ int kvc_append(kvc_t *h, int32_t layer, const void *k, const void *v,
   return KVC_OK;
 }
 
-int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Bytes of the split partials a step of this handle writes in one layer's
+// attention, laid out as kvc_attend_noalloc places them in the fixed
+// scratch: decode (m, l) and o per (row, head, split slot), then, when the
+// step has chunk rows, the same per (row, token, head, split slot) with the
+// step's chunk width C as the token stride.
+struct ScratchPlan {
+  int64_t dml = 0, dout = 0, pml = 0, pout = 0, total = 0;
+};
+ScratchPlan scratch_plan(const kvc_t *h) {
+  const int64_t B = h->cfg.batch, Hq = h->cfg.n_q_head, D = h->cfg.head_dim;
+  const int64_t dq = B * Hq * kvc::kDecodeSplitCap;
+  ScratchPlan p;
+  int64_t cur = 0;
+  p.dml = cur;
+  cur = round_up(cur + dq * 8, 256);
+  p.dout = cur;
+  cur = round_up(cur + dq * D * 4, 256);
+  bool chunk = false;
+  if (!h->step_static)
+    for (int32_t b = 0; b < h->cfg.batch; ++b) chunk |= h->n_new[b] >= 2;
+  if (chunk) {
+    const int64_t pq = B * (int64_t)h->C * Hq * kvc::kChunkSplitCap;
+    p.pml = cur;
+    cur = round_up(cur + pq * 8, 256);
+    p.pout = cur;
+    cur = round_up(cur + pq * D * 4, 256);
+  } else {
+    p.pml = p.pout = -1;
+  }
+  p.total = cur;
+  return p;
+}
+
+// One layer's attention (kvc_attend).  `scratch`: the split partials go to
+// this device array, laid out by scratch_plan, instead of the handle's buffer.
+int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream,
+                 char *scratch) {
   if (!h || !q || !out) return KVC_E_ARG;
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   if (!h->in_step || !h->appended[layer] || h->attended[layer]) return KVC_E_STATE;
   const int32_t jl = h->lay.layers[layer].joint;
   const bool joint = jl >= 0;
   if (joint && !h->appended[jl]) return KVC_E_STATE;  // the partner's keys of this step first
+  ScratchPlan sp;
+  if (scratch) {
+    sp = scratch_plan(h);
+    if (sp.total > kvc::kNoAllocScratchBytes) return KVC_E_SCRATCH;
+  }
+  // Where this call's split partials live.
+  auto parts = [&]() {
+    kvc::PartialArgs pa = partial_args(h);
+    if (scratch) {
+      pa.dml = reinterpret_cast<float *>(scratch + sp.dml);
+      pa.dout = reinterpret_cast<float *>(scratch + sp.dout);
+      pa.pml = sp.pml >= 0 ? reinterpret_cast<float *>(scratch + sp.pml) : nullptr;
+      pa.pout = sp.pout >= 0 ? reinterpret_cast<float *>(scratch + sp.pout) : nullptr;
+      pa.max_chunk = h->C;
+    }
+    return pa;
+  };
   if (!use_device(h)) return KVC_E_HIP;
   const kvc::StepArgs st = step_args(h);
   const kvc::LayerArgs la = layer_args(h, layer);
@@ -796,14 +858,14 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
   if (fast && h->C == 1 && wg_layer(h, layer, la)) {
     // a one-token step over a short window: the workgroup form writes every
     // row's output (static steps too: its grid is one workgroup per row)
-    kvc::PartialArgs pa = partial_args(h);
+    kvc::PartialArgs pa = parts();
     kvc::FusedArgs fa;
     fa.out = out;
     if (kvc::launch_decode_wg(st, la, pa, q, fa, false, launch_on(h, KVC_K_DECODE, stream)))
       return KVC_E_HIP;
   } else if (fast && h->step_static) {
     // one-token rows only; the plan is on the device
-    kvc::PartialArgs pa = partial_args(h);
+    kvc::PartialArgs pa = parts();
     const int32_t items = static_plan(h, layer, &pa);
     err = kvc::launch_decode(st, la, pa, q, items, launch_on(h, KVC_K_DECODE, stream));
     if (err) return KVC_E_HIP;
@@ -951,7 +1013,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
       if (rc != KVC_OK) return rc;
       return KVC_OK;
     };
-    kvc::PartialArgs pa = partial_args(h);
+    kvc::PartialArgs pa = parts();
     // A ring layer's chunk rows are one split each; when every row is a full
     // chunk (no decode rows, no padded queries, no idle rows) the chunk
     // kernel writes the outputs itself and the merge launch is skipped.
@@ -960,7 +1022,7 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
     if (direct) pa.direct_out = out;
     if (run(la, &pa) != KVC_OK) return KVC_E_HIP;
     if (joint) {
-      kvc::PartialArgs pj = partial_args(h);
+      kvc::PartialArgs pj = parts();
       pj.base = kvc::SplitRef{1, la.ring, la.window, pa.dec_split_keys, pa.pre_split_keys};
       if (run(lj, &pj) != KVC_OK) return KVC_E_HIP;
       pa.joint = kvc::SplitRef{1, lj.ring, lj.window, pj.dec_split_keys, pj.pre_split_keys};
@@ -976,6 +1038,20 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) 
   }
   h->attended[layer] = 1;
   return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) {
+  return attend_layer(h, layer, q, out, stream, nullptr);
+}
+
+int kvc_attend_noalloc(kvc_t *h, int32_t layer, const void *q, void *out, void *stream) {
+  if (!h) return KVC_E_ARG;
+  if (!h->scratch) return KVC_E_HIP;  // the device array's address was never found
+  return attend_layer(h, layer, q, out, stream, static_cast<char *>(h->scratch));
 }
 
 int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, const void *v,

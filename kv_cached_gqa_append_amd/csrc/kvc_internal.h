@@ -239,6 +239,14 @@ int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const Par
 // lj: the joint partner's layer (lj.k == nullptr: none).
 int launch_generic(int dtype, const StepArgs &st, const LayerArgs &la, const LayerArgs &lj,
                    const void *q, void *out, const Launch &lc);
+// A fixed device array per GPU holding one layer's split partials for
+// kvc_attend_noalloc (callers that cannot allocate); its size, and its
+// address on `device`, looked up once per device with that device current
+// (nullptr if the lookup failed or the device index is out of range).
+constexpr int64_t kNoAllocScratchBytes = KVC_NOALLOC_SCRATCH_BYTES;
+static_assert(kNoAllocScratchBytes == int64_t(128) << 20, "scratch size");
+constexpr int kNoAllocMaxDevices = 64;
+void *noalloc_scratch(int device);
 bool fast_decode_supported(int D, int rep);
 // Decode workgroups (one wave each) resident per compute unit; 0 on error.
 int decode_waves_per_cu(int D, int rep);

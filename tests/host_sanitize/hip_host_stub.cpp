@@ -342,6 +342,16 @@ int launch_generic(int, const StepArgs &st, const LayerArgs &la, const LayerArgs
   ++stub::g_launches;
   return 0;
 }
+void *noalloc_scratch(int device) {
+  // a host stand-in for the device array, registered like the buffers
+  static char *mem = nullptr;
+  if (device != 0) return nullptr;
+  if (!mem) {
+    mem = static_cast<char *>(std::aligned_alloc(256, (size_t)kNoAllocScratchBytes));
+    stub_register(mem, (size_t)kNoAllocScratchBytes);
+  }
+  return mem;
+}
 bool fast_decode_supported(int D, int rep) {
   return (D == 64 || D == 128) && (rep == 1 || rep == 2 || rep == 4 || rep == 8 || rep == 16);
 }

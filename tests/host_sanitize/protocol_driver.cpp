@@ -128,7 +128,22 @@ struct Run {
     }
     CHECK(kvc_reset(h, std::vector<int32_t>{0}.data(), 1, nullptr) == KVC_E_STATE);
     CHECK(kvc_append(h, order[0], k(), v(), n.data(), C, nullptr, nullptr) == KVC_E_STATE);
-    for (int l : order) CHECK(kvc_attend(h, l, q(), out(), nullptr) == KVC_OK);
+    // every other layer through the fixed-scratch entry point, which
+    // refuses a step whose partials would not fit it
+    bool chunk = false;
+    for (int32_t x : n) chunk |= x >= 2;
+    const int64_t B = cfg.c.batch, Hq = cfg.c.n_q_head, D = cfg.c.head_dim;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    int64_t need = up(B * Hq * 64 * 8) + up(B * Hq * 64 * D * 4);
+    if (chunk) need += up(B * C * Hq * 16 * 8) + up(B * C * Hq * 16 * D * 4);
+    for (int l : order) {
+      if (l % 2) {
+        const int rc = kvc_attend_noalloc(h, l, q(), out(), nullptr);
+        CHECK(rc == (need <= (int64_t)KVC_NOALLOC_SCRATCH_BYTES ? KVC_OK : KVC_E_SCRATCH));
+        if (rc == KVC_OK) continue;
+      }
+      CHECK(kvc_attend(h, l, q(), out(), nullptr) == KVC_OK);
+    }
     CHECK(kvc_attend(h, order[0], q(), out(), nullptr) == KVC_E_STATE);
     CHECK(kvc_advance(h, nullptr) == KVC_OK);
     for (int b = 0; b < cfg.c.batch; ++b) lens[b] += n[b];
