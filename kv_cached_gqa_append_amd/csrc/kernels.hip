@@ -1926,10 +1926,16 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const int W = la.window;
 
   // -- this wave's two 16-row query blocks; lane (q4, nl) holds row nl --------
+  // Their loads (and those of their rotation) go out here; the rotation runs
+  // after the first key tiles' loads are issued, so the two round trips
+  // overlap instead of following one another.
+  constexpr int HS = NDS / 2;  // partner d + D/2 sits HS steps later
   int rq[2], qi[2], hl[2];
   bool rvalid[2];
   int64_t qpos[2];
-  bf16x8_t qf[2][NDS];
+  uint4 qv[2][NDS];
+  float4 rp[2][HS][4];  // (cos, sin) of the 8 consecutive frequencies of a step, 4 per load
+  const bool rot = st.rope != nullptr;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     rq[blk] = qt * QT + wave * 32 + blk * 16 + nl;
@@ -1937,42 +1943,56 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     qi[blk] = rq[blk] / REP;
     hl[blk] = rq[blk] % REP;
     qpos[blk] = L + qi[blk];
-    float raw[NDS][8];
     const bf16 *qsrc = q + (((int64_t)b * st.C + qi[blk]) * st.Hq + g * REP + hl[blk]) * D;
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      if (rvalid[blk]) {
-        const uint4 x = *reinterpret_cast<const uint4 *>(qsrc + ds * 32 + q4 * 8);
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    for (int ds = 0; ds < NDS; ++ds)
+      qv[blk][ds] = rvalid[blk] ? *reinterpret_cast<const uint4 *>(qsrc + ds * 32 + q4 * 8)
+                                : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int ds = 0; ds < HS; ++ds) {
+      const float4 *rsrc =
+          reinterpret_cast<const float4 *>(st.rope + (qpos[blk] * (D / 2) + ds * 32 + q4 * 8) * 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        rp[blk][ds][u] = (rot && rvalid[blk]) ? rsrc[u] : make_float4(1.f, 0.f, 1.f, 0.f);
+    }
+  }
+  // (the loads above are issued before anything below: the hand-placed tile
+  // waits count only the tile loads that follow them)
+  asm volatile("" ::: "memory");
+  bf16x8_t qf[2][NDS];
+  auto make_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float raw[NDS][8];
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        const uint32_t w[4] = {qv[blk][ds].x, qv[blk][ds].y, qv[blk][ds].z, qv[blk][ds].w};
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
           raw[ds][2 * e2] = bf_lo(w[e2]);
           raw[ds][2 * e2 + 1] = bf_hi(w[e2]);
         }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) raw[ds][e] = 0.f;
       }
+      if (rot && rvalid[blk]) {
+#pragma unroll
+        for (int ds = 0; ds < HS; ++ds)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float4 cs = rp[blk][ds][e / 2];
+            const float c = (e & 1) ? cs.z : cs.x;
+            const float sn = (e & 1) ? cs.w : cs.y;
+            const float x1 = raw[ds][e], x2 = raw[ds + HS][e];
+            raw[ds][e] = x1 * c - x2 * sn;
+            raw[ds + HS][e] = x1 * sn + x2 * c;
+          }
+      }
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[blk][ds][e] = (bf16)raw[ds][e];
     }
-    if (st.rope && rvalid[blk]) {
-      constexpr int HS = NDS / 2;  // partner d + D/2 sits HS steps later
-#pragma unroll
-      for (int ds = 0; ds < HS; ++ds)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int d = ds * 32 + q4 * 8 + e;
-          const float c = st.rope[(qpos[blk] * (D / 2) + d) * 2 + 0];
-          const float sn = st.rope[(qpos[blk] * (D / 2) + d) * 2 + 1];
-          const float x1 = raw[ds][e], x2 = raw[ds + HS][e];
-          raw[ds][e] = x1 * c - x2 * sn;
-          raw[ds + HS][e] = x1 * sn + x2 * c;
-        }
-    }
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[blk][ds][e] = (bf16)raw[ds][e];
-  }
+  };
   const bool wave_live = __builtin_amdgcn_readfirstlane((int)(__ballot(rvalid[0]) != 0)) != 0;
 
   // -- key segments -------------------------------------------------------------
@@ -2128,6 +2148,16 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // positions fit in 32 bits (max_len < 2^31)
   const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
   const int first_i = st.first[b];  // left padding: keys before it are hidden
+  // Ring history: slot t < rr holds position t + ring_lo, slot t >= rr
+  // position t + ring_hi (rr = L mod W: the slot the next token takes), in
+  // 32-bit arithmetic once per kernel instead of per score.
+  const int ring_rr = la.ring ? (int)(L % W) : 0;
+  const int ring_lo = Li - ring_rr, ring_hi = Li - ring_rr - W;
+  // The oldest position a ring history tile [t0, t0 + 32) holds (a tile
+  // across slot rr holds position L - W, the oldest of all).
+  auto ring_min_pos = [=](int t0) __attribute__((always_inline)) {
+    return t0 + 31 < ring_rr ? t0 + ring_lo : (t0 >= ring_rr ? t0 + ring_hi : Li - W);
+  };
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   floatx4 oacc[2][NDB];
 #pragma unroll
@@ -2162,8 +2192,14 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // on a windowed layer, inside its last position's window) needs no mask:
     // only the tiles at the diagonal and the edges do.
     const int t0i = (int)t0, vloi = (int)vlo, vhii = (int)vhi;
-    const bool full = kind == 0 && t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
-                      (W == 0 || pmax_i - t0i < W) && t0i >= first_i;
+    // (a ring history tile: every slot holds data, and its oldest position
+    // is inside the window of the q tile's last query and past the left
+    // padding; every history position is below the q tile's first)
+    const int rmin = ring_min_pos(t0i);
+    const bool full = kind == 0 ? (t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
+                                   (W == 0 || pmax_i - t0i < W) && t0i >= first_i)
+                                : (kind == 1 && t0i + 32 <= vhii && pmax_i - rmin < W &&
+                                   rmin >= first_i && rmin >= 0);
     // Both blocks' masks and maxima first, then one (rarely taken) branch
     // for the accumulators' rescale, so that the exponentials and the P.V
     // products of the two blocks share one basic block and the scheduler can
@@ -2193,7 +2229,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
             if (kind == 0)
               pos = t;
             else if (kind == 1)
-              pos = (int)ring_slot_pos(t, L, W);
+              pos = t + (t < ring_rr ? ring_lo : ring_hi);
             else
               pos = Li + t;
             bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp &&
@@ -2284,8 +2320,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // stage is rewritten two steps after it was last read, behind a barrier).
   // Steps run in groups of P so set indices are compile-time; the last group
   // is padded with empty steps, so every path keeps the same loads in flight.
-  // The queries' loads above are retired before the first tile load.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // The queries' loads above are older than every tile load, so the tile
+  // waits retire them too.
   // (a set's loads retire together: waiting for its first register while
   // the later sets' 2 LPT (P - 1) loads stay outstanding covers all of it)
   constexpr int AFTER = 2 * LPT * (CP - 1);
@@ -2298,6 +2334,10 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   };
   u32x4 rk[CP][LPT], rv[CP][LPT];
   static_for<0, CP>([&](auto t) { issue(decltype(t)::value, rk[decltype(t)::value], rv[decltype(t)::value]); });
+  // Nothing below moves above the tile loads: the queries are rotated while
+  // the first tiles are in flight.
+  __builtin_amdgcn_sched_barrier(0);
+  make_q();
   wait_set(rk[0], rv[0]);
   store(0, rk[0], rv[0], 0);
   issue(CP, rk[0], rv[0]);
@@ -2337,11 +2377,15 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         const float inv = 1.f / lt;
         bf16 *o = static_cast<bf16 *>(pa.direct_out) +
                   (((int64_t)b * st.C + qi[blk]) * st.Hq + g * REP + hl[blk]) * D;
+        // (four consecutive elements per lane and d block: one 8-byte store)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db) {
+          float y[4];
 #pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            o[db * 16 + q4 * 4 + jj] = from_f<bf16>(fmaf(inv, oacc[blk][db][jj], 0.f) + 0.f);
+          for (int jj = 0; jj < 4; ++jj) y[jj] = fmaf(inv, oacc[blk][db][jj], 0.f) + 0.f;
+          *reinterpret_cast<uint2 *>(o + db * 16 + q4 * 4) =
+              make_uint2(pack_bf16(y[0], y[1]), pack_bf16(y[2], y[3]));
+        }
       }
       continue;
     }
@@ -2360,6 +2404,94 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
           for (int jj = 0; jj < 4; ++jj)
             pa.pout[slot * D + db * 16 + q4 * 4 + jj] = oacc[blk][db][jj];
       }
+    }
+  }
+
+  // -- ring commit (colibri PR "How it works": append after scoring) ---------------
+  // A ring layer's chunk rows were scored from the ring and from staging;
+  // once every q tile of this (row, KV head) has read them, the staged rows
+  // that survive the keep rule (positions >= L + n - W) go to their slots
+  // p mod W.  Each workgroup counts its finish; the last one commits.  Every
+  // other workgroup's loads have returned before its count (its waves
+  // waited for all of them), so no read of a slot can follow its overwrite.
+  if (pa.ring_cnt != nullptr) {
+    __shared__ int commit_last;
+    __syncthreads();
+    if (tid == 0) {
+      const int nqt = (int)cdiv((int64_t)n * REP, QT);
+      const int prev =
+          __hip_atomic_fetch_add(pa.ring_cnt + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      commit_last = prev == nqt - 1;
+    }
+    __syncthreads();
+    if (commit_last) {
+      const int i0 = n > W ? n - W : 0;  // first kept staged row
+      constexpr int CU = 4;  // copies per thread in flight
+      // K: row-major on both sides, 16-byte chunks
+      constexpr int KC = D / 8;
+      const int nkc = (n - i0) * KC;
+      for (int c0 = tid; c0 < nkc; c0 += CU * NT) {
+        uint4 x[CU];
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int c = c0 + u * NT;
+          if (c < nkc)
+            x[u] = *reinterpret_cast<const uint4 *>(
+                k_row<bf16>(la.sk, bg, la.stage_rows_alloc, i0 + c / KC, D) + (c % KC) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < CU; ++u) {
+          const int c = c0 + u * NT;
+          if (c < nkc)
+            *reinterpret_cast<uint4 *>(
+                k_row<bf16>(la.k, bg, la.rows_alloc, (L + i0 + c / KC) % W, D) + (c % KC) * 8) = x[u];
+        }
+      }
+      // V: 16-row blocks stored transposed on both sides.  When the kept rows
+      // start a block on both sides (and W is whole blocks), each whole block
+      // is one contiguous run of D x 16 elements; the rest goes element by
+      // element.
+      int iv = i0;
+      if ((L + i0) % kVBlock == 0 && i0 % kVBlock == 0 && W % kVBlock == 0) {
+        constexpr int BC = D * kVBlock / 8;  // 16-byte chunks per block
+        const int nb = (n - i0) / kVBlock;
+        for (int c0 = tid; c0 < nb * BC; c0 += CU * NT) {
+          uint4 x[CU];
+#pragma unroll
+          for (int u = 0; u < CU; ++u) {
+            const int c = c0 + u * NT;
+            if (c < nb * BC)
+              x[u] = *reinterpret_cast<const uint4 *>(
+                  v_block<bf16>(la.sv, bg, la.stage_rows_alloc, i0 / kVBlock + c / BC, D) +
+                  (c % BC) * 8);
+          }
+#pragma unroll
+          for (int u = 0; u < CU; ++u) {
+            const int c = c0 + u * NT;
+            if (c < nb * BC)
+              *reinterpret_cast<uint4 *>(
+                  v_block<bf16>(la.v, bg, la.rows_alloc,
+                                ((L + i0) / kVBlock + c / BC) % (W / kVBlock), D) +
+                  (c % BC) * 8) = x[u];
+          }
+        }
+        iv = i0 + nb * kVBlock;
+      }
+      const int nv = (n - iv) * D;
+      for (int e0 = tid; e0 < nv; e0 += 8 * NT) {
+        bf16 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * NT;
+          if (e < nv) x[u] = *v_elem<bf16>(la.sv, bg, la.stage_rows_alloc, iv + e / D, e % D, D);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int e = e0 + u * NT;
+          if (e < nv) *v_elem<bf16>(la.v, bg, la.rows_alloc, (L + iv + e / D) % W, e % D, D) = x[u];
+        }
+      }
+      if (tid == 0) __hip_atomic_store(pa.ring_cnt + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

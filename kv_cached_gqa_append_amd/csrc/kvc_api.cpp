@@ -855,6 +855,7 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
   const bool fast = h->cfg.dtype == KVC_BF16 && kvc::fast_decode_supported(D, la.rep) &&
                     kvc::fast_prefill_supported(D, la.rep);
   int err = 0;
+  bool committed = false;  // the chunk launches committed the staged ring rows
   if (fast && h->C == 1 && wg_layer(h, layer, la)) {
     // a one-token step over a short window: the workgroup form writes every
     // row's output (static steps too: its grid is one workgroup per row)
@@ -1020,7 +1021,10 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
     bool direct = la.ring && !joint && h->C >= 2 && !h->no_direct;
     for (int32_t b = 0; b < B && direct; ++b) direct = h->n_new[b] == h->C;
     if (direct) pa.direct_out = out;
+    // staged ring rows: the chunk launches commit them after scoring
+    if (staged) pa.ring_cnt = reinterpret_cast<int32_t *>(h->base + h->lay.cnt_off);
     if (run(la, &pa) != KVC_OK) return KVC_E_HIP;
+    committed = staged;
     if (joint) {
       kvc::PartialArgs pj = parts();
       pj.base = kvc::SplitRef{1, la.ring, la.window, pa.dec_split_keys, pa.pre_split_keys};
@@ -1032,7 +1036,7 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
       if (err) return KVC_E_HIP;
     }
   }
-  if (staged) {
+  if (staged && !committed) {
     err = kvc::launch_commit(h->cfg.dtype, st, la, launch_on(h, KVC_K_COMMIT, stream));
     if (err) return KVC_E_HIP;
   }

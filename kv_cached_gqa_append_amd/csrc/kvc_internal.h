@@ -128,6 +128,10 @@ struct PartialArgs {
   void *direct_out;
   SplitRef base;   // a launch over the partner's keys: its slots follow these splits
   SplitRef joint;  // the combine: the partner's splits follow the layer's own
+  // Non-null on a ring layer's chunk launches with staged rows: one counter
+  // per (row, KV head), zero between launches; the last q tile of a (row,
+  // KV head) to finish commits its staged rows to the ring.
+  int32_t *ring_cnt;
 };
 constexpr int kDecodeOrderMax = 256;
 
