@@ -573,6 +573,15 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
     }
   }
   const int64_t bg = (int64_t)b * la.hkv + g;
+  // Staging: V rows past the chunk's n rows, to the end of their 32-row tile,
+  // are zero (the chunk kernel reads whole tiles and masks those rows).
+  if (staged && i == 0) {
+    int64_t end = ((int64_t)n + kRowAlign - 1) / kRowAlign * kRowAlign;
+    if (end > la.stage_rows_alloc) end = la.stage_rows_alloc;
+    for (int d = threadIdx.x; d < st.D; d += 64)
+      for (int64_t rz = n; rz < end; ++rz)
+        *v_elem<T>(la.sv, bg, la.stage_rows_alloc, rz, d, st.D) = from_f<T>(0.f);
+  }
   T *kd, *vd;
   if (staged) {
     if (!valid) return;  // staging rows of padding are never read
@@ -1850,14 +1859,6 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // the score accumulator already has the layout P^T needs as an operand.
 // Masks apply only on tiles at the diagonal or an edge.
 // ---------------------------------------------------------------------------
-struct KeySeg {
-  const char *kreg, *vreg;  // region bases
-  int ralloc;               // rows per head in the region
-  int64_t first, end;       // storage rows [first, end) to visit (first % 32 == 0)
-  int64_t vlo, vhi;         // rows holding data of this sequence
-  int kind;                 // 0: position = row; 1: ring history; 2: staging (pos = L + row)
-};
-
 // PAGED: a paged full layer; a 32-row tile spans two pages, and the chunks
 // each wave loads lie in one of them.
 // QW: waves per workgroup, 32 query rows each (8: 256-row query tiles, the
@@ -1995,16 +1996,23 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   };
   const bool wave_live = __builtin_amdgcn_readfirstlane((int)(__ballot(rvalid[0]) != 0)) != 0;
 
-  // -- key segments -------------------------------------------------------------
+  // -- key runs ------------------------------------------------------------------
+  // At most two runs of storage rows, visited in order: a full layer's cache
+  // rows (run 0 only), or a ring layer's history slots (run 0) and then the
+  // chunk's own rows in staging (run 1).  Per run, as 32-bit scalars: the
+  // first row (a multiple of 32), the rows holding this sequence's data
+  // [vlo, vhi), and the position of row t, t + (t < psplit ? poff_a : poff_b):
+  // a full layer's row is its position; ring slot t holds t + L - L mod W
+  // below L mod W (the slot the next token takes) and t + L - L mod W - W
+  // from there on; staging row t holds L + t.  (Positions fit in 32 bits:
+  // max_len < 2^31.)
   // Positions of the whole q-tile span [pmin, pmax].
   const int rlast = (qt + 1) * QT - 1 < n * REP - 1 ? (qt + 1) * QT - 1 : n * REP - 1;
   const int64_t pmin = L + (int64_t)(qt * QT) / REP;
   const int64_t pmax = L + rlast / REP;
-  KeySeg seg0{}, seg1{};
+  const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
+  int f0, e0, vlo0, vhi0, psplit0 = 0, pa0 = 0, pb0 = 0;
   if (!la.ring) {
-    seg0.kreg = la.k;
-    seg0.vreg = la.v;
-    seg0.ralloc = la.rows_alloc;
     int64_t a = cbase + (int64_t)ks * SKP;
     int64_t e = a + SKP < chi ? a + SKP : chi;
     if (e > pmax + 1) e = pmax + 1;
@@ -2012,43 +2020,32 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
       const int64_t wlo = (pmin - W + 1) / 32 * 32;
       if (a < wlo) a = wlo;
     }
-    seg0.first = a;
-    seg0.end = e > a ? e : a;
-    seg0.vlo = clo;
-    seg0.vhi = chi;
-    seg0.kind = 0;
+    f0 = (int)a;
+    e0 = (int)(e > a ? e : a);
+    vlo0 = (int)clo;
+    vhi0 = (int)chi;
   } else {
-    const int64_t nh = L < W ? L : W;
-    seg0.kreg = la.k;
-    seg0.vreg = la.v;
-    seg0.ralloc = la.rows_alloc;
-    seg0.first = 0;
-    seg0.end = nh;
-    seg0.vlo = 0;
-    seg0.vhi = nh;
-    seg0.kind = 1;
-    seg1.kreg = la.sk;
-    seg1.vreg = la.sv;
-    seg1.ralloc = la.stage_rows_alloc;
-    seg1.first = 0;
-    seg1.end = n;
-    seg1.vlo = 0;
-    seg1.vhi = n;
-    seg1.kind = 2;
+    const int nh = L < W ? Li : W;
+    f0 = 0;
+    e0 = nh;
+    vlo0 = 0;
+    vhi0 = nh;
+    psplit0 = (int)(L % W);
+    pa0 = Li - psplit0;
+    pb0 = Li - psplit0 - W;
   }
-  // Tiles of the two segments, visited one after the other.
-  const int n0 = __builtin_amdgcn_readfirstlane((int)cdiv(seg0.end - seg0.first, 32));
-  const int n1 = __builtin_amdgcn_readfirstlane(la.ring ? (int)cdiv(seg1.end - seg1.first, 32) : 0);
+  const int n0 = __builtin_amdgcn_readfirstlane((e0 - f0 + 31) / 32);
+  const int n1 = __builtin_amdgcn_readfirstlane(la.ring ? (n + 31) / 32 : 0);
   const int ntiles = n0 + n1;
 
-  // -- buffer resources: this head's K and V in each segment, and an empty one
-  const int64_t reg0 = (int64_t)seg0.ralloc * D * 2;
-  const i32x4 dk0 = sgpr_rsrc(seg0.kreg + bg * reg0, (int)reg0);
-  const i32x4 dv0 = sgpr_rsrc(seg0.vreg + bg * reg0, (int)reg0);
-  const int64_t reg1 = la.ring ? (int64_t)seg1.ralloc * D * 2 : 0;
-  const i32x4 dk1 = la.ring ? sgpr_rsrc(seg1.kreg + bg * reg1, (int)reg1) : dk0;
-  const i32x4 dv1 = la.ring ? sgpr_rsrc(seg1.vreg + bg * reg1, (int)reg1) : dv0;
-  const i32x4 dnone = sgpr_rsrc(seg0.kreg, 0);
+  // -- buffer resources: this head's K and V in each run, and an empty one
+  const int64_t reg0 = (int64_t)la.rows_alloc * D * 2;
+  const i32x4 dk0 = sgpr_rsrc(la.k + bg * reg0, (int)reg0);
+  const i32x4 dv0 = sgpr_rsrc(la.v + bg * reg0, (int)reg0);
+  const int64_t reg1 = la.ring ? (int64_t)la.stage_rows_alloc * D * 2 : 0;
+  const i32x4 dk1 = la.ring ? sgpr_rsrc(la.sk + bg * reg1, (int)reg1) : dk0;
+  const i32x4 dv1 = la.ring ? sgpr_rsrc(la.sv + bg * reg1, (int)reg1) : dv0;
+  const i32x4 dnone = sgpr_rsrc(la.k, 0);
   // Thread tid loads chunks tid + e * NT (e < LPT) of each tile; threads
   // past a tile's chunk count (D < 128: whole waves) load nothing.
   const bool loader = wave * 64 < KCH;
@@ -2058,37 +2055,22 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   constexpr int page_b = kPageRows * D * 2;
   auto voffs = [&](int e) { return (tid + e * NT) * 16; };
   auto phalf = [&](int e) { return __builtin_amdgcn_readfirstlane(((wave * 64 + e * NT) * 16) / page_b); };
+  // First storage row of tile i (run 0, then run 1 from row 0).
+  auto tile_row = [=](int i) __attribute__((always_inline)) {
+    return i < n0 ? f0 + i * 32 : (i - n0) * 32;
+  };
 
-  // Tile i: its segment, first storage row and bounds (uniform scalars).
-  struct TileInfo {
-    int kind;
-    int64_t t0, vlo, vhi;
-  };
-  const int64_t f0 = seg0.first, lo0 = seg0.vlo, hi0 = seg0.vhi;
-  const int64_t f1 = seg1.first, lo1 = seg1.vlo, hi1 = seg1.vhi;
-  const int kind0 = seg0.kind, kind1 = seg1.kind;
-  auto tile_of = [=](int i) __attribute__((always_inline)) -> TileInfo {
-    // field by field: a select between two whole structs would go through memory
-    const bool first = i < n0;
-    TileInfo t;
-    t.kind = first ? kind0 : kind1;
-    t.t0 = first ? f0 + (int64_t)i * 32 : f1 + (int64_t)(i - n0) * 32;
-    t.vlo = first ? lo0 : lo1;
-    t.vhi = first ? hi0 : hi1;
-    return t;
-  };
   // Issue the loads of tile i (zeros and no memory access past the last
-  // tile or for threads without a chunk): one K and one V 16-byte chunk.
+  // tile or for threads without a chunk).
   auto issue = [&](int i, u32x4 (&rk)[LPT], u32x4 (&rv)[LPT]) __attribute__((always_inline)) {
     const bool live = loader && i < ntiles;
     const bool second = i >= n0;
-    const TileInfo ti = tile_of(live ? i : 0);
-    const int64_t t0 = ti.t0;
+    const int t0 = tile_row(live ? i : 0);
 #pragma unroll
     for (int e = 0; e < LPT; ++e) {
       if constexpr (PAGED) {
         // this wave's chunk e of the tile lies in the tile's page phalf(e)
-        const int idx = live ? (int)(t0 / kPageRows) + phalf(e) : 0;
+        const int idx = live ? t0 / kPageRows + phalf(e) : 0;
         const int pg = ptab[(int64_t)b * la.ppr + idx];
         const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
         const i32x4 ka = rsrc_sel(live, sgpr_rsrc(la.k + off, page_b), dnone);
@@ -2099,45 +2081,33 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
         const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
         // K rows and V blocks advance by the same bytes per row
-        const int so = __builtin_amdgcn_readfirstlane((int)(t0 * D * 2));
+        const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
         tile_load<0>(rk[e], ka, voffs(e), so);
         tile_load<0>(rv[e], va, voffs(e), so);
       }
     }
   };
-  // Write tile i's chunks (already waited for) to LDS stage s; V rows outside
-  // the segment's data are zeroed (their p is 0, and 0 times garbage could be
-  // NaN).
-  auto store = [&](int i, const u32x4 (&rka)[LPT], const u32x4 (&rva)[LPT], int s)
+  // Write tile i's chunks (already waited for) to LDS stage s.  Every V row
+  // a tile holds past its run's data is zero in memory (an append zeroes V
+  // to the end of the 32-row tile it enters, in the cache and in staging;
+  // pages are zeroed when taken), and rows before the data are real tokens,
+  // so a masked score's p = 0 multiplies a finite value.
+  auto store = [&](const u32x4 (&rka)[LPT], const u32x4 (&rva)[LPT], int s)
                    __attribute__((always_inline)) {
     if (!loader) return;
-    const TileInfo ti = tile_of(i < ntiles ? i : 0);
-    const int64_t t0 = ti.t0, vlo = ti.vlo, vhi = ti.vhi;
 #pragma unroll
     for (int e = 0; e < LPT; ++e) {
-    const u32x4 &rk = rka[e], &rv = rva[e];
-    const int c = tid + e * NT;
-    const int rr = c / (D / 8), cc = c % (D / 8);
-    *reinterpret_cast<u32x4 *>(&lk[s][rr * KSTR + cc * 8]) = rk;
-    u32x4 x = rv;
-    if (t0 < vlo || t0 + 32 > vhi) {
-      // chunk c covers rows (c / (2D)) * 16 + (c % 2) * 8 + 0..7 of the tile
-      const int64_t r0 = t0 + (c / (2 * D)) * 16 + (c % 2) * 8;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        const int64_t ra = r0 + 2 * e2, rb = ra + 1;
-        const uint32_t keep = ((ra >= vlo && ra < vhi) ? 0x0000ffffu : 0u) |
-                              ((rb >= vlo && rb < vhi) ? 0xffff0000u : 0u);
-        x[e2] &= keep;
-      }
-    }
-    // chunk c: keys 8 kh .. 8 kh + 7 of the tile's 16-row block blk at
-    // head-dim element dd; its two 4-key halves go to lane groups 2 kh and
-    // 2 kh + 1, in the block's half of each group's 8 slots
-    const int blk = c / (2 * D), dd = (c % (2 * D)) / 2, kh = c % 2;
-    bf16 *row = &lv[s][dd * VSTR + blk * 4];
-    *reinterpret_cast<uint2 *>(row + (2 * kh) * 8) = make_uint2(x[0], x[1]);
-    *reinterpret_cast<uint2 *>(row + (2 * kh + 1) * 8) = make_uint2(x[2], x[3]);
+      const int c = tid + e * NT;
+      const int rr = c / (D / 8), cc = c % (D / 8);
+      *reinterpret_cast<u32x4 *>(&lk[s][rr * KSTR + cc * 8]) = rka[e];
+      // chunk c: keys 8 kh .. 8 kh + 7 of the tile's 16-row block blk at
+      // head-dim element dd; its two 4-key halves go to lane groups 2 kh and
+      // 2 kh + 1, in the block's half of each group's 8 slots
+      const int blk = c / (2 * D), dd = (c % (2 * D)) / 2, kh = c % 2;
+      bf16 *row = &lv[s][dd * VSTR + blk * 4];
+      const u32x4 x = rva[e];
+      *reinterpret_cast<uint2 *>(row + (2 * kh) * 8) = make_uint2(x[0], x[1]);
+      *reinterpret_cast<uint2 *>(row + (2 * kh + 1) * 8) = make_uint2(x[2], x[3]);
     }
   };
 
@@ -2145,19 +2115,16 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // Reference-max slack (log2 units): p < 2^8 keeps P well inside bf16 and
   // l, O inside fp32.
   constexpr float kLazyRescale = 8.f;
-  // positions fit in 32 bits (max_len < 2^31)
-  const int Li = (int)L, pmin_i = (int)pmin, pmax_i = (int)pmax;
   const int first_i = st.first[b];  // left padding: keys before it are hidden
-  // Ring history: slot t < rr holds position t + ring_lo, slot t >= rr
-  // position t + ring_hi (rr = L mod W: the slot the next token takes), in
-  // 32-bit arithmetic once per kernel instead of per score.
-  const int ring_rr = la.ring ? (int)(L % W) : 0;
-  const int ring_lo = Li - ring_rr, ring_hi = Li - ring_rr - W;
-  // The oldest position a ring history tile [t0, t0 + 32) holds (a tile
-  // across slot rr holds position L - W, the oldest of all).
-  auto ring_min_pos = [=](int t0) __attribute__((always_inline)) {
-    return t0 + 31 < ring_rr ? t0 + ring_lo : (t0 >= ring_rr ? t0 + ring_hi : Li - W);
-  };
+  // Lowest position each query block row may see besides its own: the
+  // window's and the left padding's bound (a pad query sees only itself).
+  int qp32[2], lowq[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    qp32[blk] = (int)qpos[blk];
+    const int wl = W > 0 ? qp32[blk] - W + 1 : 0;
+    lowq[blk] = wl > first_i ? wl : first_i;
+  }
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   floatx4 oacc[2][NDB];
 #pragma unroll
@@ -2166,9 +2133,11 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     for (int db = 0; db < NDB; ++db) oacc[blk][db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int i, int s) __attribute__((always_inline)) {
-    const TileInfo ti = tile_of(i);
-    const int kind = ti.kind;
-    const int64_t t0 = ti.t0, vlo = ti.vlo, vhi = ti.vhi;
+    const bool second = i >= n0;
+    const int t0 = tile_row(i);
+    const int vlo = second ? 0 : vlo0, vhi = second ? n : vhi0;
+    const int psplit = second ? 0 : psplit0;
+    const int poa = second ? Li : pa0, pob = second ? Li : pb0;
     // S^T = K Q^T for both query blocks, each K operand read once
     floatx4 sacc[2][2];
 #pragma unroll
@@ -2191,15 +2160,14 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // every query of the q tile sees (data rows below its first position and,
     // on a windowed layer, inside its last position's window) needs no mask:
     // only the tiles at the diagonal and the edges do.
-    const int t0i = (int)t0, vloi = (int)vlo, vhii = (int)vhi;
-    // (a ring history tile: every slot holds data, and its oldest position
-    // is inside the window of the q tile's last query and past the left
-    // padding; every history position is below the q tile's first)
-    const int rmin = ring_min_pos(t0i);
-    const bool full = kind == 0 ? (t0i >= vloi && t0i + 32 <= vhii && t0i + 31 <= pmin_i &&
-                                   (W == 0 || pmax_i - t0i < W) && t0i >= first_i)
-                                : (kind == 1 && t0i + 32 <= vhii && pmax_i - rmin < W &&
-                                   rmin >= first_i && rmin >= 0);
+    // The tile's oldest and newest positions (a ring tile across psplit
+    // holds the oldest position of all at psplit and the newest just
+    // below it).
+    const bool strad = t0 < psplit && t0 + 31 >= psplit;
+    const int minpos = strad ? psplit + pob : t0 + (t0 < psplit ? poa : pob);
+    const int maxpos = strad ? psplit - 1 + poa : t0 + 31 + (t0 + 31 < psplit ? poa : pob);
+    const bool full = t0 >= vlo && t0 + 32 <= vhi && maxpos <= pmin_i &&
+                      (W == 0 || pmax_i - minpos < W) && minpos >= first_i;
     // Both blocks' masks and maxima first, then one (rarely taken) branch
     // for the accumulators' rescale, so that the exponentials and the P.V
     // products of the two blocks share one basic block and the scheduler can
@@ -2219,22 +2187,14 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     } else {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const int qp = (int)qpos[blk];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int t = t0i + kb * 16 + q4 * 4 + jj;
-            int pos;
-            if (kind == 0)
-              pos = t;
-            else if (kind == 1)
-              pos = t + (t < ring_rr ? ring_lo : ring_hi);
-            else
-              pos = Li + t;
-            bool ok = rvalid[blk] && t >= vloi && t < vhii && pos >= 0 && pos <= qp &&
-                      (pos >= first_i || pos == qp);
-            if (W > 0) ok = ok && (qp - pos < W);
+            const int t = t0 + kb * 16 + q4 * 4 + jj;
+            const int pos = t + (t < psplit ? poa : pob);
+            const bool ok = (unsigned)(t - vlo) < (unsigned)(vhi - vlo) && pos <= qp32[blk] &&
+                            (pos >= lowq[blk] || pos == qp32[blk]);
             const float x = ok ? sacc[blk][kb][jj] : -INFINITY;
             sv[blk][kb][jj] = x;
             tmax[blk] = fmaxf(tmax[blk], x);
@@ -2339,14 +2299,14 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   __builtin_amdgcn_sched_barrier(0);
   make_q();
   wait_set(rk[0], rv[0]);
-  store(0, rk[0], rv[0], 0);
+  store(rk[0], rv[0], 0);
   issue(CP, rk[0], rv[0]);
   for (int i0 = 0; i0 < ntiles; i0 += CP) {
     static_for<0, CP>([&](auto u) {
       constexpr int S = (decltype(u)::value + 1) % CP;   // set of tile i + 1
       const int i = i0 + decltype(u)::value;
       wait_set(rk[S], rv[S]);
-      store(i + 1, rk[S], rv[S], (i + 1) % NSTAGE);
+      store(rk[S], rv[S], (i + 1) % NSTAGE);
       issue(i + 1 + CP, rk[S], rv[S]);
       lds_barrier();
       if (wave_live && i < ntiles) compute(i, i % NSTAGE);
