@@ -414,6 +414,12 @@ enum { KVC_K_APPEND = 0, KVC_K_DECODE = 1, KVC_K_PREFILL = 2, KVC_K_COMBINE = 3,
 int kvc_timing_begin(kvc_t *h, int32_t max_launches);
 int kvc_timing_begin_kinds(kvc_t *h, int32_t max_launches, int32_t kind_mask);
 int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind);
+/* While timing: the first min(cap, launches so far) timed launches, in
+ * launch order: kind, start and end in ms from the first timed launch's
+ * start (waits for them).  Returns that count, or a negative status
+ * (KVC_E_STATE when timing is off).  Launches on two streams overlap; the
+ * union of their spans is the time the kernels kept the GPU busy. */
+int kvc_timing_spans(kvc_t *h, int32_t cap, int32_t *kinds, double *start_ms, double *end_ms);
 
 /* Static text for a status code; KVC_E_FULL reads "KV cache full", the
  * message of tiny_agent "generate.py" append and pycraft-1 update. */

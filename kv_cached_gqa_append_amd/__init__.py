@@ -153,6 +153,8 @@ def lib():
         L.kvc_timing_begin_kinds.restype = ctypes.c_int
         L.kvc_timing_end.argtypes = [VP, P(ctypes.c_double), P(I32)]
         L.kvc_timing_end.restype = ctypes.c_int
+        L.kvc_timing_spans.argtypes = [VP, I32, P(I32), P(ctypes.c_double), P(ctypes.c_double)]
+        L.kvc_timing_spans.restype = ctypes.c_int
         L.kvc_strerror.argtypes = [ctypes.c_int]
         L.kvc_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -374,6 +376,33 @@ def kvc_timing_begin(h, max_launches: int, kinds=None) -> None:
     for k in kinds:
         mask |= 1 << KERNEL_KINDS.index(k)
     _check(lib().kvc_timing_begin_kinds(h, int(max_launches), mask), "kvc_timing_begin_kinds")
+
+
+def kvc_timing_spans(h, cap: int):
+    """[(kind, start_ms, end_ms)] of the timed launches so far (timing on)."""
+    kinds = (ctypes.c_int32 * cap)()
+    t0 = (ctypes.c_double * cap)()
+    t1 = (ctypes.c_double * cap)()
+    n = lib().kvc_timing_spans(h, int(cap), kinds, t0, t1)
+    if n < 0:
+        _check(n, "kvc_timing_spans")
+    return [(KERNEL_KINDS[kinds[i]], float(t0[i]), float(t1[i])) for i in range(n)]
+
+
+def busy_ms(spans, kinds):
+    """Length of the union of the spans of these kinds (overlaps once)."""
+    iv = sorted((a, b) for k, a, b in spans if k in kinds)
+    total, cur_a, cur_b = 0.0, None, None
+    for a, b in iv:
+        if cur_b is None or a > cur_b:
+            if cur_b is not None:
+                total += cur_b - cur_a
+            cur_a, cur_b = a, b
+        else:
+            cur_b = max(cur_b, b)
+    if cur_b is not None:
+        total += cur_b - cur_a
+    return total
 
 
 def kvc_timing_end(h):

@@ -2458,6 +2458,24 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
 
 bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && rep >= 1; }
 
+template <int D, int REP, int QW>
+static int chunk_wgs_t() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_chunk<D, REP, false, QW>, QW * 64, 0) !=
+      hipSuccess)
+    return 0;
+  return n;
+}
+
+int chunk_wgs_per_cu(int D, int rep, int qw) {
+#define KVC_OCC(DD, RR)                                                              \
+  if (D == DD && rep == RR) return qw == 4 ? chunk_wgs_t<DD, RR, 4>() : chunk_wgs_t<DD, RR, 8>();
+  KVC_OCC(128, 1) KVC_OCC(128, 2) KVC_OCC(128, 4) KVC_OCC(128, 8) KVC_OCC(128, 16)
+  KVC_OCC(64, 1) KVC_OCC(64, 2) KVC_OCC(64, 4) KVC_OCC(64, 8) KVC_OCC(64, 16)
+#undef KVC_OCC
+  return 0;
+}
+
 template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, int qw, const Launch &lc) {

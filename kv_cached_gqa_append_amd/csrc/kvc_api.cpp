@@ -47,6 +47,8 @@ struct kvc_cache {
   // query heads per KV head (0 = not yet queried), and overrides
   int32_t n_cu = 0;
   int32_t dec_occ[17] = {0};
+  // chunk workgroups per CU, 8-wave and 4-wave, by query heads per KV head (0 = not queried)
+  int32_t chunk_occ[17][2] = {{0}};
   int32_t dec_split_fixed = 0;    // keys per split (multiple of 16); 0 = planned
   int32_t dec_waves_target = 0;   // waves per decode launch; 0 = resident slots
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
@@ -911,8 +913,8 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
         if (wg8 > 0 && wg8 < h->n_cu) pa->chunk_small = 2;
       }
       // Chunk split length.  Each launch (8-wave and 4-wave workgroups) is
-      // priced as a list schedule over its resident slots (two 8-wave or four
-      // 4-wave workgroups per CU): the larger of its total work over the
+      // priced as a list schedule over its resident slots (the workgroups of
+      // each kind a CU holds at once, from the occupancy query): the larger of its total work over the
       // slots and its longest item, where an item costs its keys plus a fixed
       // kChunkSplitCost (staging the query tile, writing and merging a
       // partial).  The split count per row (1 .. ccap, never under
@@ -921,7 +923,10 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
       // the cap; rows of mixed lengths, whose longest item sets the time,
       // keep the cap.
       {
-        const int64_t slots8 = 2 * (int64_t)h->n_cu, slots4 = 4 * (int64_t)h->n_cu;
+        int32_t *occ = h->chunk_occ[lx.rep <= 16 ? lx.rep : 0];
+        if (occ[0] == 0) occ[0] = std::max(1, kvc::chunk_wgs_per_cu(D, lx.rep, 8));
+        if (occ[1] == 0) occ[1] = std::max(1, kvc::chunk_wgs_per_cu(D, lx.rep, 4));
+        const int64_t slots8 = occ[0] * (int64_t)h->n_cu, slots4 = occ[1] * (int64_t)h->n_cu;
         auto cost = [&](int64_t sk) {
           int64_t sum8 = 0, sum4 = 0, top8 = 0, top4 = 0;
           for (int32_t b = 0; b < B; ++b) {
@@ -1296,6 +1301,23 @@ int kvc_timing_begin_kinds(kvc_t *h, int32_t max_launches, int32_t kind_mask) {
   h->ev_mask = kind_mask;
   h->timing = true;
   return KVC_OK;
+}
+
+int kvc_timing_spans(kvc_t *h, int32_t cap, int32_t *kinds, double *start_ms, double *end_ms) {
+  if (!h || cap < 0 || (cap > 0 && (!kinds || !start_ms || !end_ms))) return KVC_E_ARG;
+  if (!h->timing) return KVC_E_STATE;
+  const int32_t n = std::min(cap, h->ev_used);
+  for (int32_t i = 0; i < n; ++i) {
+    float a = 0.f, b = 0.f;
+    if (hipEventSynchronize(h->ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&a, h->ev[0], h->ev[2 * i]) != hipSuccess ||
+        hipEventElapsedTime(&b, h->ev[0], h->ev[2 * i + 1]) != hipSuccess)
+      return KVC_E_HIP;
+    kinds[i] = h->ev_kind[i];
+    start_ms[i] = a;
+    end_ms[i] = b;
+  }
+  return n;
 }
 
 int kvc_timing_end(kvc_t *h, double *ms_per_kind, int32_t *launches_per_kind) {

@@ -255,5 +255,7 @@ bool fast_decode_supported(int D, int rep);
 // Decode workgroups (one wave each) resident per compute unit; 0 on error.
 int decode_waves_per_cu(int D, int rep);
 bool fast_prefill_supported(int D, int rep);
+// Chunk-attention workgroups of qw waves resident per compute unit; 0 on error.
+int chunk_wgs_per_cu(int D, int rep, int qw);
 
 }  // namespace kvc

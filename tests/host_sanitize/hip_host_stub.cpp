@@ -357,5 +357,6 @@ bool fast_decode_supported(int D, int rep) {
 }
 int decode_waves_per_cu(int D, int rep) { return fast_decode_supported(D, rep) ? 8 : 0; }
 bool fast_prefill_supported(int D, int rep) { return (D == 64 || D == 128) && rep >= 1; }
+int chunk_wgs_per_cu(int D, int rep, int qw) { return fast_prefill_supported(D, rep) ? (qw == 4 ? 2 : 1) : 0; }
 
 }  // namespace kvc

@@ -239,7 +239,13 @@ void exercise(Cfg &cfg, int steps, unsigned seed, bool chunks) {
     r.step(n, 1, g);
     double ms[KVC_K_NKINDS];
     int32_t cnt[KVC_K_NKINDS];
+    int32_t kinds[8];
+    double t0[8], t1[8];
+    const int ns = kvc_timing_spans(r.h, 8, kinds, t0, t1);
+    CHECK(ns >= 1 && ns <= 8);
+    for (int i = 0; i < ns; ++i) CHECK(kinds[i] >= 0 && kinds[i] < KVC_K_NKINDS && t1[i] >= t0[i]);
     CHECK(kvc_timing_end(r.h, ms, cnt) == KVC_OK);
+    CHECK(kvc_timing_spans(r.h, 8, kinds, t0, t1) == KVC_E_STATE);
     CHECK(kvc_timing_end(r.h, ms, cnt) == KVC_E_STATE);
     r.check_lens();
   }

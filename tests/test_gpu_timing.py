@@ -26,9 +26,17 @@ def test_timing_counts_only_the_chosen_kinds():
     assert all(v[1] == 0 for k, v in t.items() if k != "decode"), t
     K.kvc_timing_begin(h, 64)
     pair.step(n, 1)
+    spans = K.kvc_timing_spans(h, 64)
     t = K.kvc_timing_end(h)
     for kind in ("append", "decode", "combine"):
         assert t[kind][1] == work.n_layer, (kind, t)
+    # spans: one per timed launch, in launch order on one stream, so they do
+    # not overlap and their union equals the summed kernel time
+    assert len(spans) == sum(v[1] for v in t.values())
+    assert all(b >= a >= 0.0 for _, a, b in spans)
+    assert all(spans[i][1] >= spans[i - 1][2] - 1e-3 for i in range(1, len(spans)))
+    tot = sum(v[0] for v in t.values())
+    assert abs(K.busy_ms(spans, set(K.KERNEL_KINDS)) - tot) <= 1e-3 * len(spans) + 1e-6 * tot
     with pytest.raises(ValueError):  # a bit past the last kind: KVC_E_ARG
         K._check(K.lib().kvc_timing_begin_kinds(h, 8, 1 << len(K.KERNEL_KINDS)),
                  "kvc_timing_begin_kinds")
