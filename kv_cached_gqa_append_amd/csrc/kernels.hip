@@ -959,6 +959,27 @@ __device__ __forceinline__ void tile_load(u32x4 &x, i32x4 rsrc, int voff, int so
                : "=v"(x)
                : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF));
 }
+// A load of 64 16-byte chunks straight into LDS: lane L's chunk (at voff +
+// soff of the buffer) lands at LDS byte m0 + 16 L.  The compiler does not
+// see the LDS write, so the waits for it are placed by hand (lds_wait) and
+// an LDS read of the data follows a barrier.  Non-temporal like the tile
+// loads.
+// (m0 is the compiler's: its value is kept in a scratch register around
+// the load.)
+__device__ __forceinline__ void lds_load(uint32_t m0, int voff, i32x4 rsrc, int soff) {
+  int keep;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\t"
+               "buffer_load_dwordx4 %2, %3, %4 offen nt lds ; lds slab load\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(keep)
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0) ; lds slab wait" : : "n"(N) : "memory");
+}
 // Wait until at most N tile loads are outstanding (loads complete in order).
 template <int N>
 __device__ __forceinline__ void tile_wait(u32x4 &x) {
@@ -1870,24 +1891,26 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
                                                    const int32_t *__restrict__ ptab) {
   constexpr int NDS = D / 32;              // 32-wide d steps (QK contraction)
   constexpr int NDB = D / 16;              // 16-wide d blocks (PV output)
-  constexpr int KSTR = D + 8;              // padded K row in LDS (elements)
+  constexpr int CPR = D / 8;               // 16-byte chunks of a K row
   constexpr int KCH = 32 * D / 8;          // 16-byte chunks of a K tile (= of a V tile)
   constexpr int NT = QW * 64;              // threads
   constexpr int QT = QW * 32;              // query rows per workgroup
-  constexpr int LPT = KCH > NT ? KCH / NT : 1;  // K (and V) chunks per thread per tile
-  constexpr int NSTAGE = 3;
-  // Tiles in flight per thread (LPT K and LPT V 16-byte chunks each): the
-  // workgroup's own loads must cover the memory latency.
-  constexpr int CP = (D >= 128 ? 6 : 8) / LPT;
-  static_assert(KCH <= NT * LPT && CP >= 2, "chunk mapping");
-  __shared__ __align__(16) bf16 lk[NSTAGE][32 * KSTR];
-  // V^T of a tile: row d holds the 32 keys in the order the PV operand of
-  // lane group q4 takes them (keys 4q4..4q4+3, then 16+4q4..16+4q4+3), so an
-  // operand is one 16-byte read; rows padded to 40 keys so that the reads of
-  // 8 consecutive d fall in distinct banks.
-  constexpr int VSTR = 40;
-  __shared__ __align__(16) bf16 lv[NSTAGE][D * VSTR];
-
+  // Tiles go from memory straight to LDS (buffer loads with the lds bit):
+  // one load instruction fills a 1 KB slab of 64 chunks, lane L writing
+  // chunk L.  A tile is NSL slabs (K, then V), each wave loading SPW of them.
+  constexpr int NSL = 2 * KCH / 64;
+  constexpr int SPW = NSL / QW;
+  // LDS stages: NSTAGE - 1 tiles are in flight while one is computed.  The
+  // eight-wave workgroup is alone on its CU; two four-wave ones share one.
+  constexpr int NSTAGE = QW == 8 ? 8 : 4;
+  constexpr int STAGE_B = 2 * KCH * 16;    // bytes of a stage: K, then V
+  static_assert(SPW >= 1 && NSL % QW == 0, "chunk mapping");
+  // Stage layout.  K: 32 rows of CPR chunks, chunk c of row r at position
+  // r * CPR + (c ^ swz(r)): the 16 rows an operand read takes (see qk) land
+  // in distinct banks.  V: the cache's own layout, two 16-row blocks of
+  // [d][16 keys], chunk (d, half) of a block at position 2 d + (half ^ bit 3
+  // of d): the 16 d of an operand read land in distinct banks.
+  __shared__ __align__(16) char ltile[NSTAGE][STAGE_B];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int q4 = lane >> 4, nl = lane & 15;
@@ -2046,68 +2069,61 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const i32x4 dk1 = la.ring ? sgpr_rsrc(la.sk + bg * reg1, (int)reg1) : dk0;
   const i32x4 dv1 = la.ring ? sgpr_rsrc(la.sv + bg * reg1, (int)reg1) : dv0;
   const i32x4 dnone = sgpr_rsrc(la.k, 0);
-  // Thread tid loads chunks tid + e * NT (e < LPT) of each tile; threads
-  // past a tile's chunk count (D < 128: whole waves) load nothing.
-  const bool loader = wave * 64 < KCH;
-  // paged: bytes of one head's page, the page of the tile a wave's chunk e
-  // falls in (K row c / (D / 8) and V block c / (2 D) agree; 64 chunks never
-  // straddle a page), and the chunk's offset inside it
+  // This wave's slabs: j = wave + QW e (e < SPW); slab j < KCH / 64 holds K
+  // chunks, the rest V chunks.  Per lane: the byte offset of the chunk it
+  // fetches within the tile, and the slab's byte offset within a stage.
+  constexpr int KSL = KCH / 64;            // K slabs per tile
+  int soff_lane[SPW];                      // source offset within the tile (bytes)
+#pragma unroll
+  for (int e = 0; e < SPW; ++e) {
+    const int j = wave + QW * e;
+    const int pos = (j < KSL ? j : j - KSL) * 64 + lane;  // chunk position in the LDS region
+    if (j < KSL) {
+      const int r = pos / CPR, pc = pos % CPR;
+      const int swz = ((r & 3) | (((r >> 3) & 3) << 2)) & (CPR - 1);
+      soff_lane[e] = (r * CPR + (pc ^ swz)) * 16;
+    } else {
+      const int blk = pos / (2 * D), qq = pos % (2 * D), d = qq >> 1;
+      soff_lane[e] = (blk * 2 * D + (qq ^ ((d >> 3) & 1))) * 16;
+    }
+  }
+  // paged: the 16-row page of slab j within a tile (a slab is 64 chunks: K
+  // rows of one page, or part of one V block), the same for every lane
+  auto slab_page = [](int j) __attribute__((always_inline)) {
+    return j < KSL ? (j * 64 / CPR) / kPageRows : ((j - KSL) * 64) / (2 * D);
+  };
+  // paged: bytes of one head's page (16 K rows, or one V block)
   constexpr int page_b = kPageRows * D * 2;
-  auto voffs = [&](int e) { return (tid + e * NT) * 16; };
-  auto phalf = [&](int e) { return __builtin_amdgcn_readfirstlane(((wave * 64 + e * NT) * 16) / page_b); };
   // First storage row of tile i (run 0, then run 1 from row 0).
   auto tile_row = [=](int i) __attribute__((always_inline)) {
     return i < n0 ? f0 + i * 32 : (i - n0) * 32;
   };
-
-  // Issue the loads of tile i (zeros and no memory access past the last
-  // tile or for threads without a chunk).
-  auto issue = [&](int i, u32x4 (&rk)[LPT], u32x4 (&rv)[LPT]) __attribute__((always_inline)) {
-    const bool live = loader && i < ntiles;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&ltile[0][0];
+  // Issue the loads of tile i into stage st_ (zeros and no memory access
+  // past the last tile).
+  auto issue = [&](int i, int st_) __attribute__((always_inline)) {
+    const bool live = i < ntiles;
     const bool second = i >= n0;
     const int t0 = tile_row(live ? i : 0);
 #pragma unroll
-    for (int e = 0; e < LPT; ++e) {
+    for (int e = 0; e < SPW; ++e) {
+      const int j = wave + QW * e;
+      const bool isv = j >= KSL;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(
+          lds0 + st_ * STAGE_B + (isv ? KCH * 16 + (j - KSL) * 1024 : j * 1024));
       if constexpr (PAGED) {
-        // this wave's chunk e of the tile lies in the tile's page phalf(e)
-        const int idx = live ? t0 / kPageRows + phalf(e) : 0;
+        // a slab lies in one page: K rows of one block, or one V block
+        const int sp = slab_page(j);
+        const int idx = live ? t0 / kPageRows + sp : 0;
         const int pg = ptab[(int64_t)b * la.ppr + idx];
         const int64_t off = ((int64_t)pg * la.hkv + g) * page_b;
-        const i32x4 ka = rsrc_sel(live, sgpr_rsrc(la.k + off, page_b), dnone);
-        const i32x4 va = rsrc_sel(live, sgpr_rsrc(la.v + off, page_b), dnone);
-        tile_load<0>(rk[e], ka, voffs(e) % page_b, 0);
-        tile_load<0>(rv[e], va, voffs(e) % page_b, 0);
+        const i32x4 rs = rsrc_sel(live, sgpr_rsrc((isv ? la.v : la.k) + off, page_b), dnone);
+        lds_load(m0, soff_lane[e] - sp * page_b, rs, 0);
       } else {
-        const i32x4 ka = rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
-        const i32x4 va = rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
+        const i32x4 rs = rsrc_sel(live, isv ? rsrc_sel(second, dv1, dv0) : rsrc_sel(second, dk1, dk0), dnone);
         // K rows and V blocks advance by the same bytes per row
-        const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
-        tile_load<0>(rk[e], ka, voffs(e), so);
-        tile_load<0>(rv[e], va, voffs(e), so);
+        lds_load(m0, soff_lane[e], rs, __builtin_amdgcn_readfirstlane(t0 * D * 2));
       }
-    }
-  };
-  // Write tile i's chunks (already waited for) to LDS stage s.  Every V row
-  // a tile holds past its run's data is zero in memory (an append zeroes V
-  // to the end of the 32-row tile it enters, in the cache and in staging;
-  // pages are zeroed when taken), and rows before the data are real tokens,
-  // so a masked score's p = 0 multiplies a finite value.
-  auto store = [&](const u32x4 (&rka)[LPT], const u32x4 (&rva)[LPT], int s)
-                   __attribute__((always_inline)) {
-    if (!loader) return;
-#pragma unroll
-    for (int e = 0; e < LPT; ++e) {
-      const int c = tid + e * NT;
-      const int rr = c / (D / 8), cc = c % (D / 8);
-      *reinterpret_cast<u32x4 *>(&lk[s][rr * KSTR + cc * 8]) = rka[e];
-      // chunk c: keys 8 kh .. 8 kh + 7 of the tile's 16-row block blk at
-      // head-dim element dd; its two 4-key halves go to lane groups 2 kh and
-      // 2 kh + 1, in the block's half of each group's 8 slots
-      const int blk = c / (2 * D), dd = (c % (2 * D)) / 2, kh = c % 2;
-      bf16 *row = &lv[s][dd * VSTR + blk * 4];
-      const u32x4 x = rva[e];
-      *reinterpret_cast<uint2 *>(row + (2 * kh) * 8) = make_uint2(x[0], x[1]);
-      *reinterpret_cast<uint2 *>(row + (2 * kh + 1) * 8) = make_uint2(x[2], x[3]);
     }
   };
 
@@ -2148,15 +2164,20 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t *>(&lk[s][(kb * 16 + nl) * KSTR + ds * 32 + q4 * 8]);
+        // A row i of this product is key 8 (i / 4) + 4 kb + i % 4, so lane
+        // (q4, nl) ends with keys 8 q4 .. 8 q4 + 7 of the tile, the P^T
+        // operand order of P.V
+        const int r = 8 * (nl >> 2) + 4 * kb + (nl & 3), c = ds * 4 + q4;
+        const int swz = ((r & 3) | (((r >> 3) & 3) << 2)) & (CPR - 1);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
+            &ltile[s][(r * CPR + (c ^ swz)) * 16]);
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
           sacc[blk][kb] =
               __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[blk][ds], sacc[blk][kb], 0, 0, 0);
       }
     // mask + scale + online softmax per block; sacc[blk][kb][jj] is key row
-    // t0 + kb*16 + 4*q4 + jj, query row nl of the block.  A tile whose keys
+    // t0 + 8 q4 + 4 kb + jj, query row nl of the block.  A tile whose keys
     // every query of the q tile sees (data rows below its first position and,
     // on a windowed layer, inside its last position's window) needs no mask:
     // only the tiles at the diagonal and the edges do.
@@ -2191,7 +2212,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            const int t = t0 + kb * 16 + q4 * 4 + jj;
+            const int t = t0 + 8 * q4 + 4 * kb + jj;
             const int pos = t + (t < psplit ? poa : pob);
             const bool ok = (unsigned)(t - vlo) < (unsigned)(vhi - vlo) && pos <= qp32[blk] &&
                             (pos >= lowq[blk] || pos == qp32[blk]);
@@ -2224,13 +2245,17 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha[blk];
     }
-    // O^T += V^T P^T; k-slot 8*q4 + e <-> key (e < 4 ? 4*q4 + e : 16 + 4*q4 + e - 4);
-    // each V operand (head-dim row db * 16 + nl) serves both blocks
+    // O^T += V^T P^T; k-slot 8 q4 + e <-> key 8 q4 + e: 16 bytes of block
+    // q4 / 2 at (d, half q4 % 2).  Each V operand (head-dim row db * 16 + nl)
+    // serves both blocks.
     bf16x8_t pf[2];
     uint4 av[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      av[db] = *reinterpret_cast<const uint4 *>(&lv[s][(db * 16 + nl) * VSTR + q4 * 8]);
+    for (int db = 0; db < NDB; ++db) {
+      const int d = db * 16 + nl, qq = 2 * d + (q4 & 1);
+      av[db] = *reinterpret_cast<const uint4 *>(
+          &ltile[s][KCH * 16 + ((q4 >> 1) * 2 * D + (qq ^ ((d >> 3) & 1))) * 16]);
+    }
     auto probs = [&](int blk) __attribute__((always_inline)) {
       float ps = 0.f;
 #pragma unroll
@@ -2269,58 +2294,27 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);     // MFMA
   };
 
-  // LDS stores of a tile complete, then every wave meets: the tile is
-  // published (global loads stay in flight: no vmcnt wait here).
-  auto lds_barrier = []() __attribute__((always_inline)) { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
-
-  // Pipeline, P = CP register sets: at step i, tile i + 1 (set (i + 1) % P)
-  // is waited for and written to LDS stage (i + 1) % 3, tile i + 1 + P is
-  // issued into the same set, one barrier publishes the stage, and tile i is
-  // computed from stage i % 3; tiles i + 2 .. i + 1 + P stay in flight (a
-  // stage is rewritten two steps after it was last read, behind a barrier).
-  // Steps run in groups of P so set indices are compile-time; the last group
-  // is padded with empty steps, so every path keeps the same loads in flight.
-  // The queries' loads above are older than every tile load, so the tile
-  // waits retire them too.
-  // (a set's loads retire together: waiting for its first register while
-  // the later sets' 2 LPT (P - 1) loads stay outstanding covers all of it)
-  constexpr int AFTER = 2 * LPT * (CP - 1);
-  auto wait_set = [&](u32x4 (&rka)[LPT], u32x4 (&rva)[LPT]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int e = 0; e < LPT; ++e) {
-      tile_wait<AFTER>(rka[e]);
-      tile_wait<AFTER>(rva[e]);
-    }
-  };
-  u32x4 rk[CP][LPT], rv[CP][LPT];
-  static_for<0, CP>([&](auto t) { issue(decltype(t)::value, rk[decltype(t)::value], rv[decltype(t)::value]); });
+  // Pipeline: tiles 0 .. NSTAGE - 2 go out first, into stages 0 .. NSTAGE -
+  // 2.  Step i: this wave waits for its own loads of tile i (the NSTAGE - 2
+  // tiles issued after it stay in flight), every wave meets at the barrier
+  // (tile i is then in LDS, and every wave is done with tile i - 1), tile
+  // i + NSTAGE - 1 goes out into the stage tile i - 1 used, and tile i is
+  // computed.  Loads past the last tile read nothing and write zeros.  The
+  // queries' loads above are older than every tile load, so the tile waits
+  // retire them too.
+  for (int t = 0; t < NSTAGE - 1; ++t) issue(t, t);
   // Nothing below moves above the tile loads: the queries are rotated while
   // the first tiles are in flight.
   __builtin_amdgcn_sched_barrier(0);
   make_q();
-  wait_set(rk[0], rv[0]);
-  store(rk[0], rv[0], 0);
-  issue(CP, rk[0], rv[0]);
-  for (int i0 = 0; i0 < ntiles; i0 += CP) {
-    static_for<0, CP>([&](auto u) {
-      constexpr int S = (decltype(u)::value + 1) % CP;   // set of tile i + 1
-      const int i = i0 + decltype(u)::value;
-      wait_set(rk[S], rv[S]);
-      store(rk[S], rv[S], (i + 1) % NSTAGE);
-      issue(i + 1 + CP, rk[S], rv[S]);
-      lds_barrier();
-      if (wave_live && i < ntiles) compute(i, i % NSTAGE);
-    });
+  for (int i = 0; i < ntiles; ++i) {
+    lds_wait<SPW * (NSTAGE - 2)>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    issue(i + NSTAGE - 1, (i + NSTAGE - 1) % NSTAGE);
+    if (wave_live) compute(i, i % NSTAGE);
   }
-  // Retire the loads still in flight before their registers go away.
-  static_for<0, CP>([&](auto t) {
-#pragma unroll
-    for (int e = 0; e < LPT; ++e) {
-      tile_wait<0>(rk[decltype(t)::value][e]);
-      tile_wait<0>(rv[decltype(t)::value][e]);
-    }
-  });
-  asm volatile("" ::: "memory");
+  // the loads of tiles past the end land before the LDS is released
+  lds_wait<0>();
 
   // -- partials for this split (over a joint partner's keys: after the
   // layer's own splits) ------------------------------------------------------------
@@ -2386,71 +2380,61 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __syncthreads();
     if (commit_last) {
       const int i0 = n > W ? n - W : 0;  // first kept staged row
-      constexpr int CU = 4;  // copies per thread in flight
+      // Copies of n_items 16-byte chunks, four per thread in flight: every
+      // load is issued (past the end the last chunk again) before the stores.
+      auto copy4 = [&](int n_items, auto src_of, auto dst_of) __attribute__((always_inline)) {
+        for (int c0 = tid; c0 < n_items; c0 += 4 * NT) {
+          const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
+          const uint4 x0 = *src_of(c0);
+          const uint4 x1 = *src_of(c1 < n_items ? c1 : n_items - 1);
+          const uint4 x2 = *src_of(c2 < n_items ? c2 : n_items - 1);
+          const uint4 x3 = *src_of(c3 < n_items ? c3 : n_items - 1);
+          *dst_of(c0) = x0;
+          if (c1 < n_items) *dst_of(c1) = x1;
+          if (c2 < n_items) *dst_of(c2) = x2;
+          if (c3 < n_items) *dst_of(c3) = x3;
+        }
+      };
       // K: row-major on both sides, 16-byte chunks
       constexpr int KC = D / 8;
-      const int nkc = (n - i0) * KC;
-      for (int c0 = tid; c0 < nkc; c0 += CU * NT) {
-        uint4 x[CU];
-#pragma unroll
-        for (int u = 0; u < CU; ++u) {
-          const int c = c0 + u * NT;
-          if (c < nkc)
-            x[u] = *reinterpret_cast<const uint4 *>(
+      copy4(
+          (n - i0) * KC,
+          [&](int c) {
+            return reinterpret_cast<const uint4 *>(
                 k_row<bf16>(la.sk, bg, la.stage_rows_alloc, i0 + c / KC, D) + (c % KC) * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < CU; ++u) {
-          const int c = c0 + u * NT;
-          if (c < nkc)
-            *reinterpret_cast<uint4 *>(
-                k_row<bf16>(la.k, bg, la.rows_alloc, (L + i0 + c / KC) % W, D) + (c % KC) * 8) = x[u];
-        }
-      }
+          },
+          [&](int c) {
+            return reinterpret_cast<uint4 *>(
+                k_row<bf16>(la.k, bg, la.rows_alloc, (Li + i0 + c / KC) % W, D) + (c % KC) * 8);
+          });
       // V: 16-row blocks stored transposed on both sides.  When the kept rows
       // start a block on both sides (and W is whole blocks), each whole block
       // is one contiguous run of D x 16 elements; the rest goes element by
       // element.
       int iv = i0;
-      if ((L + i0) % kVBlock == 0 && i0 % kVBlock == 0 && W % kVBlock == 0) {
+      if ((Li + i0) % kVBlock == 0 && i0 % kVBlock == 0 && W % kVBlock == 0) {
         constexpr int BC = D * kVBlock / 8;  // 16-byte chunks per block
         const int nb = (n - i0) / kVBlock;
-        for (int c0 = tid; c0 < nb * BC; c0 += CU * NT) {
-          uint4 x[CU];
-#pragma unroll
-          for (int u = 0; u < CU; ++u) {
-            const int c = c0 + u * NT;
-            if (c < nb * BC)
-              x[u] = *reinterpret_cast<const uint4 *>(
+        copy4(
+            nb * BC,
+            [&](int c) {
+              return reinterpret_cast<const uint4 *>(
                   v_block<bf16>(la.sv, bg, la.stage_rows_alloc, i0 / kVBlock + c / BC, D) +
                   (c % BC) * 8);
-          }
-#pragma unroll
-          for (int u = 0; u < CU; ++u) {
-            const int c = c0 + u * NT;
-            if (c < nb * BC)
-              *reinterpret_cast<uint4 *>(
+            },
+            [&](int c) {
+              return reinterpret_cast<uint4 *>(
                   v_block<bf16>(la.v, bg, la.rows_alloc,
-                                ((L + i0) / kVBlock + c / BC) % (W / kVBlock), D) +
-                  (c % BC) * 8) = x[u];
-          }
-        }
+                                ((Li + i0) / kVBlock + c / BC) % (W / kVBlock), D) +
+                  (c % BC) * 8);
+            });
         iv = i0 + nb * kVBlock;
       }
+      // (the rest: rows that do not start a block, element by element)
       const int nv = (n - iv) * D;
-      for (int e0 = tid; e0 < nv; e0 += 8 * NT) {
-        bf16 x[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * NT;
-          if (e < nv) x[u] = *v_elem<bf16>(la.sv, bg, la.stage_rows_alloc, iv + e / D, e % D, D);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int e = e0 + u * NT;
-          if (e < nv) *v_elem<bf16>(la.v, bg, la.rows_alloc, (L + iv + e / D) % W, e % D, D) = x[u];
-        }
-      }
+      for (int e = tid; e < nv; e += NT)
+        *v_elem<bf16>(la.v, bg, la.rows_alloc, (Li + iv + e / D) % W, e % D, D) =
+            *v_elem<bf16>(la.sv, bg, la.stage_rows_alloc, iv + e / D, e % D, D);
       if (tid == 0) __hip_atomic_store(pa.ring_cnt + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
