@@ -132,10 +132,10 @@ def timed_decode_bytes(work, steps, warmup, fused=False):
 
 def _kname(name):
     for k in ("k_decode", "k_combine", "k_append", "k_chunk", "k_advance", "k_commit",
-              "k_set_rows", "k_generic"):
+              "k_set_rows", "k_generic", "k_static_begin"):
         if k in name:
             return k
-    return name
+    return name if len(name) <= 40 else name[:37] + "..."
 
 
 def summarize_trace(trace_csv, steps, warmup, layers, fused=False):
@@ -248,6 +248,186 @@ def summarize_mfma(csv_path, chunks, chunk=64):
     return "\n".join(out)
 
 
+def _union_us(iv):
+    """Length of the union of (start, end) nanosecond intervals, in us."""
+    tot, cs, ce = 0, None, None
+    for a, b in sorted(iv):
+        if ce is None or a > ce:
+            if ce is not None:
+                tot += ce - cs
+            cs, ce = a, b
+        else:
+            ce = max(ce, b)
+    if ce is not None:
+        tot += ce - cs
+    return tot / 1e3
+
+
+def _csv_steps(path, order="Start_Timestamp", counter=None):
+    """The dispatches of a rocprofv3 csv (kernel trace, or one counter of a
+    --pmc run), cut into protocol steps: each step ends with its k_advance.
+    A dispatch is (kind, start ns, end ns, counter value)."""
+    rows = [r for r in csv.DictReader(open(path))
+            if counter is None or r.get("Counter_Name") == counter]
+    rows.sort(key=lambda r: int(r[order]))
+    steps, cur = [], []
+    for r in rows:
+        cur.append((_kname(r["Kernel_Name"]), int(r["Start_Timestamp"]),
+                    int(r["End_Timestamp"]), float(r.get("Counter_Value") or 0.0)))
+        if cur[-1][0] == "k_advance":
+            steps.append(cur)
+            cur = []
+    return steps, cur
+
+
+def _split_layers(step):
+    """The dispatches of one unfused step, per layer: each layer starts at its
+    k_append (what precedes the first one, the step's count upload, and the
+    closing k_advance are left out)."""
+    layers = []
+    for d in step:
+        if d[0] == "k_append":
+            layers.append([])
+        if layers and d[0] != "k_advance":
+            layers[-1].append(d)
+    return layers
+
+
+def _kind_table(dispatches, n_steps):
+    out = ["| kernel | dispatches | summed us | union of spans us | avg us | per step us |",
+           "|---|---|---|---|---|---|"]
+    by = {}
+    for d in dispatches:
+        by.setdefault(d[0], []).append(d)
+    for k, v in sorted(by.items(), key=lambda kv: -sum(d[2] - d[1] for d in kv[1])):
+        tot = sum(d[2] - d[1] for d in v) / 1e3
+        out.append(f"| {k} | {len(v)} | {tot:.1f} | {_union_us([(d[1], d[2]) for d in v]):.1f} | "
+                   f"{tot / len(v):.2f} | {tot / n_steps:.1f} |")
+    return out
+
+
+def _layer_table(steps, window):
+    """Per layer kind (global / sliding ring): mean span of a layer (first
+    dispatch start to last dispatch end), mean time its kernels kept the GPU
+    busy (union of spans) and the mean per kernel kind."""
+    per = {"global": {"span": [], "busy": [], "kinds": {}},
+           "ring": {"span": [], "busy": [], "kinds": {}}}
+    for st in steps:
+        for l, lay in enumerate(_split_layers(st)):
+            p = per["global" if window[l] == 0 else "ring"]
+            p["span"].append((max(d[2] for d in lay) - min(d[1] for d in lay)) / 1e3)
+            p["busy"].append(_union_us([(d[1], d[2]) for d in lay]))
+            for d in lay:
+                p["kinds"].setdefault(d[0], []).append((d[2] - d[1]) / 1e3)
+    out = ["| layer kind | layers timed | span us (mean) | busy us (mean) | per-kind avg us |",
+           "|---|---|---|---|---|"]
+    for k, p in per.items():
+        if not p["span"]:
+            continue
+        kinds = ", ".join(f"{n} {np.mean(v):.2f} x{len(v) / len(p['span']):.2g}"
+                          for n, v in sorted(p["kinds"].items()))
+        out.append(f"| {k} | {len(p['span'])} | {np.mean(p['span']):.2f} | "
+                   f"{np.mean(p['busy']):.2f} | {kinds} |")
+    return out
+
+
+def _periods(steps):
+    """Advance-end to advance-end periods of consecutive steps, in ms."""
+    ends = [st[-1][2] for st in steps]
+    return np.diff(np.asarray(ends, dtype=np.int64)) / 1e6
+
+
+def summarize_legs(trace_csv, only, steps, mixed_layers):
+    """Markdown summary of a rocprofv3 kernel trace of `bench.py --only mixed`
+    or `--only long_decode`: the steps are cut at each k_advance and the legs
+    located by their step counts (the history fill, then the legs' warmup,
+    timed and per-layer steps in the order the leg runs them)."""
+    all_steps, _ = _csv_steps(trace_csv)
+    out = [f"{len(all_steps)} protocol steps in the trace", ""]
+    if only == "mixed":
+        timed = all_steps[-steps:]
+        per = _periods(all_steps[-steps - 1:])
+        disp = [d for st in timed for d in st]
+        att = [d for d in disp if d[0] in ("k_decode", "k_chunk", "k_combine")]
+        out += [f"## Timed steps: the last {steps} ({mixed_layers} layers each)", "",
+                f"step period (advance to advance): {per.mean():.3f} ms mean", "",
+                f"attention kernels (decode, chunk, combine): union of spans "
+                f"{_union_us([(d[1], d[2]) for d in att]) / 1e3:.3f} ms, summed "
+                f"{sum(d[2] - d[1] for d in att) / 1e6:.3f} ms over {steps} steps", ""]
+        out += _kind_table(disp, steps)
+        return "\n".join(out)
+    work = wl.LONG_5TO1
+    win, W, S, C4 = work.window, 4, steps, 4
+    fill = len(wl.fill_plan(np.full(work.batch, 510 * 64), 64))
+    legs = [("prefill: 510 chunk steps of 64 (kvc_append + kvc_attend)", 0, fill, True)]
+    o = fill + W
+    legs.append(("decode, kvc_append + kvc_attend (timed steps)", o, o + S, True))
+    o += S + C4 + W
+    legs.append(("decode, kvc_append_attend (timed steps)", o, o + S, False))
+    o += S + C4 + W
+    legs.append(("decode, replays of the captured static step (timed steps)", o, o + S, False))
+    for title, a, b, unfused in legs:
+        sel = all_steps[a:b]
+        if len(sel) != b - a:
+            out += [f"## {title}: trace holds {len(sel)} of its {b - a} steps", ""]
+            continue
+        per = _periods(all_steps[max(a - 1, 0):b])
+        out += [f"## {title}", "", f"steps {a}..{b - 1} of the trace; step period (advance to "
+                f"advance) {per.mean():.3f} ms mean, {np.median(per):.3f} ms median", ""]
+        out += _kind_table([d for st in sel for d in st], len(sel))
+        if unfused:
+            out += [""] + _layer_table(sel, win)
+        out.append("")
+    return "\n".join(out)
+
+
+def summarize_mixed_counters(fetch_csv, write_csv, steps, layers):
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE (two rocprofv3 --pmc runs of
+    `bench.py --only mixed --copy-probe`) over the timed steps, per kernel
+    kind, scaled by what the counters read for the 1 GiB copy probe, against
+    the algorithmic bytes of those steps."""
+    work = wl.MIXED_B32.replace(n_layer=layers, n_kv_head=(8,) * layers, window=(0,) * layers)
+    lens = wl.initial_lens_mixed_b32(work.batch).astype(np.int64)
+    sched = [wl.n_new_mixed_b32(s, work.batch, work.max_chunk) for s in range(2 + steps)]
+    for n in sched[:2]:
+        lens = lens + n
+    att = app = 0
+    for n in sched[2:]:
+        a, p, _, _ = mixed_layer_work(work, lens, n)
+        att, app = att + a * layers, app + p * layers
+        lens = lens + n
+    res = {}
+    for tag, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        st, tail = _csv_steps(path, "Dispatch_Id", tag)
+        copy = [d[3] * 1024 for d in tail if "copyBuffer" in d[0]]
+        if not copy:
+            raise SystemExit(f"{path}: no copy probe dispatch after the last step (--copy-probe)")
+        f = COPY_BYTES / copy[-1]
+        by = {}
+        for s in st[-steps:]:
+            for d in s:
+                by[d[0]] = by.get(d[0], 0.0) + d[3] * 1024 * f
+        res[tag] = (by, f, copy[-1])
+    fb, ff, fc = res["FETCH_SIZE"]
+    wb, wf, wc = res["WRITE_SIZE"]
+    kinds = sorted(set(fb) | set(wb), key=lambda k: -(fb.get(k, 0) + wb.get(k, 0)))
+    out = [f"copy probe (1 GiB read + 1 GiB written): FETCH_SIZE {fc / 1024:.1f} KiB -> factor "
+           f"{ff:.3f}; WRITE_SIZE {wc / 1024:.1f} KiB -> factor {wf:.3f}", "",
+           f"timed steps: {steps}, {layers} layers each", "",
+           "| kernel | FETCH bytes (scaled) | WRITE bytes (scaled) |", "|---|---|---|"]
+    for k in kinds:
+        out.append(f"| {k} | {fb.get(k, 0):.4e} | {wb.get(k, 0):.4e} |")
+    attk = ("k_decode", "k_chunk", "k_combine")
+    ta = sum(fb.get(k, 0) + wb.get(k, 0) for k in attk)
+    tp = fb.get("k_append", 0) + wb.get("k_append", 0)
+    out += ["", f"attention kernels (decode, chunk, combine): traffic {ta:.4e} B, algorithmic "
+            f"{att:.4e} B, ratio {ta / att:.4f}",
+            f"append kernel: traffic {tp:.4e} B, algorithmic {app:.4e} B, ratio "
+            f"{tp / app if app else float('nan'):.4f}", "",
+            f"kernels_sha256_16: {kernels_sha()}"]
+    return "\n".join(out)
+
+
 def counter_traffic(bytes_per_launch, fused):
     """HBM traffic per decode launch from the committed counter summary, if it
     was taken on the current kernel source; else None."""
@@ -263,6 +443,18 @@ def counter_traffic(bytes_per_launch, fused):
     ratio = float(kv["traffic_ratio"])
     return {"bytes": round(ratio * bytes_per_launch), "ratio": ratio,
             "measured_bytes_per_launch": float(kv["traffic_bytes_per_launch"])}
+
+
+def copy_probe(dev):
+    """A 1 GiB device-to-device copy: the reference the HBM counters are
+    scaled by."""
+    src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log("[bench] copy probe: 1 GiB read + 1 GiB written")
+    del src, dst
 
 
 def fill_history(cache, work, target, dev):
@@ -819,7 +1011,21 @@ def main():
                     help="print the HBM traffic summary of two rocprofv3 --pmc runs of this "
                          "bench (FETCH_SIZE, WRITE_SIZE; same --steps / --warmup / --layers, "
                          "--copy-probe) and exit")
+    ap.add_argument("--summarize-legs", metavar="KERNEL_TRACE_CSV",
+                    help="print the step summary of a rocprofv3 kernel trace of --only mixed or "
+                         "--only long_decode (same --only and step counts) and exit")
+    ap.add_argument("--summarize-mixed-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the HBM traffic summary of two rocprofv3 --pmc runs of --only "
+                         "mixed --copy-probe (same --mixed-steps / --mixed-layers) and exit")
     args = ap.parse_args()
+    if args.summarize_legs:
+        n = args.mixed_steps if args.only == "mixed" else args.long_decode_steps
+        print(summarize_legs(args.summarize_legs, args.only, n, args.mixed_layers))
+        return
+    if args.summarize_mixed_counters:
+        print(summarize_mixed_counters(*args.summarize_mixed_counters, args.mixed_steps,
+                                       args.mixed_layers))
+        return
     if args.summarize_mfma:
         print(summarize_mfma(args.summarize_mfma, args.prefill_chunks))
         return
@@ -841,8 +1047,10 @@ def main():
         print(json.dumps({"prefill": prefill_leg(dev, args.prefill_chunks)}), flush=True)
         return
     if args.only == "mixed":
-        print(json.dumps({"mixed": mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)}),
-              flush=True)
+        obj = {"mixed": mixed_leg(dev, args.mixed_steps, 2, args.mixed_layers)}
+        if args.copy_probe:
+            copy_probe(dev)
+        print(json.dumps(obj), flush=True)
         return
     if args.only == "paged":
         print(json.dumps({"paged": paged_leg(dev, args.paged_steps, args.warmup)}), flush=True)
@@ -955,13 +1163,7 @@ def main():
     achieved, kbytes, dec_n, kinds = head["achieved"], head["kbytes"], head["dec_n"], head["kinds"]
 
     if args.copy_probe:
-        src = torch.empty(2 ** 30, dtype=torch.uint8, device=dev).random_()
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        log("[bench] copy probe: 1 GiB read + 1 GiB written")
-        del src, dst
+        copy_probe(dev)
 
     cache.close()
     del cache, qs, ks, vs, outs

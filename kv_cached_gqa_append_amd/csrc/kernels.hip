@@ -1281,81 +1281,56 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   auto &pls = pls_all[wv];
   const int g = pa.dec_transpose ? blockIdx.x : blockIdx.y;
   const int item = pa.dec_transpose ? blockIdx.y : blockIdx.x;
-  const int SK = __builtin_amdgcn_readfirstlane(pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
   int b;
-  int64_t split64;
-  auto row_at = [&](int r) {
-    return pa.dec_order_dev ? (int)pa.dec_order_dev[r] : pa.dec_ordered ? (int)pa.dec_order[r] : r;
-  };
-  find_item(
-      st.B, item,
-      [&](int r0) -> int {
-        const int r = row_at(r0);
-        const int nr = st.n_new[r];
-        if (NW > 1) return nr <= 1 ? 1 : 0;  // one workgroup per row
-        if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
-        const DecodeSpan sp = decode_span_dev(la, st.lens[r], st.first[r]);
-        return (int)cdiv(sp.hi - sp.base, SK);
-      },
-      &b, &split64);
-  if (b < 0) return;
-  b = __builtin_amdgcn_readfirstlane(row_at(b));
-  if constexpr (FUSED || NW > 1) {
-    if (st.n_new[b] == 0) {  // idle row: its padded token (and zero outputs)
-      if (FUSED && wv == 0) store_idle_token<D>(la, fa, b, g, st.lens[b], lane);
-      if constexpr (MERGE || NW > 1) {  // (else the merge kernel writes them)
-        bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
-        for (int e = wv * 64 + lane; e < REP * D; e += 64 * NW) o[e] = (bf16)0.f;
-      }
-      return;
-    }
+  int64_t split64 = 0;
+  int nn_b;
+  int64_t p_b, first_b;
+  if constexpr (NW > 1) {
+    // One workgroup per row: a one-token step's counts are all 0 or 1, so
+    // the row is the grid index.  Its count, length and first visible
+    // position are loaded together.
+    b = __builtin_amdgcn_readfirstlane(item);
+    nn_b = st.n_new[b];
+    p_b = st.lens[b];
+    first_b = st.first[b];
+  } else {
+    const int SK = __builtin_amdgcn_readfirstlane(pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
+    auto row_at = [&](int r) {
+      return pa.dec_order_dev ? (int)pa.dec_order_dev[r] : pa.dec_ordered ? (int)pa.dec_order[r] : r;
+    };
+    find_item(
+        st.B, item,
+        [&](int r0) -> int {
+          const int r = row_at(r0);
+          const int nr = st.n_new[r];
+          if (nr != 1) return (FUSED && nr == 0) ? 1 : 0;
+          const DecodeSpan sp = decode_span_dev(la, st.lens[r], st.first[r]);
+          return (int)cdiv(sp.hi - sp.base, SK);
+        },
+        &b, &split64);
+    if (b < 0) return;
+    b = __builtin_amdgcn_readfirstlane(row_at(b));
+    nn_b = FUSED ? st.n_new[b] : 1;
+    p_b = st.lens[b];
+    first_b = st.first[b];
   }
-  const int split = NW > 1 ? wv : (int)split64;
   const int h0 = g * REP;
-  const int64_t p = st.lens[b];
-  const DecodeSpan span = decode_span_dev(la, p, st.first[b]);
-  const int64_t base64 = span.base, hi64 = span.hi;
-  // Row indices fit in 32 bits (rows <= max_len < 2^31).
-  const int hi = (int)hi64, va = (int)span.va, vn = (int)span.vn, vwrap = span.vwrap;
+  const int64_t bg = (int64_t)b * la.hkv + g;
+  const int split = NW > 1 ? wv : (int)split64;
   // The row's 16-key tiles are dealt round-robin to its splits: split s
   // takes tiles s, s + nsplit, s + 2 nsplit, ... (counts differ by at most
   // one).  The splits of a row then sweep its K and V regions side by side,
   // so the waves in flight read from far fewer places in HBM than if each
   // split streamed its own contiguous run.  SK is a multiple of TK, so the
   // split count cdiv(hi - base, SK) is also cdiv(tiles, SK / TK) and every
-  // split gets a tile.
-  const int ntile = (hi - (int)base64 + TK - 1) / TK;
-  // (the workgroup form: one split per wave, at most one per tile; waves
-  // past the row's splits stream nothing and hold empty partials)
-  const int nsplit = NW > 1 ? (ntile < NW ? ntile : NW) : (hi - (int)base64 + SK - 1) / SK;
-  // (uniform values; readfirstlane keeps them in scalar registers, where the
-  // tile loads take their offsets)
-  const int t_begin = __builtin_amdgcn_readfirstlane((int)base64 + split * TK);
-  const int t_stride = __builtin_amdgcn_readfirstlane(nsplit * TK);
-  const int n_iter = __builtin_amdgcn_readfirstlane((ntile - split + nsplit - 1) / nsplit);
-  const int64_t bg = (int64_t)b * la.hkv + g;
-  // Fused: the new key's storage row (full layout: p; ring: p % W) lies in
-  // exactly one split.  That wave loads the token's key, value and rotation
-  // here, ahead of the queries' loads, and stores the rotated row before its
-  // tile loads.
-  bool appender = false;
-  float ax1 = 0.f, ax2 = 0.f, arc = 1.f, ars = 0.f;
-  bf16 av1 = (bf16)0.f, av2 = (bf16)0.f;
-  if constexpr (FUSED) {
-    const int r_new = la.ring ? (int)(p % la.window) : (int)p;
-    appender = (r_new - (int)base64) / TK % nsplit == split;
-    if (appender && lane < D / 2) {
-      const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
-      const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
-      ax1 = (float)ks[lane];
-      ax2 = (float)ks[lane + D / 2];
-      av1 = vs[lane];
-      av2 = vs[lane + D / 2];
-      if (st.rope) {
-        arc = st.rope[(p * (D / 2) + lane) * 2 + 0];
-        ars = st.rope[(p * (D / 2) + lane) * 2 + 1];
-      }
-    }
+  // split gets a tile.  The workgroup form takes nsplit = min(tiles, NW)
+  // with one split per wave: wave w reads tiles w, w + NW, ... from slot 0
+  // (a ring layer's span starts there; a row of fewer than NW tiles gives
+  // wave w at most tile w).
+  int t_begin, t_stride;
+  if constexpr (NW > 1) {
+    t_begin = split * TK;
+    t_stride = NW * TK;
   }
 
   const int kr = lane / LK, j = lane % LK;          // QK: key in round, chunk group
@@ -1379,6 +1354,7 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   };
   constexpr int LPT = NR * NCH + VT;  // loads per tile
   constexpr int page_b = kPageRows * D * 2;  // bytes of one head's page (K or V)
+  int n_iter = 0;  // tiles of this split (loads past them: zero descriptors)
   auto load = [&](int it, Tile &T) {
     const bool live = it < n_iter;
     const int t0 = t_begin + (live ? it : 0) * t_stride;
@@ -1420,26 +1396,80 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   };
 
   // -- queries: REP heads of token 0 rotated at p; each lane keeps its share --
-  // The loads of the queries and their rotation go out first, then the
-  // first tiles, before any of them is waited for, so the queries' round
-  // trip and the first tiles' overlap.  In the appending kernel the wave
-  // whose split holds the new row stores it before its tile loads.
-  constexpr int QE = REP * D / 64;                  // query elements per lane
-  const bf16 *qsrc = q + ((int64_t)b * st.C * st.Hq + h0) * D;
   // Lane l holds elements l + 64 i, all at head-dim index d = l + 64 i mod D,
   // so it needs one rotation entry (frequency l mod D/2); the partner of an
   // element (d + D/2 mod D) is its own element i ^ 1 at D 128 and lane
-  // l ^ 32's element i at D 64.  No branch around the loads, so they go out
-  // back to back: without a table, the rotation's load reads the query row
-  // (16-byte aligned) and is not used.  bf16 values stay as loaded bits.
+  // l ^ 32's element i at D 64.  bf16 values stay as loaded bits.
+  constexpr int QE = REP * D / 64;                  // query elements per lane
   static_assert(D == 64 || D == 128, "query staging covers head_dim 64 and 128");
-  const uint16_t *qraw = reinterpret_cast<const uint16_t *>(qsrc);
+  const uint16_t *qraw = reinterpret_cast<const uint16_t *>(q + ((int64_t)b * st.C * st.Hq + h0) * D);
   uint16_t qx[QE];
+  Tile T[NBUF];
+  if constexpr (FUSED || NW > 1) {
+    if (nn_b == 0) {  // idle row: its padded token (and zero outputs)
+      if (FUSED && wv == 0) store_idle_token<D>(la, fa, b, g, p_b, lane);
+      if constexpr (MERGE || NW > 1) {  // (else the merge kernel writes them)
+        bf16 *o = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + g * REP) * D;
+        for (int e = wv * 64 + lane; e < REP * D; e += 64 * NW) o[e] = (bf16)0.f;
+      }
+      return;
+    }
+  }
+  const int64_t p = p_b;
+  const DecodeSpan span = decode_span_dev(la, p, first_b);
+  const int64_t base64 = span.base, hi64 = span.hi;
+  // Row indices fit in 32 bits (rows <= max_len < 2^31).
+  const int hi = (int)hi64, va = (int)span.va, vn = (int)span.vn, vwrap = span.vwrap;
+  const int ntile = (hi - (int)base64 + TK - 1) / TK;
+  int nsplit;
+  if constexpr (NW > 1) {
+    // (waves past the row's splits compute nothing and hold empty partials)
+    nsplit = ntile < NW ? ntile : NW;
+    n_iter = __builtin_amdgcn_readfirstlane((ntile - split + NW - 1) / NW);
+  } else {
+    const int SK = __builtin_amdgcn_readfirstlane(pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys);
+    nsplit = (hi - (int)base64 + SK - 1) / SK;
+    // (uniform values; readfirstlane keeps them in scalar registers, where
+    // the tile loads take their offsets)
+    t_begin = __builtin_amdgcn_readfirstlane((int)base64 + split * TK);
+    t_stride = __builtin_amdgcn_readfirstlane(nsplit * TK);
+    n_iter = __builtin_amdgcn_readfirstlane((ntile - split + nsplit - 1) / nsplit);
+  }
+  // Fused: the new key's storage row (full layout: p; ring: p % W) lies in
+  // exactly one split.  That wave loads the token's key, value and rotation
+  // here, ahead of the queries' loads, and stores the rotated row before its
+  // tile loads.
+  bool appender = false;
+  float ax1 = 0.f, ax2 = 0.f, arc = 1.f, ars = 0.f;
+  bf16 av1 = (bf16)0.f, av2 = (bf16)0.f;
+  if constexpr (FUSED) {
+    const int r_new = la.ring ? (int)(p % la.window) : (int)p;
+    appender = (r_new - (int)base64) / TK % nsplit == split;
+    if (appender && lane < D / 2) {
+      const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
+      const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
+      ax1 = (float)ks[lane];
+      ax2 = (float)ks[lane + D / 2];
+      av1 = vs[lane];
+      av2 = vs[lane + D / 2];
+      if (st.rope) {
+        arc = st.rope[(p * (D / 2) + lane) * 2 + 0];
+        ars = st.rope[(p * (D / 2) + lane) * 2 + 1];
+      }
+    }
+  }
+
+  // The loads of the queries and their rotation go out first, then the
+  // first tiles, before any of them is waited for, so the queries' round
+  // trip and the first tiles' overlap.  In the appending kernel the wave
+  // whose split holds the new row stores it before its tile loads.  No
+  // branch around the rotation's load: without a table it reads the query
+  // row (16-byte aligned) and is not used.
   const bool rot = st.rope != nullptr;
 #pragma unroll
   for (int i = 0; i < QE; ++i) qx[i] = qraw[lane + 64 * i];
   const float2 qcs = *reinterpret_cast<const float2 *>(
-      rot ? st.rope + (p * (D / 2) + lane % (D / 2)) * 2 : reinterpret_cast<const float *>(qsrc));
+      rot ? st.rope + (p * (D / 2) + lane % (D / 2)) * 2 : reinterpret_cast<const float *>(qraw));
   const float qc = qcs.x, qsn = qcs.y;
   if constexpr (FUSED) {
     if (appender) {
@@ -1454,7 +1484,6 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   // appending wave's tiles come after its store (the memory pipeline keeps
   // one wave's accesses to one address in order).
   asm volatile("" ::: "memory");
-  Tile T[NBUF];
 #pragma unroll
   for (int i = 0; i < NBUF - 1; ++i) load(i, T[i]);
   // Nothing below moves above the tile loads: the compiler computes nothing
