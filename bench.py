@@ -7,13 +7,13 @@ idle rows (n_new = 0, redrawn per step).  The history is filled through the
 real protocol in 64-token chunks before timing (untimed); q/k/v are
 synthetic N(0, 1) tensors already resident in HBM.
 
-One step = for each of the 32 layers kvc_append + kvc_attend (append, decode
-attention and split-combine kernels), then one kvc_advance; the decode
-attention kernel is the roofline kernel.  A second timed leg then runs the
-same steps through kvc_append_attend (per layer an appending decode kernel,
-RoPE + append + decode attention, and the split merge) and reports it next
-to the headline
-(``--fused`` makes it the headline, ``--no-other-leg`` skips it), and a
+One step = for each of the 32 layers one kvc_append_attend (an appending
+decode kernel: RoPE + append of the new token + decode attention, then the
+split merge), then one kvc_advance; the appending decode kernel is the
+roofline kernel.  A second timed leg then runs the same steps through
+kvc_append + kvc_attend (append, decode attention and split-merge kernels)
+and reports it next to the headline (``--two-call`` makes it the headline,
+``--no-other-leg`` skips it), and a
 third replays a captured static step (kvc_static_begin, kvc_append_attend
 per layer, kvc_advance) from a HIP graph, reported as ``graph``.  Warmup
 steps run first; the timed steps are bracketed by torch.cuda.synchronize().
@@ -992,9 +992,9 @@ def main():
                     help="timed steps of the paged decode leg (0 skips it)")
     ap.add_argument("--only", choices=("mixed", "long_decode", "paged"),
                     help="run only that leg and print its object")
-    ap.add_argument("--fused", action="store_true",
-                    help="headline leg through kvc_append_attend (appending decode + merge) instead "
-                         "of kvc_append + kvc_attend")
+    ap.add_argument("--two-call", action="store_true",
+                    help="headline leg through kvc_append + kvc_attend (two calls per layer) "
+                         "instead of kvc_append_attend (the appending decode + merge)")
     ap.add_argument("--no-other-leg", action="store_true",
                     help="skip the second timed leg through the other entry point")
     ap.add_argument("--layers", type=int, default=0,
@@ -1031,11 +1031,11 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.layers,
-                              args.fused))
+                              not args.two_call))
         return
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, args.steps, args.warmup, args.layers,
-                                 args.fused))
+                                 not args.two_call))
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this hot path runs on one GPU; multi-GPU runs are not part of it "
@@ -1139,10 +1139,10 @@ def main():
         return r
 
     per_leg = args.steps + args.warmup
-    head = timed_leg(args.fused, schedule[:per_leg])
+    head = timed_leg(not args.two_call, schedule[:per_leg])
     other = None
     if legs == 2:
-        o = timed_leg(not args.fused, schedule[per_leg:2 * per_leg])
+        o = timed_leg(args.two_call, schedule[per_leg:2 * per_leg])
         other = {"entry": "kvc_append_attend" if o["fused"] else "kvc_append+kvc_attend",
                  "value": round(o["value"], 1), "unit": "GB/s",
                  "ms_per_step": round(o["ms_step"], 4),

@@ -530,6 +530,29 @@ int launch_static_begin(const StaticBeginArgs &a, void *stream) {
 // ---------------------------------------------------------------------------
 // fused RoPE + append: one wave per (row b, token i, KV head g)
 // ---------------------------------------------------------------------------
+
+// Zero V rows [lo, end) of one head's region (end at most one 32-row tile
+// past lo).  In the V layout each (16-row block, d) pair holds its 16 rows
+// contiguously, so a block's rows from lo on are one run per d: element
+// stores up to an 8-byte boundary, then 8-byte stores.  Lane l takes
+// d = l, l + 64, ...
+template <typename T>
+__device__ __forceinline__ void zero_v_rows(char *base, int64_t bg, int rows_alloc, int64_t lo,
+                                            int64_t end, int D, int lane) {
+  constexpr int G = 8 / (int)sizeof(T);  // elements per 8-byte store
+  for (int64_t blk = lo / kVBlock; blk * kVBlock < end; ++blk) {
+    const int k0 = lo > blk * kVBlock ? (int)(lo - blk * kVBlock) : 0;
+    const int k1 = end < (blk + 1) * kVBlock ? (int)(end - blk * kVBlock) : kVBlock;
+    for (int d = lane; d < D; d += 64) {
+      T *run = v_elem<T>(base, bg, rows_alloc, blk * kVBlock, d, D);
+      int k = k0;
+      for (; k < k1 && (k % G != 0 || k + G > k1); ++k) run[k] = from_f<T>(0.f);
+      for (; k + G <= k1; k += G) *reinterpret_cast<uint2 *>(run + k) = make_uint2(0u, 0u);
+      for (; k < k1; ++k) run[k] = from_f<T>(0.f);
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const T *__restrict__ k,
                                                const T *__restrict__ v, int32_t *slot_out) {
@@ -566,10 +589,8 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
     if (old_top == 0 || (new_top - 1) / kRowAlign != (old_top - 1) / kRowAlign) {
       int64_t end = (new_top + kRowAlign - 1) / kRowAlign * kRowAlign;
       if (end > la.rows_alloc) end = la.rows_alloc;
-      const int64_t bgz = (int64_t)b * la.hkv + g;
-      for (int d = threadIdx.x; d < st.D; d += 64)
-        for (int64_t rz = new_top; rz < end; ++rz)
-          *v_elem<T>(la.v, bgz, la.rows_alloc, rz, d, st.D) = from_f<T>(0.f);
+      zero_v_rows<T>(la.v, (int64_t)b * la.hkv + g, la.rows_alloc, new_top, end, st.D,
+                     (int)threadIdx.x);
     }
   }
   const int64_t bg = (int64_t)b * la.hkv + g;
@@ -578,9 +599,7 @@ __global__ __launch_bounds__(64) void k_append(StepArgs st, LayerArgs la, const 
   if (staged && i == 0) {
     int64_t end = ((int64_t)n + kRowAlign - 1) / kRowAlign * kRowAlign;
     if (end > la.stage_rows_alloc) end = la.stage_rows_alloc;
-    for (int d = threadIdx.x; d < st.D; d += 64)
-      for (int64_t rz = n; rz < end; ++rz)
-        *v_elem<T>(la.sv, bg, la.stage_rows_alloc, rz, d, st.D) = from_f<T>(0.f);
+    zero_v_rows<T>(la.sv, bg, la.stage_rows_alloc, n, end, st.D, (int)threadIdx.x);
   }
   T *kd, *vd;
   if (staged) {
@@ -1111,9 +1130,7 @@ __device__ __forceinline__ void store_token_row(const LayerArgs &la, const Fused
     if (old_top == 0 || (new_top - 1) / kRowAlign != (old_top - 1) / kRowAlign) {
       int64_t end = (new_top + kRowAlign - 1) / kRowAlign * kRowAlign;
       if (end > la.rows_alloc) end = la.rows_alloc;
-      for (int d = lane; d < D; d += 64)
-        for (int64_t rz = new_top; rz < end; ++rz)
-          *v_elem<bf16>(la.v, bg, la.rows_alloc, rz, d, D) = (bf16)0.f;
+      zero_v_rows<bf16>(la.v, bg, la.rows_alloc, new_top, end, D, lane);
     }
   }
 }
