@@ -280,13 +280,14 @@ def _csv_steps(path, order="Start_Timestamp", counter=None):
     return steps, cur
 
 
-def _split_layers(step):
-    """The dispatches of one unfused step, per layer: each layer starts at its
-    k_append (what precedes the first one, the step's count upload, and the
-    closing k_advance are left out)."""
+def _split_layers(step, first="k_append"):
+    """The dispatches of one step, per layer: each layer starts at its first
+    kernel (k_append through kvc_append + kvc_attend, k_decode through
+    kvc_append_attend); what precedes the first layer (the step's count
+    upload) and the closing k_advance are left out."""
     layers = []
     for d in step:
-        if d[0] == "k_append":
+        if d[0] == first:
             layers.append([])
         if layers and d[0] != "k_advance":
             layers[-1].append(d)
@@ -306,28 +307,35 @@ def _kind_table(dispatches, n_steps):
     return out
 
 
-def _layer_table(steps, window):
+def _layer_table(steps, window, first="k_append", dec_bytes=None):
     """Per layer kind (global / sliding ring): mean span of a layer (first
     dispatch start to last dispatch end), mean time its kernels kept the GPU
-    busy (union of spans) and the mean per kernel kind."""
+    busy (union of spans) and the mean per kernel kind; with dec_bytes (the
+    algorithmic bytes of one layer's decode launch, per kind), the decode
+    kernel's rate."""
     per = {"global": {"span": [], "busy": [], "kinds": {}},
            "ring": {"span": [], "busy": [], "kinds": {}}}
     for st in steps:
-        for l, lay in enumerate(_split_layers(st)):
+        for l, lay in enumerate(_split_layers(st, first)):
             p = per["global" if window[l] == 0 else "ring"]
             p["span"].append((max(d[2] for d in lay) - min(d[1] for d in lay)) / 1e3)
             p["busy"].append(_union_us([(d[1], d[2]) for d in lay]))
             for d in lay:
                 p["kinds"].setdefault(d[0], []).append((d[2] - d[1]) / 1e3)
-    out = ["| layer kind | layers timed | span us (mean) | busy us (mean) | per-kind avg us |",
-           "|---|---|---|---|---|"]
+    out = ["| layer kind | layers timed | span us (mean) | busy us (mean) | per-kind avg us |" +
+           (" decode GB/s |" if dec_bytes else ""),
+           "|---|---|---|---|---|" + ("---|" if dec_bytes else "")]
     for k, p in per.items():
         if not p["span"]:
             continue
         kinds = ", ".join(f"{n} {np.mean(v):.2f} x{len(v) / len(p['span']):.2g}"
                           for n, v in sorted(p["kinds"].items()))
-        out.append(f"| {k} | {len(p['span'])} | {np.mean(p['span']):.2f} | "
-                   f"{np.mean(p['busy']):.2f} | {kinds} |")
+        row = (f"| {k} | {len(p['span'])} | {np.mean(p['span']):.2f} | "
+               f"{np.mean(p['busy']):.2f} | {kinds} |")
+        if dec_bytes:
+            dv = p["kinds"].get("k_decode")
+            row += f" {dec_bytes[k] / (np.mean(dv) * 1e3):.0f} |" if dv else " |"
+        out.append(row)
     return out
 
 
@@ -349,24 +357,40 @@ def summarize_legs(trace_csv, only, steps, mixed_layers):
         per = _periods(all_steps[-steps - 1:])
         disp = [d for st in timed for d in st]
         att = [d for d in disp if d[0] in ("k_decode", "k_chunk", "k_combine")]
+        union_ms = _union_us([(d[1], d[2]) for d in att]) / 1e3
+        work = wl.MIXED_B32.replace(n_layer=mixed_layers, n_kv_head=(8,) * mixed_layers,
+                                    window=(0,) * mixed_layers)
+        lens = wl.initial_lens_mixed_b32(work.batch).astype(np.int64)
+        sched = [wl.n_new_mixed_b32(i, work.batch, work.max_chunk) for i in range(2 + steps)]
+        for n in sched[:2]:
+            lens = lens + n
+        att_b = 0
+        for n in sched[2:]:
+            att_b += mixed_layer_work(work, lens, n)[0] * mixed_layers
+            lens = lens + n
+        gbs = att_b / (union_ms / 1e3) / 1e9
         out += [f"## Timed steps: the last {steps} ({mixed_layers} layers each)", "",
                 f"step period (advance to advance): {per.mean():.3f} ms mean", "",
                 f"attention kernels (decode, chunk, combine): union of spans "
-                f"{_union_us([(d[1], d[2]) for d in att]) / 1e3:.3f} ms, summed "
-                f"{sum(d[2] - d[1] for d in att) / 1e6:.3f} ms over {steps} steps", ""]
+                f"{union_ms:.3f} ms, summed "
+                f"{sum(d[2] - d[1] for d in att) / 1e6:.3f} ms over {steps} steps", "",
+                f"attention: {att_b / 1e9:.2f} GB algorithmic over the union = {gbs:.0f} GB/s, "
+                f"{gbs / PEAK_HBM_GBS:.4f} of the HBM peak", ""]
         out += _kind_table(disp, steps)
         return "\n".join(out)
     work = wl.LONG_5TO1
     win, W, S, C4 = work.window, 4, steps, 4
     fill = len(wl.fill_plan(np.full(work.batch, 510 * 64), 64))
-    legs = [("prefill: 510 chunk steps of 64 (kvc_append + kvc_attend)", 0, fill, True)]
+    legs = [("prefill: 510 chunk steps of 64 (kvc_append + kvc_attend)", 0, fill, "k_append")]
     o = fill + W
-    legs.append(("decode, kvc_append + kvc_attend (timed steps)", o, o + S, True))
+    legs.append(("decode, kvc_append + kvc_attend (timed steps)", o, o + S, "k_append"))
     o += S + C4 + W
-    legs.append(("decode, kvc_append_attend (timed steps)", o, o + S, False))
+    legs.append(("decode, kvc_append_attend (timed steps)", o, o + S, "k_decode"))
     o += S + C4 + W
-    legs.append(("decode, replays of the captured static step (timed steps)", o, o + S, False))
-    for title, a, b, unfused in legs:
+    legs.append(("decode, replays of the captured static step (timed steps)", o, o + S,
+                 "k_decode"))
+    B, D, sz = work.batch, work.head_dim, work.dtype_bytes
+    for title, a, b, first in legs:
         sel = all_steps[a:b]
         if len(sel) != b - a:
             out += [f"## {title}: trace holds {len(sel)} of its {b - a} steps", ""]
@@ -375,8 +399,16 @@ def summarize_legs(trace_csv, only, steps, mixed_layers):
         out += [f"## {title}", "", f"steps {a}..{b - 1} of the trace; step period (advance to "
                 f"advance) {per.mean():.3f} ms mean, {np.median(per):.3f} ms median", ""]
         out += _kind_table([d for st in sel for d in st], len(sel))
-        if unfused:
-            out += [""] + _layer_table(sel, win)
+        dec_bytes = None
+        if a > 0:
+            # one-token steps: a layer's decode reads every visible key (global:
+            # all, ring: the W newest) of each row and KV head, its queries and
+            # outputs; the appending kernel also reads and writes the new k, v
+            L = 510 * 64 + (a - fill)
+            qo = B * work.n_q_head * D * sz * 2 + (B * 8 * D * sz * 4 if first == "k_decode" else 0)
+            dec_bytes = {"global": B * (L + 1) * 8 * D * sz * 2 + qo,
+                         "ring": B * min(L + 1, max(work.window)) * 8 * D * sz * 2 + qo}
+        out += [""] + _layer_table(sel, win, first, dec_bytes)
         out.append("")
     return "\n".join(out)
 
