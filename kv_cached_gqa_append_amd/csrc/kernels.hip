@@ -1914,12 +1914,12 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // Workgroup = 8 waves = up to 256 query rows of one (row b, KV head g), so
 // each key tile is read from HBM once for all of them; query row
 // r = i * REP + hl (token-major), wave w holds rows w*32 .. w*32+31 as two
-// 16-row blocks.  Key tiles of 32 rows pass through a 3-stage LDS ring:
-// every thread loads 16 bytes of K and 16 bytes of V per tile with raw buffer
-// loads (hand-placed waits, several tiles in flight), writes them to LDS (K
-// row-major with padded rows; V transposed, each head-dim row holding the
-// keys in the order the PV operand takes them), and one barrier per tile
-// publishes them.  Per wave and tile:
+// 16-row blocks.  Key tiles of 32 rows pass through a ring of LDS stages
+// (8 for the 8-wave workgroup, 4 for the 4-wave one): buffer loads with the
+// lds bit move each tile from HBM straight into its stage (no registers on
+// the way; K chunks at swizzled positions, V in the cache's own
+// [d][16 keys] block order), waits for them are placed by hand, and one
+// barrier per tile publishes the stage.  Per wave and tile:
 //   S^T (32 keys x 16 queries) = K . Q^T   with v_mfma_f32_16x16x32_bf16
 //   O^T (D x 16 queries)     += V^T . P^T  with the same instruction,
 // each K and V operand one 16-byte LDS read, used for both query blocks;
