@@ -978,6 +978,15 @@ __device__ __forceinline__ void tile_load(u32x4 &x, i32x4 rsrc, int voff, int so
                : "=v"(x)
                : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF));
 }
+// The same load through the caches (no nt): for loads that take only part of
+// each cache line, the rest going to a neighbouring load instruction.
+template <int OFF>
+__device__ __forceinline__ void tile_load_cached(u32x4 &x, i32x4 rsrc, int voff, int soff) {
+  static_assert(OFF >= 0 && OFF < 4096, "buffer immediate offsets are 12 bits");
+  asm volatile("buffer_load_dwordx4 %0, %1, %2, %3 offen offset:%4 ; tile load"
+               : "=v"(x)
+               : "v"(voff), "s"(rsrc), "s"(soff), "n"(OFF));
+}
 // A load of 64 16-byte chunks straight into LDS: lane L's chunk (at voff +
 // soff of the buffer) lands at LDS byte m0 + 16 L.  The compiler does not
 // see the LDS write, so the waits for it are placed by hand (lds_wait) and
@@ -1835,6 +1844,315 @@ static void launch_decode_fused_t(const StepArgs &st, const LayerArgs &la, const
 // share one CU.
 constexpr int kDecodeWgWaves = 8;
 
+// The workgroup form on the matrix cores (REP 8 and 16): one workgroup of
+// NW waves per (row, KV head), as above, but the rep query heads form one
+// 16-column block of v_mfma_f32_16x16x32_bf16 (REP 8 leaves 8 columns
+// empty).  Per 32-key tile a wave computes S^T = K Q^T (2 x D/32 products)
+// and O^T += V^T P^T (D/16 products), its K and V operands loaded from HBM
+// straight into registers in operand order: lane (q4, nl) takes 16 bytes of
+// key 8 (nl / 4) + 4 kb + nl % 4 (so its scores are keys 8 q4 .. 8 q4 + 7,
+// the P^T operand it then holds) and the 8 keys 8 q4 .. 8 q4 + 7 of head-dim
+// row 16 db + nl of the tile's V blocks.  The vector form spends about
+// REP x D / 64 dot2 instructions per key and lane, which at REP 8 and only
+// one workgroup per (row, KV head) is the larger part of its time.  Wave w
+// takes tiles w, w + NW, ... from slot 0 (at most one per tile below NW
+// tiles); the waves' partials merge through LDS with k_combine's weights
+// and order.  Rows of a tile outside the span are masked in the scores;
+// their V is finite (the append zeroes V to the end of the 32-row tile it
+// enters).
+template <int D, int REP, bool FUSED>
+__global__ __launch_bounds__(64 * kDecodeWgWaves) __attribute__((amdgpu_waves_per_eu(2)))
+void k_decode_wgm(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict__ q,
+                  FusedArgs fa) {
+  constexpr int NW = kDecodeWgWaves;
+  constexpr int NDS = D / 32;  // 32-wide d steps (QK contraction)
+  constexpr int NDB = D / 16;  // 16-wide d blocks (PV output)
+  constexpr int HS = NDS / 2;  // the partner d + D/2 sits HS steps later
+  constexpr int TT = 32;       // keys per tile
+  static_assert(REP == 8 || REP == 16, "one 16-column query block");
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  __shared__ __align__(16) float wout[NW][REP][D];
+  __shared__ float wml[NW][REP][2];
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int q4 = lane >> 4, nl = lane & 15;
+  const int g = pa.dec_transpose ? blockIdx.x : blockIdx.y;
+  // One workgroup per row (a one-token step's counts are all 0 or 1).  No
+  // branch until the tiles are out: each branch around a load makes the
+  // compiler wait for it at the join, and the prologue would become a chain
+  // of round trips.  An idle row (n_new == 0) runs with no splits: no tile
+  // is computed and the merge writes zero outputs.
+  const int b = __builtin_amdgcn_readfirstlane(pa.dec_transpose ? (int)blockIdx.y : (int)blockIdx.x);
+  const int nn_b = st.n_new[b];
+  const int p32 = st.lens[b];
+  const int first32 = st.first[b];
+  // (the row's three counters and the layer's arguments in one batch of
+  // scalar loads, waited for once, rather than one round trip after another)
+  asm volatile("" ::"s"(nn_b), "s"(p32), "s"(first32), "s"(la.window), "s"(la.rows_alloc),
+               "s"(la.hkv), "s"(la.ring), "s"(la.k), "s"(la.v), "s"(st.rope), "s"(st.Hq));
+  const int64_t p = p32;
+  const bool idle = nn_b == 0;
+  const int h0 = g * REP;
+  bf16 *ob = static_cast<bf16 *>(fa.out) + ((int64_t)b * st.Hq + h0) * D;
+  // A ring layer (the span of decode_span_dev, in 32 bits: positions stay
+  // below 2^31): the visible positions [start, p] sit in slots [0, hi) from
+  // slot 0, the oldest at slot va; vwrap = W.
+  const int W = la.window;
+  int start = p32 - W + 1 > 0 ? p32 - W + 1 : 0;
+  start = p32 < first32 ? p32 : (start > first32 ? start : first32);
+  const int vn = p32 + 1 - start, hi = p32 + 1 < W ? p32 + 1 : W;
+  const int va = start % W, vwrap = W;
+  const int ntile = idle ? 0 : (hi + TT - 1) / TT;
+  const int nsplit = ntile < NW ? ntile : NW;
+  const int n_iter = __builtin_amdgcn_readfirstlane((ntile - wv + NW - 1) / NW);
+  const int64_t bg = (int64_t)b * la.hkv + g;
+  // (an idle row's length may be max_len: no rotation entry is read for it)
+  const bool rot = st.rope != nullptr && !idle;
+
+  const bool qrow = nl < REP;
+  const float *rbase = st.rope != nullptr ? st.rope : reinterpret_cast<const float *>(q);
+  const int64_t rrow = rot ? p : 0;
+
+  // Appending form: the wave whose tiles hold the new row's slot p mod W
+  // stores the rotated row before its tile loads (one wave's accesses to one
+  // address keep their order); an idle row's wave 0 stores its padded token.
+  bool appender = false;
+  if constexpr (FUSED) {
+    const int r_new = p32 % W;
+    appender = !idle && (r_new / TT) % NW == wv;
+    const int e = lane & (D / 2 - 1);
+    const bf16 *ks = static_cast<const bf16 *>(fa.k) + bg * D;
+    const bf16 *vs = static_cast<const bf16 *>(fa.v) + bg * D;
+    const float ax1 = (float)ks[e], ax2 = (float)ks[e + D / 2];
+    const bf16 av1 = vs[e], av2 = vs[e + D / 2];
+    const float2 acs = *reinterpret_cast<const float2 *>(rbase + (rrow * (D / 2) + e) * 2);
+    if (appender) {
+      float y1 = ax1, y2 = ax2;
+      if (rot) rope_pair(ax1, ax2, acs.x, acs.y, &y1, &y2);
+      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
+    } else if (idle && wv == 0) {
+      store_token_row<D>(la, fa, b, g, p, false, ax1, ax2, (bf16)0.f, (bf16)0.f, lane);
+    }
+  }
+
+  // -- the query block: lane (q4, nl) holds head nl's d = 32 ds + 8 q4 .. + 7
+  // (rotated at p), the Q^T operand of each d step; heads past REP are zero.
+  // Every lane loads (heads past REP read head 0; without a table the
+  // rotation's loads read the start of q, at least REP * D elements, and go
+  // unused) and selects afterwards.  These loads go out through the same
+  // hand-waited path as the tiles, ahead of them, so that the compiler
+  // neither sinks them below the tiles nor waits for the tiles with them.
+  // (the appending wave's loads and stores above stay above these loads)
+  asm volatile("" ::: "memory");
+  const i32x4 rq = sgpr_rsrc(q + ((int64_t)b * st.C * st.Hq + h0) * D, REP * D * 2);
+  const i32x4 rr = sgpr_rsrc(rbase + rrow * D, D * 4);  // one position's D/2 (cos, sin)
+  u32x4 qv[NDS];
+  u32x4 rp[HS][4];  // (cos, sin) of the 8 consecutive frequencies of a step
+  {
+    const int qoff = (qrow ? nl : 0) * D * 2 + q4 * 16;
+    static_for<0, NDS>([&](auto ds) {
+      tile_load<decltype(ds)::value * 64>(qv[decltype(ds)::value], rq, qoff, 0);
+    });
+    static_for<0, HS>([&](auto ds) {
+      static_for<0, 4>([&](auto u) {
+        tile_load<decltype(ds)::value * 256 + decltype(u)::value * 16>(
+            rp[decltype(ds)::value][decltype(u)::value], rr, q4 * 64, 0);
+      });
+    });
+  }
+  constexpr int QLD = NDS + 4 * HS;  // the query block's loads
+
+  // -- tiles: K and V operands straight from HBM ------------------------------
+  // An operand load takes 64 of each K row's 256 bytes (16 rows per load);
+  // through the caches the row's other pieces, loaded next, hit the line
+  // the first one brought in (W = 512 rings: 12.5 -> 10.3 us per layer
+  // against non-temporal loads).
+  const int64_t region = (int64_t)la.rows_alloc * D * 2;  // bytes per (b, g)
+  const i32x4 rk = sgpr_rsrc(la.k + bg * region, (int)region);
+  const i32x4 rv = sgpr_rsrc(la.v + bg * region, (int)region);
+  const i32x4 rnone = sgpr_rsrc(la.k + bg * region, 0);  // zero records: no access
+  const int koff = ((8 * (nl >> 2) + (nl & 3)) * D + q4 * 8) * 2;
+  const int voff = ((q4 >> 1) * 16 * D + nl * 16 + (q4 & 1) * 8) * 2;
+  struct Tile {
+    u32x4 k[2][NDS];
+    u32x4 v[NDB];
+  };
+  constexpr int LPT = 2 * NDS + NDB;  // loads per tile
+  auto load = [&](int it, Tile &T) {
+    const bool live = it < n_iter;
+    const int t0 = (wv + (live ? it : 0) * NW) * TT;
+    const i32x4 ka = live ? rk : rnone, va_ = live ? rv : rnone;
+    // K rows and V blocks advance by the same bytes per row
+    const int so = __builtin_amdgcn_readfirstlane(t0 * D * 2);
+    static_for<0, 2>([&](auto kb) {
+      static_for<0, NDS>([&](auto ds) {
+        constexpr int off = decltype(kb)::value * 4 * D * 2 + decltype(ds)::value * 64;
+        tile_load_cached<off>(T.k[decltype(kb)::value][decltype(ds)::value], ka, koff, so);
+      });
+    });
+    static_for<0, NDB>([&](auto db) {
+      tile_load_cached<decltype(db)::value * 16 * 32>(T.v[decltype(db)::value], va_, voff, so);
+    });
+  };
+  auto wait_tile = [&](Tile &T, auto after) {
+    constexpr int N = decltype(after)::value * LPT;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) tile_wait<N>(T.k[kb][ds]);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) tile_wait<N>(T.v[db]);
+  };
+  // (the loads and stores above are older than every tile load, as the
+  // hand-placed waits require)
+  asm volatile("" ::: "memory");
+  Tile T[2];
+  load(0, T[0]);
+  load(1, T[1]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // the query block's loads are older than both tiles': wait for them only
+#pragma unroll
+  for (int ds = 0; ds < NDS; ++ds) tile_wait<2 * LPT>(qv[ds]);
+#pragma unroll
+  for (int ds = 0; ds < HS; ++ds)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tile_wait<2 * LPT>(rp[ds][u]);
+  static_assert(2 * LPT < 64, "vmcnt is 6 bits");
+  (void)QLD;
+  bf16x8_t qf[NDS];
+  {
+    float raw[NDS][8];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      const uint32_t w[4] = {qv[ds].x, qv[ds].y, qv[ds].z, qv[ds].w};
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        raw[ds][2 * e2] = bf_lo(w[e2]);
+        raw[ds][2 * e2 + 1] = bf_hi(w[e2]);
+      }
+    }
+#pragma unroll
+    for (int ds = 0; ds < HS; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const u32x4 cs = rp[ds][e / 2];
+        const float c = __uint_as_float((e & 1) ? cs.z : cs.x);
+        const float sn = __uint_as_float((e & 1) ? cs.w : cs.y);
+        const float x1 = raw[ds][e], x2 = raw[ds + HS][e];
+        const float y1 = x1 * c - x2 * sn, y2 = x1 * sn + x2 * c;
+        raw[ds][e] = rot ? y1 : x1;
+        raw[ds + HS][e] = rot ? y2 : x2;
+      }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[ds][e] = (bf16)(qrow ? raw[ds][e] : 0.f);
+  }
+
+  const float scale = kLog2e * rsqrtf((float)D);
+  float mrun = -INFINITY, lrun = 0.f;  // this lane's column (head nl), scaled log2 domain
+  floatx4 oacc[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto step = [&](int it, Tile &T) __attribute__((always_inline)) {
+    const int t0 = (wv + it * NW) * TT;
+    floatx4 sacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds)
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, T.k[kb][ds]), qf[ds], sacc[kb], 0, 0, 0);
+    // sacc[kb][jj]: key t0 + 8 q4 + 4 kb + jj, head nl
+    float sv[2][4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int key = t0 + 8 * q4 + 4 * kb + jj;
+        const int d = key - va + (key < va ? vwrap : 0);
+        const bool ok = key < hi && (unsigned)d < (unsigned)vn;
+        const float x = ok ? sacc[kb][jj] : -INFINITY;
+        sv[kb][jj] = x;
+        tmax = fmaxf(tmax, x);
+      }
+    // the column's max over the tile: its 4 lane groups hold 8 keys each
+    const float mn = fmaxf(mrun, swap32_max(swap16_max(tmax)) * scale);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    const float alpha = __builtin_amdgcn_exp2f(mrun - ms);
+    mrun = mn;
+    float ps = 0.f;
+    bf16x8_t pf;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sv[kb][jj], scale, -ms));
+        ps += pe;
+        pf[kb * 4 + jj] = (bf16)pe;
+      }
+    lrun = lrun * alpha + ps;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      oacc[db] *= alpha;
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, T.v[db]),
+                                                        pf, oacc[db], 0, 0, 0);
+    }
+  };
+  // Two register tiles: one tile's loads are out while the other computes.
+  for (int it = 0; it < n_iter; it += 2) {
+    wait_tile(T[0], std::integral_constant<int, 1>{});
+    step(it, T[0]);
+    load(it + 2, T[0]);
+    wait_tile(T[1], std::integral_constant<int, 1>{});
+    if (it + 1 < n_iter) step(it + 1, T[1]);
+    load(it + 3, T[1]);
+  }
+  // retire the loads still in flight before their registers are reused
+#pragma unroll
+  for (int i = 0; i < 2; ++i) wait_tile(T[i], std::integral_constant<int, 0>{});
+
+  // -- this wave's partial to LDS, then wave w merges heads w, w + NW, ... ------
+  if (wv < nsplit) {
+    const float lt = swap32_sum(swap16_sum(lrun));
+    if (qrow) {
+      if (q4 == 0) {
+        wml[wv][nl][0] = lt > 0.f ? mrun : -INFINITY;
+        wml[wv][nl][1] = lt;
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) wout[wv][nl][db * 16 + 4 * q4 + jj] = oacc[db][jj];
+    }
+  }
+  __syncthreads();
+  for (int h = wv; h < REP; h += NW) {
+    // split weights 2^(m_s - M) / L (a split with no visible key: l == 0)
+    const float ls = lane < nsplit ? wml[lane][h][1] : 0.f;
+    const float msv = (lane < nsplit && ls > 0.f) ? wml[lane][h][0] : -INFINITY;
+    const float M = wave_max(msv);
+    const float w = ls > 0.f ? exp2f(msv - M) : 0.f;
+    const float Lt = wave_sum(w * ls);
+    const int wt = __builtin_bit_cast(int, w / Lt);
+    auto wt_of = [&](int sp) {
+      return __builtin_bit_cast(float, __builtin_amdgcn_readlane(wt, sp));
+    };
+    for (int d = lane; d < D; d += 64) {
+      float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      int sp = 0;
+      for (; sp + 8 <= nsplit; sp += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) a[u] = combine_acc(a[u], wt_of(sp + u), wout[sp + u][h][d]);
+      }
+      for (; sp < nsplit; ++sp) a[0] = combine_acc(a[0], wt_of(sp), wout[sp][h][d]);
+      ob[h * D + d] = (bf16)combine_tree(a);
+    }
+  }
+}
+
 template <int D, int REP>
 static void launch_decode_wg_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                                const void *q, const FusedArgs &fa, bool fused,
@@ -1842,24 +2160,31 @@ static void launch_decode_wg_t(const StepArgs &st, const LayerArgs &la, const Pa
   const dim3 grid = pa.dec_transpose ? dim3((unsigned)la.hkv, (unsigned)st.B)
                                      : dim3((unsigned)st.B, (unsigned)la.hkv);
   const dim3 block(64 * kDecodeWgWaves);
-  if (fused)
-    launch_kernel((k_decode<D, REP, true, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
-                  st, la, pa, (const bf16 *)q, fa, la.table);
-  else
-    launch_kernel((k_decode<D, REP, false, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
-                  st, la, pa, (const bf16 *)q, fa, la.table);
+  if constexpr (REP == 8 || REP == 16) {
+    if (fused)
+      launch_kernel((k_decode_wgm<D, REP, true>), grid, block, lc, st, la, pa, (const bf16 *)q, fa);
+    else
+      launch_kernel((k_decode_wgm<D, REP, false>), grid, block, lc, st, la, pa, (const bf16 *)q, fa);
+  } else {
+    if (fused)
+      launch_kernel((k_decode<D, REP, true, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
+                    st, la, pa, (const bf16 *)q, fa, la.table);
+    else
+      launch_kernel((k_decode<D, REP, false, false, 3, 2, false, kDecodeWgWaves>), grid, block, lc,
+                    st, la, pa, (const bf16 *)q, fa, la.table);
+  }
 }
 
 int launch_decode_wg(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                      const void *q, const FusedArgs &fa, bool fused, const Launch &lc) {
-  if (st.C != 1 || la.paged || la.rep > 8) return (int)hipErrorInvalidValue;
+  if (st.C != 1 || la.paged || (la.rep > 8 && la.rep != 16)) return (int)hipErrorInvalidValue;
 #define KVC_DEC(DD, RR)                                                  \
   if (st.D == DD && la.rep == RR) {                                      \
     launch_decode_wg_t<DD, RR>(st, la, pa, q, fa, fused, lc);           \
     return (int)hipGetLastError();                                       \
   }
-  KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8)
-  KVC_DEC(64, 1) KVC_DEC(64, 2) KVC_DEC(64, 4) KVC_DEC(64, 8)
+  KVC_DEC(128, 1) KVC_DEC(128, 2) KVC_DEC(128, 4) KVC_DEC(128, 8) KVC_DEC(128, 16)
+  KVC_DEC(64, 1) KVC_DEC(64, 2) KVC_DEC(64, 4) KVC_DEC(64, 8) KVC_DEC(64, 16)
 #undef KVC_DEC
   return (int)hipErrorInvalidValue;
 }

@@ -727,9 +727,11 @@ kvc::PartialArgs partial_args(const kvc_t *h) {
 // form instead: one workgroup per (row, KV head) whose waves take the splits
 // and merge through LDS.  (A window mask over a full-length layout keeps the
 // split plan, which its paged form shares, so that the two give the same
-// bits; joint layers and REP > 8 keep it too.)
+// bits; joint layers keep it too.  REP 8 and 16 run the form on the matrix
+// cores, REP 1 to 4 on the vector units.)
 bool wg_layer(const kvc_t *h, int32_t layer, const kvc::LayerArgs &la) {
-  return !h->no_wg && la.ring && la.window <= kWgMaxWindow && !la.paged && la.rep <= 8 &&
+  return !h->no_wg && la.ring && la.window <= kWgMaxWindow && !la.paged &&
+         (la.rep <= 8 || la.rep == 16) &&
          h->lay.layers[layer].joint < 0 && h->cfg.dtype == KVC_BF16 &&
          kvc::fast_decode_supported(h->cfg.head_dim, la.rep);
 }

@@ -243,6 +243,23 @@ def test_fused_decode_rings_and_idle_rows(merge, wg, monkeypatch):
     _fused_vs_two_calls(work, prompts, steps, "fused_ring")
 
 
+# One-token steps of ring layers with REP 8 and 16 take the workgroup form on
+# the matrix cores: rings of 48 and 200 slots (a partial last 32-key tile),
+# rows short of the window, filling it and wrapped past it, idle rows; both
+# entry points against the oracle, and bit for bit against each other.
+@pytest.mark.parametrize("D,rep", [(64, 8), (64, 16), (128, 8), (128, 16)])
+def test_ring_decode_matrix_core_form(D, rep):
+    say(f"case: ring one-token steps, workgroup form on the matrix cores, D={D} rep={rep}, "
+        f"W=48/200, idle rows")
+    hkv = 2
+    work = wl.Workload(f"wgm_{D}_{rep}", 2, 5, hkv * rep, (hkv, hkv), D, 600, (48, 200),
+                       "bf16", 64)
+    prompts = wl.fill_plan([5, 47, 130, 260, 0], 64)
+    steps = [np.array([1, 1, 1, 1, 1])]
+    steps += [wl.n_new_decode_b64(s, batch=5, idle=1) for s in range(12)]
+    _fused_vs_two_calls(work, prompts, steps, f"wgm{D}_{rep}")
+
+
 @pytest.mark.parametrize("merge", ["0", "1"])
 def test_fused_decode_many_splits(merge, monkeypatch):
     monkeypatch.setenv("KVC_FUSED_MERGE", merge)
