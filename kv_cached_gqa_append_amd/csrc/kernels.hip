@@ -2665,24 +2665,36 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);     // MFMA
   };
 
-  // Pipeline: tiles 0 .. NSTAGE - 2 go out first, into stages 0 .. NSTAGE -
-  // 2.  Step i: this wave waits for its own loads of tile i (the NSTAGE - 2
-  // tiles issued after it stay in flight), every wave meets at the barrier
-  // (tile i is then in LDS, and every wave is done with tile i - 1), tile
-  // i + NSTAGE - 1 goes out into the stage tile i - 1 used, and tile i is
-  // computed.  Loads past the last tile read nothing and write zeros.  The
-  // queries' loads above are older than every tile load, so the tile waits
-  // retire them too.
-  for (int t = 0; t < NSTAGE - 1; ++t) issue(t, t);
+  // Pipeline, TP tiles per barrier (the 8-wave workgroup takes two: one
+  // barrier of all eight waves per 64 keys; 808 -> 843 TFLOP/s on the
+  // long-context prefill and 17.9 -> 17.2 ms per mixed step; four tiles and
+  // two tiles in the 4-wave workgroup measured no better).  Tiles 0 ..
+  // NSTAGE - TP - 1 go out first, into stages of their own index.  Step i
+  // (i a multiple of TP): this wave waits for its own loads of tiles i ..
+  // i + TP - 1 (the NSTAGE - 2 TP tiles issued after them stay in flight),
+  // every wave meets at the barrier (those tiles are then in LDS, and every
+  // wave is done with tiles i - TP .. i - 1), tiles i + NSTAGE - TP ..
+  // i + NSTAGE - 1 go out into the stages those used, and tiles i ..
+  // i + TP - 1 are computed.  Loads past the last tile read nothing and
+  // write zeros.  The queries' loads above are older than every tile load,
+  // so the tile waits retire them too.
+  constexpr int TP = QW == 8 ? 2 : 1;
+  static_assert(NSTAGE >= 2 * TP, "tiles in flight beside the ones computed");
+  for (int t = 0; t < NSTAGE - TP; ++t) issue(t, t);
   // Nothing below moves above the tile loads: the queries are rotated while
   // the first tiles are in flight.
   __builtin_amdgcn_sched_barrier(0);
   make_q();
-  for (int i = 0; i < ntiles; ++i) {
-    lds_wait<SPW * (NSTAGE - 2)>();
+  for (int i = 0; i < ntiles; i += TP) {
+    lds_wait<SPW * (NSTAGE - 2 * TP)>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    issue(i + NSTAGE - 1, (i + NSTAGE - 1) % NSTAGE);
-    if (wave_live) compute(i, i % NSTAGE);
+#pragma unroll
+    for (int u = 0; u < TP; ++u) issue(i + NSTAGE - TP + u, (i + NSTAGE - TP + u) % NSTAGE);
+    if (wave_live) {
+#pragma unroll
+      for (int u = 0; u < TP; ++u)
+        if (u == 0 || i + u < ntiles) compute(i + u, (i + u) % NSTAGE);
+    }
   }
   // the loads of tiles past the end land before the LDS is released
   lds_wait<0>();
