@@ -2752,16 +2752,18 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // other workgroup's loads have returned before its count (its waves
   // waited for all of them), so no read of a slot can follow its overwrite.
   if (pa.ring_cnt != nullptr) {
-    __shared__ int commit_last;
+    // (the verdict goes through the first word of the stages, free once
+    // every wave has passed the barrier below)
+    int *commit_last = reinterpret_cast<int *>(&ltile[0][0]);
     __syncthreads();
     if (tid == 0) {
       const int nqt = (int)cdiv((int64_t)n * REP, QT);
       const int prev =
           __hip_atomic_fetch_add(pa.ring_cnt + bg, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      commit_last = prev == nqt - 1;
+      *commit_last = prev == nqt - 1;
     }
     __syncthreads();
-    if (commit_last) {
+    if (*commit_last) {
       const int i0 = n > W ? n - W : 0;  // first kept staged row
       // Copies of n_items 16-byte chunks, four per thread in flight: every
       // load is issued (past the end the last chunk again) before the stores.
