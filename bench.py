@@ -284,10 +284,19 @@ def _split_layers(step, first="k_append"):
     """The dispatches of one step, per layer: each layer starts at its first
     kernel (k_append through kvc_append + kvc_attend, k_decode through
     kvc_append_attend); what precedes the first layer (the step's count
-    upload) and the closing k_advance are left out."""
+    upload) and the closing k_advance are left out.  first "chunk": chunk
+    steps through kvc_append_attend, where a global layer starts at its
+    k_append and a ring layer, which appends inside its one chunk launch, at
+    a k_chunk once the open layer has had its own."""
     layers = []
     for d in step:
-        if d[0] == first:
+        if first == "chunk":
+            start = d[0] == "k_append" or (
+                d[0] == "k_chunk" and (not layers or any(x[0] in ("k_chunk", "k_combine")
+                                                         for x in layers[-1])))
+        else:
+            start = d[0] == first
+        if start:
             layers.append([])
         if layers and d[0] != "k_advance":
             layers[-1].append(d)
@@ -381,7 +390,7 @@ def summarize_legs(trace_csv, only, steps, mixed_layers):
     work = wl.LONG_5TO1
     win, W, S, C4 = work.window, 4, steps, 4
     fill = len(wl.fill_plan(np.full(work.batch, 510 * 64), 64))
-    legs = [("prefill: 510 chunk steps of 64 (kvc_append + kvc_attend)", 0, fill, "k_append")]
+    legs = [("prefill: 510 chunk steps of 64 (kvc_append_attend)", 0, fill, "chunk")]
     o = fill + W
     legs.append(("decode, kvc_append + kvc_attend (timed steps)", o, o + S, "k_append"))
     o += S + C4 + W
@@ -490,7 +499,8 @@ def copy_probe(dev):
 
 
 def fill_history(cache, work, target, dev):
-    """Bring every row to target[b] tokens through append/attend/advance."""
+    """Bring every row to target[b] tokens in chunk steps of at most 64
+    tokens through kvc_append_attend and kvc_advance."""
     B, D = work.batch, work.head_dim
     g = torch.Generator(device=dev)
     g.manual_seed(wl.seed_of(work.name, "fill"))
@@ -503,8 +513,8 @@ def fill_history(cache, work, target, dev):
     t0 = time.perf_counter()
     for si, (n, Cs) in enumerate(plan):
         for l in range(work.n_layer):
-            cache.append(l, k[:, :Cs].contiguous(), v[:, :Cs].contiguous(), n)
-            cache.attend(l, q[:, :Cs].contiguous(), out[:, :Cs].contiguous())
+            cache.append_attend(l, q[:, :Cs].contiguous(), k[:, :Cs].contiguous(),
+                                v[:, :Cs].contiguous(), n, out=out[:, :Cs].contiguous())
         cache.advance()
         if si % 16 == 0:
             torch.cuda.synchronize()
@@ -800,7 +810,7 @@ def long_decode_leg(dev, steps, warmup, class_steps=4):
             "steps": steps, "warmup": warmup, "class_steps": class_steps,
             "kv_nbytes": {"rings": nb_ring, "full": nb_full},
             "prefill": {"tokens_per_s": round(B * prefill / fill_s, 1), "wall_s": round(fill_s, 3),
-                        "what": "510 chunk steps of 64 tokens through kvc_append + kvc_attend "
+                        "what": "510 chunk steps of 64 tokens through kvc_append_attend "
                                 "over all 66 layers, B 8, to 32,640 tokens"},
             "entries": legs}
 

@@ -153,6 +153,9 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_DECODE_MIN_TILES=t  shortest decode split, in 16-key tiles (default 4);
  *   KVC_DECODE_FUSED=0      kvc_append_attend enqueues kvc_append + kvc_attend;
  *   KVC_FUSED_MERGE=1       kvc_append_attend merges in its decode launch;
+ *   KVC_CHUNK_FUSED=0       kvc_append_attend stages ring layers' chunk
+ *                           steps as kvc_append does (then their outputs
+ *                           are bit for bit those of the two calls);
  *   KVC_CHUNK_SMALL=0       every chunk row in 8-wave workgroups;
  *   KVC_CHUNK_PLAN=0        chunk splits at the cap (16 per longest row)
  *                           instead of the cost-model plan;
@@ -278,8 +281,11 @@ int kvc_attend(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
 int kvc_attend_noalloc(kvc_t *h, int32_t layer, const void *q, void *out, void *stream);
 
 /* kvc_append followed by kvc_attend for one layer, in one call: same
- * arguments (q and out as for kvc_attend), same checks, same results, same
- * step protocol (the layer counts as appended and attended).  A one-token
+ * arguments (q and out as for kvc_attend), same checks, same stored rows and
+ * slot indices, same step protocol (the layer counts as appended and
+ * attended), and the same outputs (bit for bit, except the chunk steps of
+ * ring layers below, whose outputs agree within the attention's rounding:
+ * they visit the keys in another order).  A one-token
  * step (C == 1) in bf16 with a decode-kernel head shape (D in {64, 128},
  * Hq / Hkv_l in {1, 2, 4, 8, 16}) runs the rotation and store of each row's
  * new key and value and the decode attention over its key splits as one
@@ -290,7 +296,14 @@ int kvc_attend_noalloc(kvc_t *h, int32_t layer, const void *q, void *out, void *
  * merges too (the last split of a row and KV head to finish merges them):
  * one launch per layer, for callers whose launch rate bounds them; it reads
  * the partials back at the end of the launch, so a GPU-bound step is faster
- * without it.  Other steps enqueue the two calls' work.  While a merging
+ * without it.  A chunk step of a sliding-window ring layer in bf16 whose
+ * rows all hold 2 .. 64 tokens (C <= 64; not a joint layer or a joint
+ * layer's partner) stages nothing: the chunk-attention kernel reads the new
+ * rows from k and v, rotates them, scores them, and the last workgroup of
+ * each (row, KV head) writes the kept ones to their ring slots (colibri PR
+ * "How it works": append after scoring), so no append launch runs
+ * (KVC_CHUNK_FUSED=0 turns this off).  Other steps enqueue the two calls'
+ * work.  While a merging
  * launch runs, no other launch of the same handle may run concurrently (they
  * share split counters in the buffer).
  * Errors as for kvc_append; KVC_E_HIP if a launch fails after the append's

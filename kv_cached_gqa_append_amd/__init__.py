@@ -510,8 +510,10 @@ class Cache:
 
     def append_attend(self, layer, q, k, v, n_new, out=None, slot_out=None, stream=None):
         """append() then attend() of one layer in one call (an appending
-        decode kernel and the merge for a one-token bf16 step).  n_new: host
-        counts [B], or None inside a static step."""
+        decode kernel and the merge for a one-token bf16 step; the chunk
+        kernel alone, appending after scoring, for a ring layer's chunk step
+        of 2 .. 64 tokens per row).  n_new: host counts [B], or None inside a
+        static step."""
         if n_new is not None and len(n_new) != self.batch:
             raise ValueError(f"n_new has {len(n_new)} entries, cache batch is {self.batch}")
         C = int(k.shape[1])

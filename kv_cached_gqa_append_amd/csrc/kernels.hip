@@ -2308,12 +2308,15 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
       },
       &b, &local);
   if (b < 0) return;
+  // (the row's three counts in one round trip, before the query and tile
+  // loads: a count read later would wait for those too)
   const int64_t L = st.lens[b];
   const int n = st.n_new[b];
+  const int first_i = st.first[b];  // left padding: keys before it are hidden
   int nks = 1;
   int64_t cbase = 0, clo = 0, chi = 0;
   if (!la.ring) {
-    chunk_span_dev(la, L, n, st.first[b], &cbase, &clo, &chi);
+    chunk_span_dev(la, L, n, first_i, &cbase, &clo, &chi);
     nks = (int)cdiv(chi - cbase, SKP);
   }
   const int qt = (int)(local / nks), ks = (int)(local % nks);
@@ -2335,23 +2338,113 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   for (int blk = 0; blk < 2; ++blk) {
     rq[blk] = qt * QT + wave * 32 + blk * 16 + nl;
     rvalid[blk] = rq[blk] < n * REP;
-    qi[blk] = rq[blk] / REP;
-    hl[blk] = rq[blk] % REP;
+    // A row past the tile's queries computes with the last query row (its
+    // output is never written): every lane loads, so no load sits under a
+    // lane mask (whose results the compiler copies, waiting for them).
+    const int rqc = rvalid[blk] ? rq[blk] : n * REP - 1;
+    qi[blk] = rqc / REP;
+    hl[blk] = rqc % REP;
     qpos[blk] = L + qi[blk];
     const bf16 *qsrc = q + (((int64_t)b * st.C + qi[blk]) * st.Hq + g * REP + hl[blk]) * D;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
-      qv[blk][ds] = rvalid[blk] ? *reinterpret_cast<const uint4 *>(qsrc + ds * 32 + q4 * 8)
-                                : make_uint4(0, 0, 0, 0);
+      qv[blk][ds] = *reinterpret_cast<const uint4 *>(qsrc + ds * 32 + q4 * 8);
 #pragma unroll
     for (int ds = 0; ds < HS; ++ds) {
       const float4 *rsrc =
           reinterpret_cast<const float4 *>(st.rope + (qpos[blk] * (D / 2) + ds * 32 + q4 * 8) * 2);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        rp[blk][ds][u] = (rot && rvalid[blk]) ? rsrc[u] : make_float4(1.f, 0.f, 1.f, 0.f);
+        rp[blk][ds][u] = rot ? rsrc[u] : make_float4(1.f, 0.f, 1.f, 0.f);
     }
   }
+  // -- the chunk's own rows from the caller's K and V (the appending entry) ----
+  // Rows 0 .. 63 of this (row, KV head): K as pairs of 16-byte chunks (c,
+  // c + CPR / 2) with the (cos, sin) of their 8 frequencies, V as 16-byte
+  // chunks; rows past n hold zeros.  own_store rotates K
+  // (the append's arithmetic, so the bits match a staged row) and writes
+  // both into the stage layout, tile t of the rows into stage t.
+  const bool fz = !PAGED && la.ring && pa.ck != nullptr;
+  constexpr int OKP = kChunkOwnMax * (CPR / 2), OVC = kChunkOwnMax * CPR;
+  constexpr int KPT = (OKP + NT - 1) / NT, VPT = (OVC + NT - 1) / NT;
+  uint4 okx[KPT][2], ovx[VPT];
+  float4 ocs[KPT][4];
+  auto own_load = [&]() __attribute__((always_inline)) {
+    const bf16 *ckb = static_cast<const bf16 *>(pa.ck);
+    const bf16 *cvb = static_cast<const bf16 *>(pa.cv);
+    // (every lane loads: items past the end and rows past n read the last
+    // row, and own_store writes zeros for them)
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = min(tid + u * NT, OKP - 1), c = it % (CPR / 2);
+      const int rr = min(it / (CPR / 2), n - 1);
+      const bf16 *src = ckb + (((int64_t)b * st.C + rr) * la.hkv + g) * D + c * 8;
+      okx[u][0] = *reinterpret_cast<const uint4 *>(src);
+      okx[u][1] = *reinterpret_cast<const uint4 *>(src + D / 2);
+      const float4 *rs = reinterpret_cast<const float4 *>(st.rope + ((L + rr) * (D / 2) + c * 8) * 2);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) ocs[u][w] = rot ? rs[w] : make_float4(1.f, 0.f, 1.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = min(tid + u * NT, OVC - 1), c = it % CPR;
+      const int rr = min(it / CPR, n - 1);
+      ovx[u] = *reinterpret_cast<const uint4 *>(cvb + (((int64_t)b * st.C + rr) * la.hkv + g) * D +
+                                                 c * 8);
+    }
+  };
+  auto own_store = [&](int ntile) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < KPT; ++u) {
+      const int it = tid + u * NT, rr = it / (CPR / 2), c = it % (CPR / 2);
+      if (it < OKP && rr < ntile * 32) {
+        const bool live = rr < n;
+        const uint32_t w0[4] = {okx[u][0].x, okx[u][0].y, okx[u][0].z, okx[u][0].w};
+        const uint32_t w1[4] = {okx[u][1].x, okx[u][1].y, okx[u][1].z, okx[u][1].w};
+        uint32_t y0[4], y1[4];
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          float a[2], bb[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float x1 = h2 ? bf_hi(w0[e2]) : bf_lo(w0[e2]);
+            const float x2 = h2 ? bf_hi(w1[e2]) : bf_lo(w1[e2]);
+            const float4 cs = ocs[u][e2];
+            a[h2] = x1;
+            bb[h2] = x2;
+            if (rot) rope_pair(x1, x2, h2 ? cs.z : cs.x, h2 ? cs.w : cs.y, &a[h2], &bb[h2]);
+          }
+          y0[e2] = live ? pack_bf16(a[0], a[1]) : 0u;
+          y1[e2] = live ? pack_bf16(bb[0], bb[1]) : 0u;
+        }
+        const int r = rr % 32;
+        const int swz = ((r & 3) | (((r >> 3) & 3) << 2)) & (CPR - 1);
+        char *kt = &ltile[rr / 32][0];
+        *reinterpret_cast<uint4 *>(kt + (r * CPR + (c ^ swz)) * 16) =
+            make_uint4(y0[0], y0[1], y0[2], y0[3]);
+        *reinterpret_cast<uint4 *>(kt + (r * CPR + ((c + CPR / 2) ^ swz)) * 16) =
+            make_uint4(y1[0], y1[1], y1[2], y1[3]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int it = tid + u * NT, rr = it / CPR, c = it % CPR;
+      if (it < OVC && rr < ntile * 32) {
+        const int r = rr % 32, blk = r / 16, half = (r % 16) / 8;
+        const bool live = rr < n;
+        const uint32_t w[4] = {live ? ovx[u].x : 0u, live ? ovx[u].y : 0u, live ? ovx[u].z : 0u,
+                               live ? ovx[u].w : 0u};
+        char *vt = &ltile[rr / 32][KCH * 16] + (r % 8) * 2;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int d = c * 8 + e;
+          *reinterpret_cast<uint16_t *>(vt + (blk * 2 * D + ((2 * d + half) ^ ((d >> 3) & 1))) * 16) =
+              (uint16_t)((e & 1) ? w[e / 2] >> 16 : w[e / 2] & 0xffffu);
+        }
+      }
+    }
+  };
+  if (fz) own_load();
   // (the loads above are issued before anything below: the hand-placed tile
   // waits count only the tile loads that follow them)
   asm volatile("" ::: "memory");
@@ -2369,6 +2462,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
           raw[ds][2 * e2 + 1] = bf_hi(w[e2]);
         }
       }
+      // (rows past the tile's queries unrotated: their outputs are never
+      // written, and the branch measured a tighter main loop than without)
       if (rot && rvalid[blk]) {
 #pragma unroll
         for (int ds = 0; ds < HS; ++ds)
@@ -2465,16 +2560,23 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   };
   // paged: bytes of one head's page (16 K rows, or one V block)
   constexpr int page_b = kPageRows * D * 2;
-  // First storage row of tile i (run 0, then run 1 from row 0).
+  // The chunk's own rows (run 1) are tiles [own0, own0 + n1): after the
+  // history, or first when they come from the caller's K and V (written to
+  // their stages by own_store before the first barrier, no loads issued).
+  const int own0 = fz ? 0 : n0, hist0 = fz ? n1 : 0;
+  auto own = [=](int i) __attribute__((always_inline)) {
+    return (unsigned)(i - own0) < (unsigned)n1;
+  };
+  // First storage row of tile i (run 0 from f0, run 1 from row 0).
   auto tile_row = [=](int i) __attribute__((always_inline)) {
-    return i < n0 ? f0 + i * 32 : (i - n0) * 32;
+    return own(i) ? (i - own0) * 32 : f0 + (i - hist0) * 32;
   };
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)&ltile[0][0];
   // Issue the loads of tile i into stage st_ (zeros and no memory access
   // past the last tile).
   auto issue = [&](int i, int st_) __attribute__((always_inline)) {
     const bool live = i < ntiles;
-    const bool second = i >= n0;
+    const bool second = own(i);
     const int t0 = tile_row(live ? i : 0);
 #pragma unroll
     for (int e = 0; e < SPW; ++e) {
@@ -2502,7 +2604,6 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // Reference-max slack (log2 units): p < 2^8 keeps P well inside bf16 and
   // l, O inside fp32.
   constexpr float kLazyRescale = 8.f;
-  const int first_i = st.first[b];  // left padding: keys before it are hidden
   // Lowest position each query block row may see besides its own: the
   // window's and the left padding's bound (a pad query sees only itself).
   int qp32[2], lowq[2];
@@ -2520,7 +2621,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     for (int db = 0; db < NDB; ++db) oacc[blk][db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int i, int s) __attribute__((always_inline)) {
-    const bool second = i >= n0;
+    const bool second = own(i);
     const int t0 = tile_row(i);
     const int vlo = second ? 0 : vlo0, vhi = second ? n : vhi0;
     const int psplit = second ? 0 : psplit0;
@@ -2531,6 +2632,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) sacc[blk][kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t ka[2][NDS];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -2540,13 +2642,21 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         // operand order of P.V
         const int r = 8 * (nl >> 2) + 4 * kb + (nl & 3), c = ds * 4 + q4;
         const int swz = ((r & 3) | (((r >> 3) & 3) << 2)) & (CPR - 1);
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(
-            &ltile[s][(r * CPR + (c ^ swz)) * 16]);
+        ka[kb][ds] = *reinterpret_cast<const bf16x8_t *>(&ltile[s][(r * CPR + (c ^ swz)) * 16]);
+      }
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
-          sacc[blk][kb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[blk][ds], sacc[blk][kb], 0, 0, 0);
-      }
+          sacc[blk][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][ds], qf[blk][ds],
+                                                                  sacc[blk][kb], 0, 0, 0);
+    // Every K operand read goes out before the first product (left to
+    // itself the scheduler may read one operand, wait for it and reuse its
+    // registers for the next).
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDS, 1);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * NDS, 1);  // MFMA
     // mask + scale + online softmax per block; sacc[blk][kb][jj] is key row
     // t0 + 8 q4 + 4 kb + jj, query row nl of the block.  A tile whose keys
     // every query of the q tile sees (data rows below its first position and,
@@ -2680,10 +2790,17 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // so the tile waits retire them too.
   constexpr int TP = QW == 8 ? 2 : 1;
   static_assert(NSTAGE >= 2 * TP, "tiles in flight beside the ones computed");
-  for (int t = 0; t < NSTAGE - TP; ++t) issue(t, t);
+  static_assert(NSTAGE - TP >= kChunkOwnMax / 32, "own_store tiles all in the prologue");
+  // (Tiles written by own_store issue no loads.  They are the first ones, so
+  // every wait below still finds its tiles' loads older than the count it
+  // leaves in flight.)
+  const int skip = fz ? n1 : 0;
+  for (int t = 0; t < NSTAGE - TP; ++t)
+    if (t >= skip) issue(t, t);
   // Nothing below moves above the tile loads: the queries are rotated while
   // the first tiles are in flight.
   __builtin_amdgcn_sched_barrier(0);
+  if (fz) own_store(n1);
   make_q();
   for (int i = 0; i < ntiles; i += TP) {
     lds_wait<SPW * (NSTAGE - 2 * TP)>();
@@ -2763,7 +2880,58 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
       *commit_last = prev == nqt - 1;
     }
     __syncthreads();
-    if (*commit_last) {
+    if (*commit_last && fz) {
+      // Kept rows from the caller's K and V: staged in LDS again by
+      // own_load / own_store (the verdict's word is rewritten, so every wave
+      // reads it first), then copied out in 16-byte chunks.
+      const int i0 = n > W ? n - W : 0;  // first kept row
+      __syncthreads();
+      own_load();
+      own_store(n1);
+      __syncthreads();
+      constexpr int KC = D / 8;
+      for (int c = tid; c < (n - i0) * KC; c += NT) {
+        const int rr = i0 + c / KC, ch = c % KC, r = rr % 32;
+        const int swz = ((r & 3) | (((r >> 3) & 3) << 2)) & (CPR - 1);
+        *reinterpret_cast<uint4 *>(k_row<bf16>(la.k, bg, la.rows_alloc, (Li + rr) % W, D) + ch * 8) =
+            *reinterpret_cast<const uint4 *>(&ltile[rr / 32][(r * CPR + (ch ^ swz)) * 16]);
+      }
+      // V: runs of 8 rows that start at a multiple of 8 on both sides (one
+      // 16-byte chunk per d), the rest element by element
+      const int a8 = (Li % 8 == 0 && W % 8 == 0) ? (i0 + 7) / 8 * 8 : n;
+      const int e8 = a8 < n ? a8 + (n - a8) / 8 * 8 : a8;
+      auto vsrc = [&](int rr, int d) __attribute__((always_inline)) {
+        const int r = rr % 32, blk = r / 16, half = (r % 16) / 8;
+        return &ltile[rr / 32][KCH * 16 + (blk * 2 * D + ((2 * d + half) ^ ((d >> 3) & 1))) * 16] +
+               (r % 8) * 2;
+      };
+      for (int c = tid; c < (e8 - a8) / 8 * D; c += NT) {
+        const int rr = a8 + c / D * 8, d = c % D;
+        *reinterpret_cast<uint4 *>(v_elem<bf16>(la.v, bg, la.rows_alloc, (Li + rr) % W, d, D)) =
+            *reinterpret_cast<const uint4 *>(vsrc(rr, d));
+      }
+      const int nrest = (n - i0) - (e8 - a8);
+      for (int e = tid; e < nrest * D; e += NT) {
+        const int k = e / D, d = e % D;
+        const int rr = i0 + k < a8 ? i0 + k : e8 + (k - (a8 - i0));
+        *v_elem<bf16>(la.v, bg, la.rows_alloc, (Li + rr) % W, d, D) =
+            *reinterpret_cast<const bf16 *>(vsrc(rr, d));
+      }
+      // the step's slot indices (first KV head), and V zeroed past the new
+      // top in a tile the ring enters (the append's rule)
+      if (pa.slot_out && g == 0)
+        for (int i = tid; i < st.C; i += NT)
+          pa.slot_out[(int64_t)b * st.C + i] = i < n && i >= i0 ? (Li + i) % W : W;
+      if (wave == 0) {
+        const int64_t old_top = L < W ? L : W, new_top = L + n < W ? L + n : W;
+        if (old_top == 0 || (new_top - 1) / kRowAlign != (old_top - 1) / kRowAlign) {
+          int64_t end = (new_top + kRowAlign - 1) / kRowAlign * kRowAlign;
+          if (end > la.rows_alloc) end = la.rows_alloc;
+          zero_v_rows<bf16>(la.v, bg, la.rows_alloc, new_top, end, D, lane);
+        }
+      }
+      if (tid == 0) __hip_atomic_store(pa.ring_cnt + bg, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (*commit_last) {
       const int i0 = n > W ? n - W : 0;  // first kept staged row
       // Copies of n_items 16-byte chunks, four per thread in flight: every
       // load is issued (past the end the last chunk again) before the stores.

@@ -54,6 +54,7 @@ struct kvc_cache {
   int32_t dec_min_tiles = kvc::kDecodeSplitMinTiles;  // smallest planned split, in tiles
   int32_t log_level = 0;          // KVC_LOG: 1 sizes at create, 2 also decode plans
   bool no_fused = false;          // KVC_DECODE_FUSED=0: append + attend in kvc_append_attend
+  bool no_chunk_fused = false;    // KVC_CHUNK_FUSED=0: ring chunk steps staged there too
   bool fused_merge = false;       // KVC_FUSED_MERGE=1: the appending decode merges its splits
   bool no_wg = false;             // KVC_DECODE_WG=0: short windows take the split plan too
   bool chunk_cap_only = false;    // KVC_CHUNK_PLAN=0: chunk splits from the split cap alone
@@ -501,6 +502,7 @@ int kvc_create(const kvc_config *cfg, void *dev_buf, size_t buf_bytes, void *str
     if (v >= 1 && v <= 4096) h->dec_min_tiles = (int32_t)v;
   }
   if (const char *e = std::getenv("KVC_DECODE_FUSED")) h->no_fused = std::atoi(e) == 0;
+  if (const char *e = std::getenv("KVC_CHUNK_FUSED")) h->no_chunk_fused = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_FUSED_MERGE")) h->fused_merge = std::atoi(e) != 0;
   if (const char *e = std::getenv("KVC_DECODE_WG")) h->no_wg = std::atoi(e) == 0;
   if (const char *e = std::getenv("KVC_CHUNK_PLAN")) h->chunk_cap_only = std::atoi(e) == 0;
@@ -821,8 +823,13 @@ ScratchPlan scratch_plan(const kvc_t *h) {
 
 // One layer's attention (kvc_attend).  `scratch`: the split partials go to
 // this device array, laid out by scratch_plan, instead of the handle's buffer.
+// `ck`, `cv` (kvc_append_attend on a ring layer whose rows all hold 2 ..
+// kChunkOwnMax tokens; the layer is marked appended but nothing was staged):
+// the chunk kernel takes the chunk's rows from the caller's K and V and
+// commits them, with the slot indices to `slot_out`.
 int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream,
-                 char *scratch) {
+                 char *scratch, const void *ck = nullptr, const void *cv = nullptr,
+                 int32_t *slot_out = nullptr) {
   if (!h || !q || !out) return KVC_E_ARG;
   if (layer < 0 || layer >= h->cfg.n_layer) return KVC_E_ARG;
   if (!h->in_step || !h->appended[layer] || h->attended[layer]) return KVC_E_STATE;
@@ -1030,6 +1037,11 @@ int attend_layer(kvc_t *h, int32_t layer, const void *q, void *out, void *stream
     if (direct) pa.direct_out = out;
     // staged ring rows: the chunk launches commit them after scoring
     if (staged) pa.ring_cnt = reinterpret_cast<int32_t *>(h->base + h->lay.cnt_off);
+    if (staged && ck) {
+      pa.ck = ck;
+      pa.cv = cv;
+      pa.slot_out = slot_out;
+    }
     if (run(la, &pa) != KVC_OK) return KVC_E_HIP;
     committed = staged;
     if (joint) {
@@ -1074,6 +1086,25 @@ int kvc_append_attend(kvc_t *h, int32_t layer, const void *q, const void *k, con
   const int32_t B = h->cfg.batch, D = h->cfg.head_dim;
   const bool fused = C == 1 && !h->no_fused && h->cfg.dtype == KVC_BF16 &&
                      kvc::fast_decode_supported(D, la.rep) && h->lay.layers[layer].joint < 0;
+  // A ring layer's chunk step: when every row holds 2 .. kChunkOwnMax tokens
+  // the chunk kernel reads them from k and v, scores them and commits them
+  // to the ring (no staging, no append launch).  A joint layer's partner
+  // keeps staging: the joint layer reads its staged rows.
+  const bool ring_chunk = C >= 2 && C <= kvc::kChunkOwnMax && !h->no_chunk_fused && la.ring &&
+                          la.sk && !la.paged && h->cfg.dtype == KVC_BF16 &&
+                          kvc::fast_decode_supported(D, la.rep) &&
+                          kvc::fast_prefill_supported(D, la.rep) &&
+                          h->lay.layers[layer].joint < 0 && !h->partner_only[layer];
+  if (ring_chunk) {
+    const int rc = begin_append(h, layer, n_new_host, C, stream);
+    if (rc != KVC_OK) return rc;
+    bool all = true;
+    for (int32_t b = 0; b < B; ++b) all = all && h->n_new[b] >= 2;
+    if (all) {
+      h->appended[layer] = 1;
+      return attend_layer(h, layer, q, out, stream, nullptr, k, v, slot_out_dev);
+    }
+  }
   if (!fused) {
     const int rc = kvc_append(h, layer, k, v, n_new_host, C, slot_out_dev, stream);
     if (rc != KVC_OK) return rc;

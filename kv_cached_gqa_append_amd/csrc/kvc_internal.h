@@ -132,7 +132,18 @@ struct PartialArgs {
   // per (row, KV head), zero between launches; the last q tile of a (row,
   // KV head) to finish commits its staged rows to the ring.
   int32_t *ring_cnt;
+  // Non-null (both) on a ring layer's chunk launches from the appending
+  // entry: the chunk's own rows are read from the caller's K and V
+  // [B, C, hkv, D] and rotated in the kernel instead of staged, and the
+  // committing workgroup writes the kept rows to the ring from them, the
+  // slot indices (slot_out, when non-null) and the zeroed V rows of a newly
+  // entered tile.  Every row holds 2 .. kChunkOwnMax tokens.
+  const void *ck, *cv;
+  int32_t *slot_out;
 };
+// Most tokens per row the chunk kernel takes from the caller's K and V
+// (two 32-row key tiles).
+constexpr int kChunkOwnMax = 64;
 constexpr int kDecodeOrderMax = 256;
 
 // Static one-token steps.  Layers that plan alike (same KV heads, window and

@@ -307,7 +307,7 @@ int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialAr
 }
 int launch_decode_wg(const StepArgs &st, const LayerArgs &la, const PartialArgs &, const void *q,
                      const FusedArgs &fa, bool fused, const Launch &) {
-  if (st.C != 1 || la.paged || la.rep > 8) return (int)hipErrorInvalidValue;
+  if (st.C != 1 || la.paged || (la.rep > 8 && la.rep != 16)) return (int)hipErrorInvalidValue;
   check_step(st);
   check_layer(st, la);
   if (!q || !fa.out || (fused && (!fa.k || !fa.v))) fail("workgroup decode launch");
@@ -321,6 +321,9 @@ int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &p
   if (!q || n_items < 1 || (qw != 4 && qw != 8)) fail("chunk launch");
   if (pa.pre_split_keys < kRowAlign || pa.pre_split_keys % kRowAlign) fail("chunk split keys");
   if (!pa.direct_out) inside(pa.pml, 8, "chunk partials");
+  if ((pa.ck != nullptr) != (pa.cv != nullptr)) fail("chunk rows from k without v");
+  if (pa.ck && (!la.ring || la.paged || !pa.ring_cnt || st.C < 2 || st.C > kChunkOwnMax))
+    fail("chunk rows from the caller's k, v outside a ring layer's chunk step");
   ++stub::g_launches;
   return 0;
 }

@@ -260,6 +260,48 @@ def test_ring_decode_matrix_core_form(D, rep):
     _fused_vs_two_calls(work, prompts, steps, f"wgm{D}_{rep}")
 
 
+# Chunk steps of ring layers through kvc_append_attend: when every row holds
+# 2 .. 64 tokens the chunk kernel reads them from the caller's K and V,
+# scores them before the history and commits the kept ones to the ring
+# itself (no staging, no append launch).  Rings of 8, 48 and 200 slots beside
+# a global layer; rows longer than the window, wrapping, lengths off the
+# 8-row grid, padded tokens; steps with a one-token row take append + attend.
+# Outputs against the oracle, slots and cache rows bit for bit against the
+# two calls; the fused cache's staging is never written.
+@pytest.mark.parametrize("D,rep,ring_small", [(64, 4, "1"), (128, 8, "1"), (128, 8, "0"),
+                                              (128, 1, "1")])
+def test_fused_ring_chunk_steps(D, rep, ring_small, monkeypatch):
+    monkeypatch.setenv("KVC_CHUNK_RING_SMALL", ring_small)
+    say(f"case: ring chunk steps through kvc_append_attend, D={D} rep={rep} "
+        f"ring_small={ring_small}, W=8/48/200 + global")
+    hkv = 2
+    work = wl.Workload(f"rchunk_{D}_{rep}", 4, 4, hkv * rep, (hkv,) * 4, D, 700,
+                       (8, 48, 200, 0), "bf16", 64)
+    prompts = [(np.array([64, 2, 37, 13]), 64), (np.array([5, 64, 2, 30]), 64),
+               (np.array([12, 9, 33, 2]), 40), (np.array([3, 7, 64, 5]), 64),
+               (np.array([1, 6, 2, 4]), 6), (np.array([64, 64, 64, 64]), 64),
+               (np.array([17, 2, 50, 64]), 64)]
+    a = Pair(work, poison=True, tag="rchunk")
+    b = Pair(work, poison=True, tag="rchunk")
+    for s, (n, C) in enumerate(prompts):
+        a.step(n, C, fused=True)
+        b.step(n, C)
+        if s == 3:  # (every step so far had rows of 2 .. 64 tokens only)
+            for l in range(3):
+                for view in (a.cache.k_view(l, staging=True), a.cache.v_view(l, staging=True)):
+                    assert bool(torch.isnan(view.float()).all()), \
+                        f"layer {l}: a fused chunk step wrote staging"
+    for n in [np.array([1, 1, 1, 1]), np.array([1, 0, 1, 1])]:
+        oa = a.step(n, 1, fused=True)
+        ob = b.step(n, 1)
+        for l, (x, y) in enumerate(zip(oa, ob)):
+            assert torch.equal(x, y), f"layer {l}: fused output differs from append + attend"
+    for l in range(work.n_layer):
+        _same_cache(a, b, l)
+        a.check_cache_rows(l)
+    say(f"  worst abs {a.worst:.2e} rel {a.worst_rel:.2e}")
+
+
 @pytest.mark.parametrize("merge", ["0", "1"])
 def test_fused_decode_many_splits(merge, monkeypatch):
     monkeypatch.setenv("KVC_FUSED_MERGE", merge)
