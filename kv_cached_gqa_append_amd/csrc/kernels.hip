@@ -2255,7 +2255,12 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // each wave loads lie in one of them.
 // QW: waves per workgroup, 32 query rows each (8: 256-row query tiles, the
 // only workgroup on its CU; 4: 128-row tiles for short chunks, two per CU).
-template <int D, int REP, bool PAGED = false, int QW = 8>
+// KH (with QW 8): the eight waves are two groups of four over one 128-row
+// query tile, group h computing the key tiles i with i % 2 == h; the groups'
+// softmax states merge in LDS at the end.  For launches whose 4-wave form
+// leaves one wave per SIMD (a ring layer's chunk step over a small batch):
+// two waves per SIMD, each over half the keys.
+template <int D, int REP, bool PAGED = false, int QW = 8, bool KH = false>
 __global__ __launch_bounds__(QW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
                                                    const bf16 *__restrict__ q,
@@ -2265,7 +2270,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   constexpr int CPR = D / 8;               // 16-byte chunks of a K row
   constexpr int KCH = 32 * D / 8;          // 16-byte chunks of a K tile (= of a V tile)
   constexpr int NT = QW * 64;              // threads
-  constexpr int QT = QW * 32;              // query rows per workgroup
+  static_assert(!KH || QW == 8, "key halves: two groups of four waves");
+  constexpr int QT = KH ? 128 : QW * 32;   // query rows per workgroup
   // Tiles go from memory straight to LDS (buffer loads with the lds bit):
   // one load instruction fills a 1 KB slab of 64 chunks, lane L writing
   // chunk L.  A tile is NSL slabs (K, then V), each wave loading SPW of them.
@@ -2284,6 +2290,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   __shared__ __align__(16) char ltile[NSTAGE][STAGE_B];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qwave = KH ? (wave & 3) : wave;  // this wave's 32 query rows of the tile
+  const int khalf = KH ? (wave >> 2) : 0;    // (KH) its half of the key tiles
   const int q4 = lane >> 4, nl = lane & 15;
   const int g = blockIdx.y;
   const int SKP = pa.pre_split_keys;
@@ -2299,7 +2307,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         // 4-wave launch and the rest to the 8-wave one; with 2, every row
         // goes to the 4-wave launch
         const bool small = pa.chunk_small == 2 || n * REP <= 4 * 32;
-        if (pa.chunk_small && small != (QW == 4)) return 0;
+        if (pa.chunk_small && small != (QW == 4 || KH)) return 0;
         const int nqt = (int)cdiv((int64_t)n * REP, QT);
         if (la.ring) return nqt;
         int64_t base, lo, hi;
@@ -2336,7 +2344,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const bool rot = st.rope != nullptr;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    rq[blk] = qt * QT + wave * 32 + blk * 16 + nl;
+    rq[blk] = qt * QT + qwave * 32 + blk * 16 + nl;
     rvalid[blk] = rq[blk] < n * REP;
     // A row past the tile's queries computes with the last query row (its
     // output is never written): every lane loads, so no load sits under a
@@ -2808,19 +2816,61 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
 #pragma unroll
     for (int u = 0; u < TP; ++u) issue(i + NSTAGE - TP + u, (i + NSTAGE - TP + u) % NSTAGE);
     if (wave_live) {
+      if constexpr (KH) {
+        if (i + khalf < ntiles) compute(i + khalf, (i + khalf) % NSTAGE);
+      } else {
 #pragma unroll
-      for (int u = 0; u < TP; ++u)
-        if (u == 0 || i + u < ntiles) compute(i + u, (i + u) % NSTAGE);
+        for (int u = 0; u < TP; ++u)
+          if (u == 0 || i + u < ntiles) compute(i + u, (i + u) % NSTAGE);
+      }
     }
   }
   // the loads of tiles past the end land before the LDS is released
   lds_wait<0>();
+  if constexpr (KH) {
+    // Merge the key halves: the second group leaves its state (per lane:
+    // reference max, partial sum and O^T accumulators of both blocks) in the
+    // stages, the first takes it in.  Lanes of waves w and w + 4 hold the
+    // same query rows and head-dim columns.
+    static_assert(4 * 64 * (4 + 8 * NDB) * 4 <= NSTAGE * STAGE_B, "merge area");
+    constexpr int XF = 4 + 8 * NDB;  // floats per lane
+    float *xs = reinterpret_cast<float *>(&ltile[0][0]) + (qwave * 64 + lane) * XF;
+    __syncthreads();
+    if (khalf == 1) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        xs[blk] = mrun[blk];
+        xs[2 + blk] = lrun[blk];
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) xs[4 + (blk * NDB + db) * 4 + jj] = oacc[blk][db][jj];
+      }
+    }
+    __syncthreads();
+    if (khalf == 0) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const float m1 = xs[blk], l1 = xs[2 + blk];
+        const float mm = fmaxf(mrun[blk], m1);
+        const float a0 = mrun[blk] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[blk] - mm);
+        const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+        lrun[blk] = lrun[blk] * a0 + l1 * a1;
+        mrun[blk] = mm;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            oacc[blk][db][jj] = oacc[blk][db][jj] * a0 + xs[4 + (blk * NDB + db) * 4 + jj] * a1;
+      }
+    }
+  }
 
   // -- partials for this split (over a joint partner's keys: after the
   // layer's own splits) ------------------------------------------------------------
   const int sbase = pa.base.on ? ref_splits(pa.base, L, n, first_i) : 0;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int blk = 0; blk < 2 && khalf == 0; ++blk) {
     float lt = lrun[blk] + __shfl_xor(lrun[blk], 16);
     lt += __shfl_xor(lt, 32);
     if (pa.direct_out) {
@@ -3017,7 +3067,10 @@ template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, int qw, const Launch &lc) {
   const dim3 grid((unsigned)n_items, (unsigned)la.hkv);
-  if (qw == 4) {
+  if (qw == kChunkKeyHalves && !la.paged) {
+    launch_kernel((k_chunk<D, REP, false, 8, true>), grid, dim3(512), lc, st, la, pa,
+                  (const bf16 *)q, la.table);
+  } else if (qw == 4 || qw == kChunkKeyHalves) {
     if (la.paged)
       launch_kernel((k_chunk<D, REP, true, 4>), grid, dim3(256), lc, st, la, pa, (const bf16 *)q,
                     la.table);

@@ -244,9 +244,12 @@ int launch_decode_fused(const StepArgs &st, const LayerArgs &la, const PartialAr
 // new key and value (fa.k, fa.v, fa.slot_out), as launch_decode_fused.
 int launch_decode_wg(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                      const void *q, const FusedArgs &fa, bool fused, const Launch &lc);
-// qw: waves per workgroup (8: 256 query rows per item; 4: 128).  With
-// pa.chunk_small, the 4-wave launch takes the rows of at most 128 query rows
-// and the 8-wave launch the rest.
+// qw: waves per workgroup (8: 256 query rows per item; 4: 128;
+// kChunkKeyHalves: 128, eight waves as two groups of four over alternate key
+// tiles, merged in LDS).  With pa.chunk_small, the 4-wave (or key-halves)
+// launch takes the rows of at most 128 query rows and the 8-wave launch the
+// rest.
+constexpr int kChunkKeyHalves = 2;
 int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                    const void *q, int32_t n_items, int qw, const Launch &lc);
 int launch_combine(int dtype, const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,

@@ -268,12 +268,17 @@ def test_ring_decode_matrix_core_form(D, rep):
 # 8-row grid, padded tokens; steps with a one-token row take append + attend.
 # Outputs against the oracle, slots and cache rows bit for bit against the
 # two calls; the fused cache's staging is never written.
-@pytest.mark.parametrize("D,rep,ring_small", [(64, 4, "1"), (128, 8, "1"), (128, 8, "0"),
-                                              (128, 1, "1")])
-def test_fused_ring_chunk_steps(D, rep, ring_small, monkeypatch):
+# ring_small "1" (default) sends every row of these small batches to the
+# 128-row query tiles, in the key-halves form (kh "1", default) or in 4-wave
+# workgroups (kh "0"); ring_small "0" sorts rows by size into both launches.
+@pytest.mark.parametrize("D,rep,ring_small,kh", [(64, 4, "1", "1"), (128, 8, "1", "1"),
+                                                 (128, 8, "1", "0"), (128, 8, "0", "1"),
+                                                 (128, 1, "1", "1")])
+def test_fused_ring_chunk_steps(D, rep, ring_small, kh, monkeypatch):
     monkeypatch.setenv("KVC_CHUNK_RING_SMALL", ring_small)
+    monkeypatch.setenv("KVC_CHUNK_KEY_HALVES", kh)
     say(f"case: ring chunk steps through kvc_append_attend, D={D} rep={rep} "
-        f"ring_small={ring_small}, W=8/48/200 + global")
+        f"ring_small={ring_small} key_halves={kh}, W=8/48/200 + global")
     hkv = 2
     work = wl.Workload(f"rchunk_{D}_{rep}", 4, 4, hkv * rep, (hkv,) * 4, D, 700,
                        (8, 48, 200, 0), "bf16", 64)
