@@ -2586,10 +2586,15 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     const bool live = i < ntiles;
     const bool second = own(i);
     const int t0 = tile_row(live ? i : 0);
+    // (the tile's two sources picked once; when the K slabs are a whole
+    // number of rounds of the waves, slab e of every wave is K or V alike,
+    // known at compile time)
+    const i32x4 rk = PAGED ? dnone : rsrc_sel(live, rsrc_sel(second, dk1, dk0), dnone);
+    const i32x4 rv = PAGED ? dnone : rsrc_sel(live, rsrc_sel(second, dv1, dv0), dnone);
 #pragma unroll
     for (int e = 0; e < SPW; ++e) {
       const int j = wave + QW * e;
-      const bool isv = j >= KSL;
+      const bool isv = KSL % QW == 0 ? QW * e >= KSL : j >= KSL;
       const uint32_t m0 = __builtin_amdgcn_readfirstlane(
           lds0 + st_ * STAGE_B + (isv ? KCH * 16 + (j - KSL) * 1024 : j * 1024));
       if constexpr (PAGED) {
@@ -2601,9 +2606,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
         const i32x4 rs = rsrc_sel(live, sgpr_rsrc((isv ? la.v : la.k) + off, page_b), dnone);
         lds_load(m0, soff_lane[e] - sp * page_b, rs, 0);
       } else {
-        const i32x4 rs = rsrc_sel(live, isv ? rsrc_sel(second, dv1, dv0) : rsrc_sel(second, dk1, dk0), dnone);
         // K rows and V blocks advance by the same bytes per row
-        lds_load(m0, soff_lane[e], rs, __builtin_amdgcn_readfirstlane(t0 * D * 2));
+        lds_load(m0, soff_lane[e], isv ? rv : rk, __builtin_amdgcn_readfirstlane(t0 * D * 2));
       }
     }
   };
@@ -2833,35 +2837,40 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // stages, the first takes it in.  Lanes of waves w and w + 4 hold the
     // same query rows and head-dim columns.
     static_assert(4 * 64 * (4 + 8 * NDB) * 4 <= NSTAGE * STAGE_B, "merge area");
-    constexpr int XF = 4 + 8 * NDB;  // floats per lane
-    float *xs = reinterpret_cast<float *>(&ltile[0][0]) + (qwave * 64 + lane) * XF;
+    // (16-byte slots, slot k of the 64 lanes of a wave contiguous: one
+    // conflict-free 1 KB LDS access per slot; slot 0 holds the two blocks'
+    // maxima and sums, slot 1 + blk * NDB + db their accumulators)
+    constexpr int XS = 1 + 2 * NDB;  // slots per lane
+    float4 *xs = reinterpret_cast<float4 *>(&ltile[0][0]) + qwave * XS * 64 + lane;
     __syncthreads();
     if (khalf == 1) {
+      xs[0] = make_float4(mrun[0], mrun[1], lrun[0], lrun[1]);
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        xs[blk] = mrun[blk];
-        xs[2 + blk] = lrun[blk];
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) xs[4 + (blk * NDB + db) * 4 + jj] = oacc[blk][db][jj];
-      }
+          xs[(1 + blk * NDB + db) * 64] = make_float4(oacc[blk][db][0], oacc[blk][db][1],
+                                                      oacc[blk][db][2], oacc[blk][db][3]);
     }
     __syncthreads();
     if (khalf == 0) {
+      const float4 ml = xs[0];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const float m1 = xs[blk], l1 = xs[2 + blk];
+        const float m1 = blk ? ml.y : ml.x, l1 = blk ? ml.w : ml.z;
         const float mm = fmaxf(mrun[blk], m1);
         const float a0 = mrun[blk] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun[blk] - mm);
         const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
         lrun[blk] = lrun[blk] * a0 + l1 * a1;
         mrun[blk] = mm;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            oacc[blk][db][jj] = oacc[blk][db][jj] * a0 + xs[4 + (blk * NDB + db) * 4 + jj] * a1;
+        for (int db = 0; db < NDB; ++db) {
+          const float4 o1 = xs[(1 + blk * NDB + db) * 64];
+          oacc[blk][db][0] = oacc[blk][db][0] * a0 + o1.x * a1;
+          oacc[blk][db][1] = oacc[blk][db][1] * a0 + o1.y * a1;
+          oacc[blk][db][2] = oacc[blk][db][2] * a0 + o1.z * a1;
+          oacc[blk][db][3] = oacc[blk][db][3] * a0 + o1.w * a1;
+        }
       }
     }
   }
