@@ -2625,6 +2625,32 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     const int wl = W > 0 ? qp32[blk] - W + 1 : 0;
     lowq[blk] = wl > first_i ? wl : first_i;
   }
+  // Tiles whose keys every query of the q tile sees (data rows below the
+  // tile's first position and, on a windowed layer, inside its last
+  // position's window) need no mask: only those at the diagonal and the
+  // edges do.  Within a stretch of storage rows whose position is row + po,
+  // a tile starting at row t0 is such a tile iff lo <= t0 <= hi, so the
+  // full tiles are index ranges, found once here: the run-0 rows below
+  // psplit (po = pa0: a ring's newer slots) and from psplit on (po = pb0;
+  // a full layer has psplit 0), and the run-1 rows (po = L).  A ring tile
+  // across psplit is in neither.
+  auto full_tiles = [&](int po, int vlo, int vhi, int rlo, int rhi, int base, int *klo, int *khi) {
+    int lo = max(max(vlo, first_i - po), rlo);
+    if (W > 0) lo = max(lo, pmax_i - W + 1 - po);
+    const int hi = min(min(vhi - 32, pmin_i - 31 - po), rhi);
+    *klo = lo <= base ? 0 : (lo - base + 31) / 32;
+    *khi = hi < base ? -1 : (hi - base) / 32;
+  };
+  int fa0, fa1, fb0, fb1, fo0, fo1;
+  full_tiles(pa0, vlo0, vhi0, f0, psplit0 - 32, f0, &fa0, &fa1);
+  full_tiles(pb0, vlo0, vhi0, psplit0, 1 << 30, f0, &fb0, &fb1);
+  full_tiles(Li, 0, n, 0, 1 << 30, 0, &fo0, &fo1);
+  fa0 = __builtin_amdgcn_readfirstlane(fa0);
+  fa1 = __builtin_amdgcn_readfirstlane(fa1);
+  fb0 = __builtin_amdgcn_readfirstlane(fb0);
+  fb1 = __builtin_amdgcn_readfirstlane(fb1);
+  fo0 = __builtin_amdgcn_readfirstlane(fo0);
+  fo1 = __builtin_amdgcn_readfirstlane(fo1);
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   floatx4 oacc[2][NDB];
 #pragma unroll
@@ -2670,18 +2696,11 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __builtin_amdgcn_sched_group_barrier(0x100, 2 * NDS, 1);  // DS read
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * NDS, 1);  // MFMA
     // mask + scale + online softmax per block; sacc[blk][kb][jj] is key row
-    // t0 + 8 q4 + 4 kb + jj, query row nl of the block.  A tile whose keys
-    // every query of the q tile sees (data rows below its first position and,
-    // on a windowed layer, inside its last position's window) needs no mask:
-    // only the tiles at the diagonal and the edges do.
-    // The tile's oldest and newest positions (a ring tile across psplit
-    // holds the oldest position of all at psplit and the newest just
-    // below it).
-    const bool strad = t0 < psplit && t0 + 31 >= psplit;
-    const int minpos = strad ? psplit + pob : t0 + (t0 < psplit ? poa : pob);
-    const int maxpos = strad ? psplit - 1 + poa : t0 + 31 + (t0 + 31 < psplit ? poa : pob);
-    const bool full = t0 >= vlo && t0 + 32 <= vhi && maxpos <= pmin_i &&
-                      (W == 0 || pmax_i - minpos < W) && minpos >= first_i;
+    // t0 + 8 q4 + 4 kb + jj, query row nl of the block; unmasked on the full
+    // tiles found above
+    const int kr = second ? i - own0 : i - hist0;
+    const bool full = second ? (kr >= fo0 && kr <= fo1)
+                             : ((kr >= fa0 && kr <= fa1) || (kr >= fb0 && kr <= fb1));
     // Both blocks' masks and maxima first, then one (rarely taken) branch
     // for the accumulators' rescale, so that the exponentials and the P.V
     // products of the two blocks share one basic block and the scheduler can
