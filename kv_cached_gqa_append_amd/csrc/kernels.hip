@@ -3128,45 +3128,66 @@ int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &p
 
 // ---------------------------------------------------------------------------
 // Split combine: one wave per output row (b, i, h).  Log-sum-exp merge of the
-// split partials; padded queries and idle rows get exact zeros.
+// split partials; padded queries and idle rows get exact zeros.  (Four rows
+// per workgroup measured slower: 24.6 against 22.4 us on the mixed step's
+// merges.)
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, PartialArgs pa,
                                                 T *__restrict__ out) {
-  __shared__ float wts[64];
-  const int64_t row = blockIdx.x;  // (b * C + i) * Hq + h
-  const int h = (int)(row % st.Hq);
-  const int64_t bi = row / st.Hq;
-  const int i = (int)(bi % st.C);
-  const int b = (int)(bi / st.C);
+  // (32-bit index and span arithmetic: rows, positions and split counts
+  // stay far below 2^31, and a 64-bit division by a runtime value costs
+  // hundreds of instructions)
+  // (b * C + i) * Hq + h
+  const int row = (int)blockIdx.x;
+  const int h = row % st.Hq;
+  const int bi = row / st.Hq;
+  const int i = bi % st.C;
+  const int b = bi / st.C;
   const int lane = threadIdx.x;
   const int D = st.D;
-  T *o = out + row * D;
+  T *o = out + (int64_t)row * D;
+  // (the row's three counts in one round trip: the empty asm takes all
+  // three, so none is sunk past the branch into a load of its own)
   const int n = st.n_new[b];
+  const int L = st.lens[b];
+  const int first = st.first[b];
+  asm volatile("" ::"s"(n), "s"(L), "s"(first));
   if (i >= n) {
     for (int d = lane; d < D; d += 64) o[d] = from_f<T>(0.f);
     return;
   }
-  const int64_t L = st.lens[b];
+  // Splits of one layer for this row: the decode splits of a one-token
+  // row's key span, or the key splits of a chunk row (one on a ring layer);
+  // the spans of decode_span_dev and chunk_span_dev.
+  auto splits = [&](int ring, int W, int dec_sk, int pre_sk) {
+    if (n == 1) {
+      int start = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+      start = L < first ? L : (start > first ? start : first);
+      const int base = ring ? 0 : start / kRowAlign * kRowAlign;
+      const int hi = ring ? (L + 1 < W ? L + 1 : W) : L + 1;
+      return (hi - base + dec_sk - 1) / dec_sk;
+    }
+    if (ring) return 1;
+    int lo = W > 0 ? (L - W + 1 > 0 ? L - W + 1 : 0) : 0;
+    const int f = first < L ? first : L;
+    if (f > lo) lo = f;
+    const int base = lo / kRowAlign * kRowAlign;
+    return (L + n - base + pre_sk - 1) / pre_sk;
+  };
+  // a joint partner's splits follow the layer's own
+  const int nj =
+      pa.joint.on ? splits(pa.joint.ring, pa.joint.window, pa.joint.dec_sk, pa.joint.pre_sk) : 0;
   const float *ml;
   const float *os;
-  int ns;
-  // a joint partner's splits follow the layer's own
-  const int nj = pa.joint.on ? ref_splits(pa.joint, L, n, st.first[b]) : 0;
+  const int ns =
+      splits(la.ring, la.window, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys,
+             pa.pre_split_keys) + nj;
   if (n == 1) {
-    const DecodeSpan sp = decode_span_dev(la, L, st.first[b]);
-    ns = (int)cdiv(sp.hi - sp.base, pa.dec_plan ? pa.dec_plan[0] : pa.dec_split_keys) + nj;
     const int64_t s0 = ((int64_t)b * st.Hq + h) * kDecodeSplitCap;
     ml = pa.dml + s0 * 2;
     os = pa.dout + s0 * D;
   } else {
-    ns = 1;
-    if (!la.ring) {
-      int64_t base, lo, hi;
-      chunk_span_dev(la, L, n, st.first[b], &base, &lo, &hi);
-      ns = (int)cdiv(hi - base, pa.pre_split_keys);
-    }
-    ns += nj;
     const int64_t s0 = (((int64_t)b * pa.max_chunk + i) * st.Hq + h) * kChunkSplitCap;
     ml = pa.pml + s0 * 2;
     os = pa.pout + s0 * D;
@@ -3190,8 +3211,9 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
     const float M = wave_max(ms);
     const float w = lsr > 0.f ? exp2f(ms - M) : 0.f;
     const float Lt = wave_sum(w * lsr);
-    wts[lane] = w / Lt;
-    __syncthreads();
+    // (split s's weight from lane s)
+    const int wt = __builtin_bit_cast(int, w / Lt);
+    auto wts = [&](int sp) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(wt, sp)); };
     float a[2][8];
 #pragma unroll
     for (int e = 0; e < 2; ++e)
@@ -3207,7 +3229,7 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
           x[u][e] = s == 0 ? x0[u][e] : (e < dpl ? os[(int64_t)(s + u) * D + d0 + e] : 0.f);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float wu = wts[s + u];
+        const float wu = wts(s + u);
 #pragma unroll
         for (int e = 0; e < 2; ++e) a[e][u] = combine_acc(a[e][u], wu, x[u][e]);
       }
@@ -3223,7 +3245,7 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (s + u < ns) {
-          const float wu = wts[s + u];
+          const float wu = wts(s + u);
 #pragma unroll
           for (int e = 0; e < 2; ++e) a[e][0] = combine_acc(a[e][0], wu, x[u][e]);
         }
@@ -3237,21 +3259,21 @@ __global__ __launch_bounds__(64) void k_combine(StepArgs st, LayerArgs la, Parti
   const float M = wave_max(ms);
   const float w = ls > 0.f ? exp2f(ms - M) : 0.f;
   const float Lt = wave_sum(w * ls);
-  wts[lane] = w / Lt;
-  __syncthreads();
+  const int wt = __builtin_bit_cast(int, w / Lt);
+  auto wts = [&](int sp) { return __builtin_bit_cast(float, __builtin_amdgcn_readlane(wt, sp)); };
   for (int d = lane; d < D; d += 64) {
     float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     int s = 0;
     for (; s + 8 <= ns; s += 8) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const float w = wts[s + u];
+        const float w = wts(s + u);
         const float x = os[(int64_t)(s + u) * D + d];
         a[u] = combine_acc(a[u], w, x);  // splits without keys: slot never written
       }
     }
     for (; s < ns; ++s) {
-      const float w = wts[s];
+      const float w = wts(s);
       const float x = os[(int64_t)s * D + d];
       a[0] = combine_acc(a[0], w, x);
     }
