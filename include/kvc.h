@@ -164,9 +164,9 @@ size_t kvc_nbytes(const kvc_config *cfg, int what);
  *   KVC_CHUNK_RING_SMALL=0  ring layers' chunk rows take 8-wave workgroups
  *                           by size, as other layers' do, even when that
  *                           launch would hold fewer workgroups than CUs;
- *   KVC_CHUNK_KEY_HALVES=0  such rows (when all go to 128-row query tiles)
- *                           in 4-wave workgroups instead of 8-wave ones
- *                           whose two halves take alternate key tiles;
+ *   KVC_CHUNK_KEY_HALVES=0  chunk rows of 128-row query tiles in 4-wave
+ *                           workgroups instead of 8-wave ones whose two
+ *                           halves take alternate key tiles;
  *   KVC_CHUNK_SIDE=0        both chunk launches on the caller's stream
  *                           (default: with rows of both sizes, the 4-wave
  *                           launch runs on a second stream of the handle,

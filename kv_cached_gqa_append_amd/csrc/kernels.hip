@@ -2257,9 +2257,10 @@ int launch_decode(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa
 // only workgroup on its CU; 4: 128-row tiles for short chunks, two per CU).
 // KH (with QW 8): the eight waves are two groups of four over one 128-row
 // query tile, group h computing the key tiles i with i % 2 == h; the groups'
-// softmax states merge in LDS at the end.  For launches whose 4-wave form
-// leaves one wave per SIMD (a ring layer's chunk step over a small batch):
-// two waves per SIMD, each over half the keys.
+// softmax states merge in LDS at the end.  The form of the 128-row query
+// tiles: a tile's keys take half the steps, and where the 4-wave form would
+// leave one wave per SIMD (a ring layer's chunk step over a small batch)
+// there are two.
 template <int D, int REP, bool PAGED = false, int QW = 8, bool KH = false>
 __global__ __launch_bounds__(QW * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
@@ -3095,10 +3096,14 @@ template <int D, int REP>
 static void launch_chunk_t(const StepArgs &st, const LayerArgs &la, const PartialArgs &pa,
                            const void *q, int32_t n_items, int qw, const Launch &lc) {
   const dim3 grid((unsigned)n_items, (unsigned)la.hkv);
-  if (qw == kChunkKeyHalves && !la.paged) {
-    launch_kernel((k_chunk<D, REP, false, 8, true>), grid, dim3(512), lc, st, la, pa,
-                  (const bf16 *)q, la.table);
-  } else if (qw == 4 || qw == kChunkKeyHalves) {
+  if (qw == kChunkKeyHalves) {
+    if (la.paged)
+      launch_kernel((k_chunk<D, REP, true, 8, true>), grid, dim3(512), lc, st, la, pa,
+                    (const bf16 *)q, la.table);
+    else
+      launch_kernel((k_chunk<D, REP, false, 8, true>), grid, dim3(512), lc, st, la, pa,
+                    (const bf16 *)q, la.table);
+  } else if (qw == 4) {
     if (la.paged)
       launch_kernel((k_chunk<D, REP, true, 4>), grid, dim3(256), lc, st, la, pa, (const bf16 *)q,
                     la.table);

@@ -319,7 +319,7 @@ int launch_prefill(const StepArgs &st, const LayerArgs &la, const PartialArgs &p
   check_step(st);
   check_layer(st, la);
   if (!q || n_items < 1 || (qw != 4 && qw != 8 && qw != kChunkKeyHalves)) fail("chunk launch");
-  if (qw == kChunkKeyHalves && (pa.chunk_small != 2 || la.paged)) fail("key-halves chunk launch");
+  if (qw == kChunkKeyHalves && !pa.chunk_small) fail("key-halves chunk launch");
   if (pa.pre_split_keys < kRowAlign || pa.pre_split_keys % kRowAlign) fail("chunk split keys");
   if (!pa.direct_out) inside(pa.pml, 8, "chunk partials");
   if ((pa.ck != nullptr) != (pa.cv != nullptr)) fail("chunk rows from k without v");
