@@ -2652,6 +2652,10 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   fb1 = __builtin_amdgcn_readfirstlane(fb1);
   fo0 = __builtin_amdgcn_readfirstlane(fo0);
   fo1 = __builtin_amdgcn_readfirstlane(fo1);
+  // (as absolute tile indices, each range clipped to its run)
+  const int fa_lo = hist0 + fa0, fa_hi = hist0 + min(fa1, n0 - 1);
+  const int fb_lo = hist0 + fb0, fb_hi = hist0 + min(fb1, n0 - 1);
+  const int fo_lo = own0 + fo0, fo_hi = own0 + min(fo1, n1 - 1);
   float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
   floatx4 oacc[2][NDB];
 #pragma unroll
@@ -2660,11 +2664,6 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     for (int db = 0; db < NDB; ++db) oacc[blk][db] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](int i, int s) __attribute__((always_inline)) {
-    const bool second = own(i);
-    const int t0 = tile_row(i);
-    const int vlo = second ? 0 : vlo0, vhi = second ? n : vhi0;
-    const int psplit = second ? 0 : psplit0;
-    const int poa = second ? Li : pa0, pob = second ? Li : pb0;
     // S^T = K Q^T for both query blocks, each K operand read once
     floatx4 sacc[2][2];
 #pragma unroll
@@ -2699,9 +2698,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // mask + scale + online softmax per block; sacc[blk][kb][jj] is key row
     // t0 + 8 q4 + 4 kb + jj, query row nl of the block; unmasked on the full
     // tiles found above
-    const int kr = second ? i - own0 : i - hist0;
-    const bool full = second ? (kr >= fo0 && kr <= fo1)
-                             : ((kr >= fa0 && kr <= fa1) || (kr >= fb0 && kr <= fb1));
+    const bool full = (i >= fa_lo && i <= fa_hi) || (i >= fb_lo && i <= fb_hi) ||
+                      (i >= fo_lo && i <= fo_hi);
     // Both blocks' masks and maxima first, then one (rarely taken) branch
     // for the accumulators' rescale, so that the exponentials and the P.V
     // products of the two blocks share one basic block and the scheduler can
@@ -2719,6 +2717,12 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
             tmax[blk] = fmaxf(tmax[blk], sv[blk][kb][jj]);
           }
     } else {
+      // (the tile's run: its first row, data rows and positions)
+      const bool second = own(i);
+      const int t0 = tile_row(i);
+      const int vlo = second ? 0 : vlo0, vhi = second ? n : vhi0;
+      const int psplit = second ? 0 : psplit0;
+      const int poa = second ? Li : pa0, pob = second ? Li : pb0;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
