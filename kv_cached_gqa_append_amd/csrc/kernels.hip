@@ -2952,8 +2952,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   // other workgroup's loads have returned before its count (its waves
   // waited for all of them), so no read of a slot can follow its overwrite.
   if (pa.ring_cnt != nullptr) {
-    // (the verdict goes through the first word of the stages, free once
-    // every wave has passed the barrier below)
+    // (the flag of the last workgroup goes through the first word of the
+    // stages, free once every wave has passed the barrier below)
     int *commit_last = reinterpret_cast<int *>(&ltile[0][0]);
     __syncthreads();
     if (tid == 0) {
@@ -2965,7 +2965,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __syncthreads();
     if (*commit_last && fz) {
       // Kept rows from the caller's K and V: staged in LDS again by
-      // own_load / own_store (the verdict's word is rewritten, so every wave
+      // own_load / own_store (the flag's word is rewritten, so every wave
       // reads it first), then copied out in 16-byte chunks.
       const int i0 = n > W ? n - W : 0;  // first kept row
       __syncthreads();
