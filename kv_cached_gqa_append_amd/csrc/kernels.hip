@@ -2656,8 +2656,16 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const int fa_lo = hist0 + fa0, fa_hi = hist0 + min(fa1, n0 - 1);
   const int fb_lo = hist0 + fb0, fb_hi = hist0 + min(fb1, n0 - 1);
   const int fo_lo = own0 + fo0, fo_hi = own0 + min(fo1, n1 - 1);
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+  float mrun[2] = {-INFINITY, -INFINITY};
   floatx4 oacc[2][NDB];
+  // The rows' sums of P on the matrix cores: a product with a ones operand
+  // gives, in every row of its output, the column sums of the tile's P^T
+  // (the query's sum over the tile's 32 keys), so no lane sums its 8
+  // probabilities and no cross-lane sum is left for the end.
+  floatx4 lacc[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+  bf16x8_t ones;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.f;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -2761,6 +2769,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha[blk];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) lacc[blk] *= alpha[blk];
     }
     // O^T += V^T P^T; k-slot 8 q4 + e <-> key 8 q4 + e: 16 bytes of block
     // q4 / 2 at (d, half q4 % 2).  Each V operand (head-dim row db * 16 + nl)
@@ -2774,27 +2784,26 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
           &ltile[s][KCH * 16 + ((q4 >> 1) * 2 * D + (qq ^ ((d >> 3) & 1))) * 16]);
     }
     auto probs = [&](int blk) __attribute__((always_inline)) {
-      float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float pe = __builtin_amdgcn_exp2f(fmaf(sv[blk][kb][jj], scale, -mu[blk]));
-          ps += pe;
           pf[blk][kb * 4 + jj] = (bf16)pe;
         }
-      lrun[blk] = lrun[blk] * alpha[blk] + ps;
     };
     probs(0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
       oacc[0][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8_t, av[db]), pf[0], oacc[0][db], 0, 0, 0);
+    lacc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[0], lacc[0], 0, 0, 0);
     probs(1);
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
       oacc[1][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8_t, av[db]), pf[1], oacc[1][db], 0, 0, 0);
+    lacc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pf[1], lacc[1], 0, 0, 0);
     // Instruction order for the scheduler: the V operand reads, block 0's
     // probabilities, then block 0's products each followed by a share of
     // block 1's vector work (its exponentials run while the matrix core
@@ -2804,11 +2813,11 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     __builtin_amdgcn_sched_group_barrier(0x100, NDB, 0);     // DS read
     __builtin_amdgcn_sched_group_barrier(0x002, 30, 0);      // VALU (block 0)
 #pragma unroll
-    for (int k = 0; k < NDB; ++k) {
+    for (int k = 0; k < NDB + 1; ++k) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // MFMA
       __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);     // VALU
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NDB, 0);     // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, NDB + 1, 0); // MFMA
   };
 
   // Pipeline, TP tiles per barrier (the 8-wave workgroup takes two: one
@@ -2855,6 +2864,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   }
   // the loads of tiles past the end land before the LDS is released
   lds_wait<0>();
+  float lrun[2] = {lacc[0][0], lacc[1][0]};  // each row's sum of P (any of the 4 rows)
   if constexpr (KH) {
     // Merge the key halves: the second group leaves its state (per lane:
     // reference max, partial sum and O^T accumulators of both blocks) in the
@@ -2904,8 +2914,7 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const int sbase = pa.base.on ? ref_splits(pa.base, L, n, first_i) : 0;
 #pragma unroll
   for (int blk = 0; blk < 2 && khalf == 0; ++blk) {
-    float lt = lrun[blk] + __shfl_xor(lrun[blk], 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lrun[blk];
     if (pa.direct_out) {
       // The row's only split: its final output, with the arithmetic of the
       // merge of one split (weight 1 / l, one fused term, then the merge's
