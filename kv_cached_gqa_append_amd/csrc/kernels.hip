@@ -862,13 +862,21 @@ __device__ __forceinline__ void find_item(int B, int64_t it, CountFn count, int 
 // Fused mode (one-token steps): the last split block of a (row, KV head)
 // merges the partials and writes the output; idle rows are zeroed.
 // ---------------------------------------------------------------------------
+// (the max of a lane and its partner in one instruction: fmaxf on values the
+// compiler cannot prove canonical, as a swap's results are, first quiets
+// both inputs, two instructions more; the values here are never NaN)
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ __forceinline__ float swap16_max(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float swap32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float swap16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
