@@ -878,6 +878,26 @@ __device__ __forceinline__ float swap32_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
+// max(x, -FLT_MAX) in one instruction (fmaxf would first quiet x)
+__device__ __forceinline__ float max_lowest(float x) {
+  float r;
+  asm("v_max_f32 %0, 0xff7fffff, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// Maxima of a and of b over the wave's four 16-lane rows, into every lane
+// of a and b.  A row-16 exchange of the pair sets rows (a0, b0, a2, b2)
+// against (a1, b1, a3, b3), so one maximum reduces both to row pairs; a
+// row-32 exchange and a second maximum leave (A, B, A, B), and a last
+// row-16 exchange spreads A and B over whole registers.
+__device__ __forceinline__ void rows_max_pair(float &a, float &b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  const float x = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const float z = max2(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane16_swap(__float_as_uint(z), __float_as_uint(z), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float swap16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
@@ -2761,14 +2781,17 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // tiles instead of whenever some row's max grows.
     float mu[2], alpha[2];
     bool any_move = false;
+    // the row's max over the tile: its 4 lane groups hold 8 keys each
+    rows_max_pair(tmax[0], tmax[1]);
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      // the row's max over the tile: its 4 lane groups hold 8 keys each
-      const float tm = swap32_max(swap16_max(tmax[blk])) * scale;
+      const float tm = tmax[blk] * scale;
       const bool move = tm > mrun[blk] + kLazyRescale;
       const float mn = move ? tm : mrun[blk];
       alpha[blk] = move ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
-      mu[blk] = mn == -INFINITY ? 0.f : mn;
+      // mn = -inf only where every score of the row is -inf so far, and
+      // then s * scale - mu stays -inf with any finite mu
+      mu[blk] = max_lowest(mn);
       mrun[blk] = mn;
       any_move |= move;
     }
@@ -2784,13 +2807,13 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // q4 / 2 at (d, half q4 % 2).  Each V operand (head-dim row db * 16 + nl)
     // serves both blocks.
     bf16x8_t pf[2];
+    // Row d = 16 db + nl sits at chunk 2 d + q4 % 2, bit 0 flipped by bit 3
+    // of d (= bit 3 of nl): every db adds the same 32 chunks, so one lane
+    // address serves all NDB reads through the immediate offset.
+    const char *vrow = &ltile[s][KCH * 16 + ((q4 >> 1) * 2 * D + ((2 * nl + (q4 & 1)) ^ ((nl >> 3) & 1))) * 16];
     uint4 av[NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const int d = db * 16 + nl, qq = 2 * d + (q4 & 1);
-      av[db] = *reinterpret_cast<const uint4 *>(
-          &ltile[s][KCH * 16 + ((q4 >> 1) * 2 * D + (qq ^ ((d >> 3) & 1))) * 16]);
-    }
+    for (int db = 0; db < NDB; ++db) av[db] = *reinterpret_cast<const uint4 *>(vrow + db * 32 * 16);
     auto probs = [&](int blk) __attribute__((always_inline)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
