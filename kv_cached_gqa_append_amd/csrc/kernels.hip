@@ -23,6 +23,7 @@
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <cstring>
 #include <mutex>
 #include <type_traits>
@@ -2684,7 +2685,11 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   const int fa_lo = hist0 + fa0, fa_hi = hist0 + min(fa1, n0 - 1);
   const int fb_lo = hist0 + fb0, fb_hi = hist0 + min(fb1, n0 - 1);
   const int fo_lo = own0 + fo0, fo_hi = own0 + min(fo1, n1 - 1);
-  float mrun[2] = {-INFINITY, -INFINITY};
+  // Per block: the reference max m (scaled log2 domain), the exponent
+  // offset mu = max(m, -FLT_MAX) and the threshold m + kLazyRescale past
+  // which a tile moves m; all three change only on the rare moving tiles.
+  float mrun[2] = {-INFINITY, -INFINITY}, mu[2] = {-FLT_MAX, -FLT_MAX},
+        thr[2] = {-INFINITY, -INFINITY};
   floatx4 oacc[2][NDB];
   // The rows' sums of P on the matrix cores: a product with a ones operand
   // gives, in every row of its output, the column sums of the tile's P^T
@@ -2694,6 +2699,8 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
   bf16x8_t ones;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ones[e] = (bf16)1.f;
+  // held in registers through the loop rather than rebuilt for every tile
+  asm volatile("" : "+v"(ones));
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
@@ -2779,29 +2786,29 @@ void k_chunk(StepArgs st, LayerArgs la, PartialArgs pa,
     // max passes it by more than kLazyRescale: p = 2^(s*scale - m) then
     // stays below 2^kLazyRescale, and the accumulators are rescaled on rare
     // tiles instead of whenever some row's max grows.
-    float mu[2], alpha[2];
-    bool any_move = false;
     // the row's max over the tile: its 4 lane groups hold 8 keys each
     rows_max_pair(tmax[0], tmax[1]);
+    float tm[2];
+    bool move[2];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const float tm = tmax[blk] * scale;
-      const bool move = tm > mrun[blk] + kLazyRescale;
-      const float mn = move ? tm : mrun[blk];
-      alpha[blk] = move ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
-      // mn = -inf only where every score of the row is -inf so far, and
-      // then s * scale - mu stays -inf with any finite mu
-      mu[blk] = max_lowest(mn);
-      mrun[blk] = mn;
-      any_move |= move;
+      tm[blk] = tmax[blk] * scale;
+      move[blk] = tm[blk] > thr[blk];
     }
-    if (__ballot(any_move) != 0) {
+    if (__ballot(move[0] || move[1]) != 0) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < 2; ++blk) {
+        const float mn = move[blk] ? tm[blk] : mrun[blk];
+        const float alpha = move[blk] ? __builtin_amdgcn_exp2f(mrun[blk] - mn) : 1.f;
+        // mn = -inf only where every score of the row is -inf so far, and
+        // then s * scale - mu stays -inf with any finite mu
+        mu[blk] = max_lowest(mn);
+        thr[blk] = mn + kLazyRescale;
+        mrun[blk] = mn;
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha[blk];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) lacc[blk] *= alpha[blk];
+        for (int db = 0; db < NDB; ++db) oacc[blk][db] *= alpha;
+        lacc[blk] *= alpha;
+      }
     }
     // O^T += V^T P^T; k-slot 8 q4 + e <-> key 8 q4 + e: 16 bytes of block
     // q4 / 2 at (d, half q4 % 2).  Each V operand (head-dim row db * 16 + nl)
