@@ -1146,7 +1146,7 @@ __device__ __forceinline__ float keys_sum(float x) {
 template <int D>
 __device__ __forceinline__ void store_token_row(const LayerArgs &la, const FusedArgs &fa, int b,
                                                 int g, int64_t p, bool valid, float y1, float y2,
-                                                bf16 v1, bf16 v2, int lane) {
+                                                bf16 v1, bf16 v2, int lane, bool store_v = true) {
   static_assert(D / 2 <= 64, "one (d, d + D/2) pair per lane");
   const int64_t bg = (int64_t)b * la.hkv + g;
   const int64_t r = la.ring ? (valid ? p % la.window : (int64_t)la.window)
@@ -1154,11 +1154,13 @@ __device__ __forceinline__ void store_token_row(const LayerArgs &la, const Fused
   constexpr int half = D / 2;
   if (lane < half) {
     bf16 *kd = krow_ptr<bf16>(la, b, g, r, D);
-    bf16 *vd = vcol_ptr<bf16>(la, b, g, r, D);
     kd[lane] = (bf16)y1;
     kd[lane + half] = (bf16)y2;
-    vd[lane * kVBlock] = valid ? v1 : (bf16)0.f;
-    vd[(lane + half) * kVBlock] = valid ? v2 : (bf16)0.f;
+    if (store_v) {
+      bf16 *vd = vcol_ptr<bf16>(la, b, g, r, D);
+      vd[lane * kVBlock] = valid ? v1 : (bf16)0.f;
+      vd[(lane + half) * kVBlock] = valid ? v2 : (bf16)0.f;
+    }
   }
   if (fa.slot_out && g == 0 && lane == 0) fa.slot_out[b] = (int32_t)r;
   if (valid && !la.paged) {  // (pages have V zeroed when taken)
@@ -1526,13 +1528,54 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
   const float2 qcs = *reinterpret_cast<const float2 *>(
       rot ? st.rope + (p * (D / 2) + lane % (D / 2)) * 2 : reinterpret_cast<const float *>(qraw));
   const float qc = qcs.x, qsn = qcs.y;
+  // Where the register tiles leave room for it (all shapes but the one
+  // wave of four-deep tiles, whose checked wait placement the extra branch
+  // would break), the new row's V reaches memory only after every tile load
+  // of the launch (below): it is one 2-byte store into each head-dim row's
+  // 32-byte run of its block, and ahead of the wave's tile loads it cost the
+  // decode_b64 step about 3 %.  The appending wave's own tile, loaded before
+  // that store, then takes the new values in registers: lane (half, mm)
+  // holds keys 8 half .. 8 half + 7 of head-dim row mm + 32 t in V register
+  // t, so the lanes of the new key's half get the element of their rows
+  // (from lane d of av1 below D/2, lane d - D/2 of av2 above).
+  constexpr bool kLateV = FUSED && !S::DEEP;
   if constexpr (FUSED) {
     if (appender) {
       float y1 = ax1, y2 = ax2;
       if (st.rope) rope_pair(ax1, ax2, arc, ars, &y1, &y2);
-      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane);
+      store_token_row<D>(la, fa, b, g, p, true, y1, y2, av1, av2, lane, !kLateV);
     }
   }
+  // (the new key's row in its tile and the tile's first row, uniform; the
+  // lane's two values packed in one register until the store)
+  int vkk = 0, vnew_t0 = -1;
+  const uint32_t avpk = (uint32_t)__builtin_bit_cast(uint16_t, av1) |
+                        ((uint32_t)__builtin_bit_cast(uint16_t, av2) << 16);
+  if constexpr (kLateV) {
+    if (appender) {
+      const int r_new = la.ring ? (int)(p % la.window) : (int)p;
+      vkk = __builtin_amdgcn_readfirstlane((r_new - (int)base64) % TK);
+      vnew_t0 = __builtin_amdgcn_readfirstlane(r_new - vkk);
+    }
+  }
+  auto patch_v = [&](Tile &T) {
+    const bool own = half == vkk / 8;
+    const int word = (vkk % 8) / 2;
+    const bool hi = (vkk & 1) != 0;
+#pragma unroll
+    for (int t = 0; t < VT; ++t) {
+      const bool upper = 32 * t >= D / 2;  // (the same for every lane of t)
+      const int src = mm + 32 * t - (upper ? D / 2 : 0);
+      const uint32_t nv = (uint32_t)__shfl((int)avpk, src);
+      const uint32_t bits = upper ? nv >> 16 : nv & 0xffffu;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t old = T.v[t][w];
+        const uint32_t upd = hi ? ((old & 0xffffu) | (bits << 16)) : ((old & 0xffff0000u) | bits);
+        T.v[t][w] = own && w == word ? upd : old;
+      }
+    }
+  };
   // The barrier keeps the compiler from moving the loads and stores above
   // past the tile loads: every vector memory access of the wave is then
   // older than the tiles, as the hand-placed tile waits require, and the
@@ -1693,6 +1736,9 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
     for (int u = 0; u < NBUF; ++u) {
       load(it + u + NBUF - 1, T[(u + NBUF - 1) % NBUF]);
       wait_tile(T[u], std::integral_constant<int, NBUF - 1>{});
+      if constexpr (kLateV) {
+        if (t_begin + (it + u) * t_stride == vnew_t0) patch_v(T[u]);
+      }
       if (it + u < n_iter) step(it + u, T[u]);
     }
   }
@@ -1705,6 +1751,15 @@ void k_decode(StepArgs st, LayerArgs la, PartialArgs pa, const bf16 *__restrict_
       for (int t = 0; t < NCH; ++t) tile_wait<0>(T[i].k[r][t]);
 #pragma unroll
     for (int t = 0; t < VT; ++t) tile_wait<0>(T[i].v[t]);
+  }
+  if constexpr (kLateV) {
+    // the new row's V, after the tile loads (see above)
+    if (appender && lane < D / 2) {
+      const int64_t r = la.ring ? p % la.window : p;
+      uint16_t *vd = reinterpret_cast<uint16_t *>(vcol_ptr<bf16>(la, b, g, r, D));
+      vd[lane * kVBlock] = (uint16_t)(avpk & 0xffffu);
+      vd[(lane + D / 2) * kVBlock] = (uint16_t)(avpk >> 16);
+    }
   }
 
   // ---- partials of this split ----
