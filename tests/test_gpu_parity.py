@@ -341,6 +341,22 @@ def test_fused_head_shapes(D, rep, merge, monkeypatch):
                         [np.array([1, 1, 1]), np.array([1, 0, 1])], f"fs{D}_{rep}")
 
 
+# The appending decode stores the new row's V after its tile loads and the
+# appending wave's own tile takes the values in registers: the new row at
+# every position of its 16-row block (both halves of the lanes' key ranges),
+# on a full layer and on a W = 48 ring (the workgroup form), bit for bit
+# against append + attend.
+@pytest.mark.parametrize("D,rep", [(64, 1), (64, 4), (128, 2), (128, 4)])
+def test_fused_new_row_every_block_position(D, rep):
+    say(f"case: fused one-token steps, new row at every block position, D={D} rep={rep}")
+    hkv = 2
+    work = wl.Workload(f"fpos_{D}_{rep}", 2, 4, hkv * rep, (hkv, hkv), D, 400, (0, 48), "bf16",
+                       40)
+    prompts = wl.fill_plan([33, 100, 7, 250], 40)
+    steps = [np.array([1, 1, 1, 1])] * 17 + [np.array([1, 0, 1, 1])]
+    _fused_vs_two_calls(work, prompts, steps, f"fpos{D}_{rep}")
+
+
 def test_fused_guards():
     say("case: fused entry point keeps the step protocol")
     work = wl.Workload("fguards", 2, 2, 8, (2, 2), 64, 20, (0, 4), "bf16", 16)
